@@ -1,0 +1,447 @@
+/*
+ * CPU oracle for paged-KV decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It is plain C, runs on
+ * the host, accumulates in double precision and follows the written
+ * definitions step by step, with no blocking, fusion or reordering beyond
+ * what those definitions state.  It shares no code, header, table or constant
+ * generator with the GPU library.
+ *
+ * Sources (web pages on the KV cache; cited by title and section):
+ *   [KVC]  "LLM 推理优化深度解析：KV Cache、Continuous Batching、PagedAttention
+ *          与量化，从原理到 vLLM 实战" -- sections "KV Cache 的本质" (the size
+ *          formula and its Llama-2-7B example), "MQA 与 GQA" (query heads
+ *          sharing KV heads), "PagedAttention：vLLM 的显存碎片治理" (16-token
+ *          blocks, a block table mapping logical to physical blocks).
+ *   [MGMT] "大模型推理的KV Cache管理从内存碎片到前缀缓存的优化实战" -- section
+ *          二 (classes KVCacheBlock: one block holds [heads][block_size][dim];
+ *          PagedKVCache.append_slot: logical block = token_idx // block_size),
+ *          section 四 (INT8 quantization of cached K/V, dequantize = code*scale).
+ *   [WIKI] "KV Cache 与 PagedAttention" -- "KV cache 有多大" (per-token size),
+ *          "三个直接推论" (GQA and KV quantization as byte savers).
+ *
+ * Readings where the pages leave a step open (each is listed in the design
+ * notes): pool layout [num_blocks][num_kv_heads][block_size][head_dim]; slot =
+ * physical_block*block_size + offset, negative slot = padding; query head h
+ * uses KV head h / (Hq/Hkv); context_len counts the newly written token;
+ * context_len 0 gives a zero output row; symmetric per-(block, head) scales
+ * with fp32 arithmetic; FP8 is OCP E4M3 ("fn": no infinities, 0x7F/0xFF NaN,
+ * max finite 448), round-to-nearest-even with saturation.
+ *
+ * Parity pins for every function live in tests/test_oracle_*.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Element type codes understood by the oracle (its own numbering). */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3 };
+
+/* Number of threads the parallel loops below use (1 without OpenMP).       */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+static size_t orc_elem_bytes(int dtype) {
+  switch (dtype) {
+    case ORC_F32: return 4;
+    case ORC_BF16: return 2;
+    case ORC_I8: return 1;
+    case ORC_FP8: return 1;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV-cache size.  [KVC] "KV Cache 的本质": bytes = 2 (K and V) x layers x
+ * KV heads x head dim x sequence length x bytes per element x batch.        */
+uint64_t orc_kv_cache_bytes(uint64_t layers, uint64_t kv_heads, uint64_t head_dim,
+                            uint64_t seq_len, uint64_t bytes_per_elem, uint64_t batch) {
+  return 2ull * layers * kv_heads * head_dim * seq_len * bytes_per_elem * batch;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scalar conversions to double.                                             */
+
+/* bfloat16 is the upper half of an IEEE binary32: widening appends 16 zero
+ * bits, which is exact.                                                     */
+double orc_bf16_to_double(uint16_t bits) {
+  uint32_t w = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &w, 4);
+  return (double)f;
+}
+
+/* OCP 8-bit float E4M3 ("fn" variant): 1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits.  Exponent field 0 encodes subnormals m/8 * 2^-6;
+ * exponent field 15 with mantissa 7 encodes NaN (no infinities); every other
+ * pattern is (1 + m/8) * 2^(e-7).                                           */
+double orc_e4m3_to_double(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* Encode a binary32 value as E4M3 by choosing the nearest finite value,
+ * ties to the code with an even mantissa (its lowest bit clear), values above
+ * the largest finite magnitude (448) clamped to it.  The positive finite codes
+ * 0x00..0x7E are in increasing order of value, so the search is a binary
+ * search over that ordered set.  The sign bit copies the sign of the input
+ * (so small negative values become negative zero).  NaN input is outside the
+ * oracle's domain and is not handled.                                       */
+uint8_t orc_e4m3_from_float(float x) {
+  double a = fabs((double)x);
+  int sign = signbit(x) ? 1 : 0;
+  int lo = 0, hi = 0x7E; /* decode(lo) <= a is kept invariant below */
+  uint8_t mag;
+  if (a >= orc_e4m3_to_double(0x7E)) {
+    mag = 0x7E;
+  } else {
+    /* find the largest code c with decode(c) <= a */
+    while (lo < hi) {
+      int mid = (lo + hi + 1) / 2;
+      if (orc_e4m3_to_double((uint8_t)mid) <= a)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    {
+      double below = orc_e4m3_to_double((uint8_t)lo);
+      double above = orc_e4m3_to_double((uint8_t)(lo + 1));
+      double d_below = a - below, d_above = above - a;
+      if (d_below < d_above)
+        mag = (uint8_t)lo;
+      else if (d_above < d_below)
+        mag = (uint8_t)(lo + 1);
+      else
+        mag = (lo & 1) ? (uint8_t)(lo + 1) : (uint8_t)lo;
+    }
+  }
+  return (uint8_t)((sign << 7) | mag);
+}
+
+/* Widen one stored KV element to double.  Quantized codes are multiplied by
+ * their (block, head) scale, as in [MGMT] section 四 (dequantize: code times
+ * scale); the product of an 8-bit code and a binary32 scale is exact in
+ * double.                                                                   */
+static double orc_load_elem(const void* base, size_t idx, int dtype, double scale) {
+  switch (dtype) {
+    case ORC_F32: return (double)((const float*)base)[idx];
+    case ORC_BF16: return orc_bf16_to_double(((const uint16_t*)base)[idx]);
+    case ORC_I8: return (double)((const int8_t*)base)[idx] * scale;
+    case ORC_FP8: return orc_e4m3_to_double(((const uint8_t*)base)[idx]) * scale;
+  }
+  return NAN;
+}
+
+static double orc_load_q(const void* q, size_t idx, int dtype) {
+  if (dtype == ORC_F32) return (double)((const float*)q)[idx];
+  return orc_bf16_to_double(((const uint16_t*)q)[idx]);
+}
+
+/* Offset (in elements) of (block b, KV head g, row o, dim 0) in a pool laid
+ * out as [num_blocks][num_kv_heads][block_size][head_dim]: one block holds
+ * every head's [block_size][head_dim] tile, as [MGMT] section 二 stores it. */
+static size_t orc_pool_offset(size_t b, size_t g, size_t o, int Hkv, int bs, int D) {
+  return ((b * (size_t)Hkv + g) * (size_t)bs + o) * (size_t)D;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Slot of the token at logical position t of sequence s.  [MGMT] section 二,
+ * PagedKVCache.append_slot: the logical block is t // block_size; the block
+ * table maps it to a physical block; the row inside the block is
+ * t % block_size.                                                           */
+int32_t orc_slot_of(const int32_t* block_tables, int max_blocks, int s, int t, int bs) {
+  int32_t phys = block_tables[(size_t)s * max_blocks + t / bs];
+  return phys * bs + t % bs;
+}
+
+/* Slots for the newest token of every sequence (position context_len - 1);
+ * sequences with context_len 0 get slot -1 (nothing to write).              */
+void orc_slot_mapping(const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                      int num_seqs, int bs, int32_t* slots) {
+  for (int s = 0; s < num_seqs; ++s)
+    slots[s] = context_lens[s] > 0
+                   ? orc_slot_of(block_tables, max_blocks, s, context_lens[s] - 1, bs)
+                   : -1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cache write.  [KVC] "KV Cache 的本质": each decode step appends the new
+ * token's K and V to the cache.  Token i goes to slot slot_mapping[i]; its
+ * bytes for KV head g are copied unchanged into (slot / bs, g, slot % bs).
+ * A negative slot means "no token" and is skipped.                          */
+void orc_cache_write(void* k_cache, void* v_cache, int dtype, int num_blocks, int Hkv, int bs,
+                     int D, const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                     int n) {
+  size_t eb = orc_elem_bytes(dtype);
+  size_t row = (size_t)D * eb;
+  (void)num_blocks;
+  for (int i = 0; i < n; ++i) {
+    int32_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    for (int g = 0; g < Hkv; ++g) {
+      size_t dst = orc_pool_offset((size_t)(slot / bs), (size_t)g, (size_t)(slot % bs), Hkv, bs, D);
+      size_t src = ((size_t)i * Hkv + g) * (size_t)D;
+      memcpy((char*)k_cache + dst * eb, (const char*)k_new + src * eb, row);
+      memcpy((char*)v_cache + dst * eb, (const char*)v_new + src * eb, row);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gather: copy each sequence's K and V into logical order, giving the
+ * contiguous layout the paging replaces ([KVC] "预分配的困境").  Output rows
+ * are [cu_seqlens[s] + t][g][:].                                            */
+void orc_gather(const void* k_cache, const void* v_cache, int dtype, int Hkv, int bs, int D,
+                const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                const int32_t* cu_seqlens, int num_seqs, void* k_out, void* v_out) {
+  size_t eb = orc_elem_bytes(dtype);
+  size_t row = (size_t)D * eb;
+  for (int s = 0; s < num_seqs; ++s) {
+    for (int t = 0; t < context_lens[s]; ++t) {
+      int32_t b = block_tables[(size_t)s * max_blocks + t / bs];
+      for (int g = 0; g < Hkv; ++g) {
+        size_t src = orc_pool_offset((size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs, D);
+        size_t dst = ((size_t)(cu_seqlens[s] + t) * Hkv + g) * (size_t)D;
+        memcpy((char*)k_out + dst * eb, (const char*)k_cache + src * eb, row);
+        memcpy((char*)v_out + dst * eb, (const char*)v_cache + src * eb, row);
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention of one query row over tokens [t0, t1) of sequence s, head h.
+ * Writes the logits' maximum m, the sum l of exp(logit - m) and, into o, the
+ * weighted sum of V rows divided by l.  An empty range gives m = -inf, l = 0,
+ * o = 0.  Tokens are visited in logical order through the block table.      */
+static void orc_attend_range(const void* q, int q_dtype, const void* k_cache,
+                             const void* v_cache, int kv_dtype, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables, int max_blocks,
+                             int s, int h, int Hq, int Hkv, int D, int bs, double scale, int t0,
+                             int t1, double* logits, double* m_out, double* l_out,
+                             double* o_out) {
+  /* [KVC] "MQA 与 GQA": Hq/Hkv query heads share one KV head; head h reads
+   * KV head h / (Hq/Hkv) (contiguous groups).                               */
+  int G = Hq / Hkv;
+  int g = h / G;
+  const size_t qrow = ((size_t)s * Hq + h) * (size_t)D;
+  double m = -INFINITY, l = 0.0;
+  for (int d = 0; d < D; ++d) o_out[d] = 0.0;
+  if (t1 <= t0) {
+    *m_out = m;
+    *l_out = 0.0;
+    return;
+  }
+  /* logits: scale * q . k_t  */
+  for (int t = t0; t < t1; ++t) {
+    int32_t b = block_tables[(size_t)s * max_blocks + t / bs];
+    size_t base = orc_pool_offset((size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs, D);
+    double ks = k_scale ? (double)k_scale[(size_t)b * Hkv + g] : 1.0;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += orc_load_q(q, qrow + d, q_dtype) * orc_load_elem(k_cache, base + d, kv_dtype, ks);
+    logits[t - t0] = scale * dot;
+  }
+  /* softmax with the maximum subtracted, then the weighted sum of V rows    */
+  for (int t = t0; t < t1; ++t)
+    if (logits[t - t0] > m) m = logits[t - t0];
+  for (int t = t0; t < t1; ++t) {
+    int32_t b = block_tables[(size_t)s * max_blocks + t / bs];
+    size_t base = orc_pool_offset((size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs, D);
+    double vs = v_scale ? (double)v_scale[(size_t)b * Hkv + g] : 1.0;
+    double w = exp(logits[t - t0] - m);
+    l += w;
+    for (int d = 0; d < D; ++d) o_out[d] += w * orc_load_elem(v_cache, base + d, kv_dtype, vs);
+  }
+  for (int d = 0; d < D; ++d) o_out[d] /= l;
+  *m_out = m;
+  *l_out = l;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Paged decode attention, the plain definition:
+ *   out[s][h] = sum_{t < L_s} softmax_t(scale * q[s][h] . k_t) * v_t
+ * with k_t, v_t read at (block_tables[s][t / bs], h / G, t % bs).  Paging
+ * changes where the bytes live, not the result ([KVC] "PagedAttention：vLLM
+ * 的显存碎片治理"; [MGMT] section 二).  context_len 0 gives a zero row.
+ * out is double [num_seqs][Hq][D].  Rows (s, h) are independent; OpenMP
+ * spreads them over threads without changing any row's arithmetic.         */
+int orc_decode(const void* q, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+               int max_blocks, const int32_t* context_lens, int num_seqs, int Hq, int Hkv, int D,
+               int bs, float scale, double* out) {
+  int max_len = 0;
+  int fail = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (context_lens[s] > max_len) max_len = context_lens[s];
+#pragma omp parallel reduction(| : fail)
+  {
+    double* logits = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!logits) {
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long r = 0; r < (long)num_seqs * Hq; ++r) {
+        int s = (int)(r / Hq), h = (int)(r % Hq);
+        double m, l;
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+                         max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, context_lens[s],
+                         logits, &m, &l, out + (size_t)r * D);
+      }
+      free(logits);
+    }
+  }
+  return fail ? -1 : 0;
+}
+
+/* Decode for a subset of rows: rows[i] = s * Hq + h.  out is [n_rows][D].   */
+int orc_decode_rows(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                    int kv_dtype, const float* k_scale, const float* v_scale,
+                    const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                    int num_seqs, int Hq, int Hkv, int D, int bs, float scale, const int64_t* rows,
+                    int n_rows, double* out) {
+  int max_len = 0, fail = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (context_lens[s] > max_len) max_len = context_lens[s];
+#pragma omp parallel reduction(| : fail)
+  {
+    double* logits = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!logits) {
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int i = 0; i < n_rows; ++i) {
+        int s = (int)(rows[i] / Hq), h = (int)(rows[i] % Hq);
+        double m, l;
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+                         max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, context_lens[s],
+                         logits, &m, &l, out + (size_t)i * D);
+      }
+      free(logits);
+    }
+  }
+  return fail ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Split-context form.  The context of sequence s is cut into partitions of
+ * `part` tokens; partition p covers [p*part, min((p+1)*part, L)).  For each
+ * (s, h, p) this writes the partition's maximum m, sum l and normalised
+ * output o (empty partitions: -inf, 0, 0).  m, l are [num_seqs][Hq][P], o is
+ * [num_seqs][Hq][P][D] with P = n_parts.                                    */
+int orc_decode_partials(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                        int kv_dtype, const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                        int num_seqs, int Hq, int Hkv, int D, int bs, float scale, int part,
+                        int n_parts, double* m_out, double* l_out, double* o_out) {
+  int fail = 0;
+#pragma omp parallel reduction(| : fail)
+  {
+    double* logits = (double*)malloc(sizeof(double) * (size_t)part);
+    if (!logits) {
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long r = 0; r < (long)num_seqs * Hq; ++r) {
+        int s = (int)(r / Hq), h = (int)(r % Hq);
+        int L = context_lens[s];
+        for (int p = 0; p < n_parts; ++p) {
+          int t0 = p * part;
+          int t1 = (p + 1) * part < L ? (p + 1) * part : L;
+          size_t i = (size_t)r * n_parts + p;
+          orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                           block_tables, max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, t0,
+                           t1, logits, &m_out[i], &l_out[i], o_out + i * D);
+        }
+      }
+      free(logits);
+    }
+  }
+  return fail ? -1 : 0;
+}
+
+/* Combine partition results with the log-sum-exp rule:
+ *   M = max_p m_p,  w_p = exp(m_p - M) * l_p,  out = sum_p w_p o_p / sum_p w_p
+ * skipping empty partitions; a row with no tokens gives zeros.              */
+void orc_combine_partials(const double* m, const double* l, const double* o, int rows,
+                          int n_parts, int D, double* out) {
+  for (int r = 0; r < rows; ++r) {
+    double M = -INFINITY, den = 0.0;
+    for (int p = 0; p < n_parts; ++p)
+      if (l[(size_t)r * n_parts + p] > 0.0 && m[(size_t)r * n_parts + p] > M)
+        M = m[(size_t)r * n_parts + p];
+    for (int d = 0; d < D; ++d) out[(size_t)r * D + d] = 0.0;
+    for (int p = 0; p < n_parts; ++p) {
+      size_t i = (size_t)r * n_parts + p;
+      if (!(l[i] > 0.0)) continue;
+      double w = exp(m[i] - M) * l[i];
+      den += w;
+      for (int d = 0; d < D; ++d) out[(size_t)r * D + d] += w * o[i * D + d];
+    }
+    if (den > 0.0)
+      for (int d = 0; d < D; ++d) out[(size_t)r * D + d] /= den;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV quantization, symmetric with one binary32 scale per (block, KV head)
+ * tile of block_size x head_dim values ([MGMT] section 四 quantizes cached
+ * K/V to 8 bits and restores them as code * scale; the per-(block, head)
+ * symmetric grouping is this build's reading).  With a = max |x| over the
+ * whole tile (every row, used or not):
+ *   INT8:  scale = a / 127,  code = clamp(rint(x / scale), -127, 127)
+ *   FP8:   scale = a / 448,  code = E4M3(x / scale), nearest-even, saturating
+ * a == 0 gives scale 0 and all codes 0.  Divisions and rint are binary32
+ * operations with round-to-nearest-even, matching the stored scale format.
+ * block_ids == NULL means every block.                                      */
+int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, float* scales,
+                 int num_blocks, int Hkv, int bs, int D, const int32_t* block_ids, int n_ids) {
+  int n = block_ids ? n_ids : num_blocks;
+  if (dst_dtype != ORC_I8 && dst_dtype != ORC_FP8) return -1;
+  if (src_dtype != ORC_F32 && src_dtype != ORC_BF16) return -1;
+#pragma omp parallel for schedule(static)
+  for (long it = 0; it < (long)n * Hkv; ++it) {
+    int b = block_ids ? block_ids[it / Hkv] : (int)(it / Hkv);
+    int g = (int)(it % Hkv);
+    size_t base = orc_pool_offset((size_t)b, (size_t)g, 0, Hkv, bs, D);
+    size_t cnt = (size_t)bs * D;
+    float a = 0.0f, sc;
+    for (size_t i = 0; i < cnt; ++i) {
+      float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0);
+      float ax = fabsf(x);
+      if (ax > a) a = ax;
+    }
+    sc = (dst_dtype == ORC_I8) ? a / 127.0f : a / 448.0f;
+    scales[(size_t)b * Hkv + g] = sc;
+    for (size_t i = 0; i < cnt; ++i) {
+      float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0);
+      if (dst_dtype == ORC_I8) {
+        float r = (a == 0.0f) ? 0.0f : rintf(x / sc);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        ((int8_t*)dst_k)[base + i] = (int8_t)r;
+      } else {
+        ((uint8_t*)dst_k)[base + i] = (a == 0.0f) ? 0 : orc_e4m3_from_float(x / sc);
+      }
+    }
+  }
+  return 0;
+}
