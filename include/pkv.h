@@ -1,0 +1,192 @@
+/*
+ * pkv -- paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; no C++ or framework types.  Device
+ * pointers are HIP device memory owned by the caller; the library never
+ * allocates, frees or retains memory between calls.  `stream` is a
+ * hipStream_t passed as void* (NULL = the default stream); every call only
+ * enqueues work on it and returns without synchronising.  Calls on one
+ * stream run in order, so a cache write followed by attention on the same
+ * stream sees the written token.
+ *
+ * Errors.  Every entry point checks its arguments on the host before it
+ * touches the GPU and returns a status; it never aborts or throws.  Values
+ * that live in device memory (block ids in tables, slot numbers, context
+ * lengths) are not read by the host: kernels skip a block id outside
+ * [0, num_blocks), a slot outside [0, num_blocks*block_size) and a length
+ * outside [0, max_blocks_per_seq*block_size] instead of touching memory out
+ * of range, so bad table contents give unspecified numbers, never a fault.
+ * pkv_validate_tables() copies tables to the host and reports such values.
+ *
+ * Sources (web pages on the KV cache, cited by title and section):
+ *   [KVC]  "LLM 推理优化深度解析：KV Cache、Continuous Batching、PagedAttention
+ *          与量化，从原理到 vLLM 实战": "KV Cache 的本质" (each decode step
+ *          appends the new token's K/V; size formula), "MQA 与 GQA" (query
+ *          heads share KV heads), "PagedAttention：vLLM 的显存碎片治理"
+ *          (16-token blocks; block table maps logical to physical blocks;
+ *          shared blocks for common prefixes).
+ *   [MGMT] "大模型推理的KV Cache管理从内存碎片到前缀缓存的优化实战": section
+ *          二 (KVCacheBlock stores [heads][block_size][head_dim]; append_slot
+ *          takes logical block token_idx // block_size; allocation failure is
+ *          a return value), section 四 (KV stored as 8-bit codes, restored as
+ *          code * scale).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PKV_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or
+                              inconsistent (Hq % Hkv, block_size != 16, ...)   */
+  PKV_ERR_DTYPE = 3,       /* unknown dtype code or unsupported dtype pairing   */
+  PKV_ERR_RANGE = 4,       /* a value read by pkv_validate_tables is out of range */
+  PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+  PKV_ERR_UNSUPPORTED = 6, /* valid request outside what this build implements  */
+  PKV_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed        */
+};
+
+/* Element types. */
+enum {
+  PKV_F32 = 0,      /* IEEE binary32                                            */
+  PKV_BF16 = 1,     /* bfloat16 (upper half of binary32)                        */
+  PKV_I8 = 2,       /* int8 code, value = code * scale                          */
+  PKV_FP8_E4M3 = 3  /* OCP E4M3 "fn" code (bias 7, max 448, no inf), value = decoded * scale */
+};
+
+#define PKV_BLOCK_SIZE 16
+
+/* A paged KV pool for one layer.
+ *   k_cache, v_cache: [num_blocks][num_kv_heads][block_size][head_dim] of
+ *     kv_dtype -- one block holds every KV head's [block_size][head_dim] tile,
+ *     the per-block layout of [MGMT] section 二; each (block, head) tile is
+ *     contiguous (4 KiB for bf16 x 16 x 128).
+ *   k_scale, v_scale: [num_blocks][num_kv_heads] binary32 scales, required for
+ *     PKV_I8 / PKV_FP8_E4M3 and ignored otherwise.
+ * block_size must be 16 ([KVC] "PagedAttention"); head_dim must be 64 or 128. */
+typedef struct pkv_cache_t {
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t kv_dtype;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+} pkv_cache_t;
+
+/* Human-readable text for a status code (static storage). */
+const char* pkv_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+/* Bytes of one of the two pools (K or V) for the given geometry and dtype:
+ * num_blocks * num_kv_heads * block_size * head_dim * element size.  Returns
+ * 0 for an unknown dtype or a negative size. */
+uint64_t pkv_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                        int32_t head_dim, int32_t dtype);
+
+/* Slot mapping ([MGMT] section 二, append_slot): for each sequence s with
+ * context_lens[s] > 0, slot_mapping[s] = block_tables[s][t / 16] * 16 + t % 16
+ * for its newest position t = context_lens[s] - 1; sequences with length 0
+ * (or a length past the table) get -1.
+ *   block_tables: device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens: device int32 [num_seqs]
+ *   slot_mapping: device int32 [num_seqs], written. */
+int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t* slot_mapping,
+                     void* stream);
+
+/* Cache write ([KVC] "KV Cache 的本质": each decode step appends the new
+ * token's K and V): for i < n with slot = slot_mapping[i] >= 0, copies the
+ * bytes of k[i][g][:] and v[i][g][:] into row slot % 16 of block slot / 16,
+ * KV head g, for every g.  Bit-exact copy.
+ *   k, v: device [n][num_kv_heads][head_dim] of cache->kv_dtype
+ *   slot_mapping: device int32 [n]; negative = skip; slots must be distinct.
+ * kv_dtype must be PKV_F32 or PKV_BF16 (appending into an 8-bit cache is
+ * PKV_ERR_UNSUPPORTED: quantize whole blocks with pkv_quantize instead). */
+int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
+                    const int32_t* slot_mapping, int32_t n, void* stream);
+
+/* Workspace bytes pkv_attention_decode needs for a split-context launch
+ * (partition_tokens > 0): per (sequence, query head, partition) a running
+ * maximum, a sum and a head_dim output row, all binary32, plus alignment.
+ * Returns 0 when partition_tokens == 0 (no workspace needed). */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t partition_tokens);
+
+/* A split size for the given geometry: a multiple of 16 (or 0 for no split)
+ * that gives enough independent work units to fill the GPU. */
+int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                     int32_t max_blocks_per_seq);
+
+/* Paged decode attention ([KVC] "PagedAttention", "MQA 与 GQA"):
+ *   out[s][h] = sum_{t < L} softmax_t(scale * q[s][h] . k_t) v_t,
+ *   L = context_lens[s], k_t / v_t at (block_tables[s][t / 16], h / G, t % 16),
+ *   G = num_q_heads / num_kv_heads; L == 0 gives a zero row.
+ *   q: device [num_seqs][num_q_heads][head_dim] of q_dtype
+ *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *     ceil(L / 16) are never read
+ *   context_lens: device int32 [num_seqs], 0 <= L <= max_blocks_per_seq * 16
+ *   partition_tokens: 0 = one pass per (sequence, KV head); otherwise a
+ *     positive multiple of 16: the context is cut into partitions of that many
+ *     tokens, each gives a partial (max, sum, output) and a second kernel
+ *     combines them with the log-sum-exp rule
+ *   workspace: device memory of at least pkv_decode_workspace_bytes(...) when
+ *     partition_tokens > 0 (contents need not be initialised), else may be NULL
+ *   out: device [num_seqs][num_q_heads][head_dim] of out_dtype.
+ * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8),
+ * (BF16, FP8_E4M3); out_dtype F32 or BF16 (bf16 rounded to nearest even). */
+int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
+
+/* KV quantization ([MGMT] section 四, with one symmetric binary32 scale per
+ * (block, KV head) tile): for each listed block b and KV head g, with
+ * a = max |x| over the whole 16 x head_dim tile of src (every row),
+ *   PKV_I8:       scale = a / 127, code = clamp(rint(x / scale), -127, 127)
+ *   PKV_FP8_E4M3: scale = a / 448, code = nearest E4M3 (ties to even), values
+ *                 beyond 448 in magnitude saturate to +-448
+ * a == 0 gives scale 0 and zero codes.  Divisions and rounding are binary32,
+ * round-to-nearest-even.  Quantizes src->k_cache into dst->k_cache (scales to
+ * dst->k_scale) and src->v_cache into dst->v_cache (dst->v_scale).
+ *   src: kv_dtype F32 or BF16; dst: kv_dtype I8 or FP8_E4M3, same geometry
+ *   block_ids: device int32 [n_ids], or NULL for every block (n_ids ignored). */
+int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,
+                 int32_t n_ids, void* stream);
+
+/* Gather (diagnostic): copies each sequence's K and V, in logical order, into
+ * contiguous rows k_out[cu_seqlens[s] + t][g][:] for t < context_lens[s].
+ * Bit-exact copy of the stored elements (codes for 8-bit pools).
+ *   cu_seqlens: device int32 [num_seqs + 1], cu_seqlens[s+1] = cu_seqlens[s] + L_s
+ *   k_out, v_out: device [cu_seqlens[num_seqs]][num_kv_heads][head_dim]. */
+int pkv_gather(const pkv_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* context_lens, const int32_t* cu_seqlens, int32_t num_seqs,
+               void* k_out, void* v_out, void* stream);
+
+/* Debug check of device tables (synchronises `stream`, copies to the host):
+ * every context length in [0, max_blocks_per_seq * 16] and every used table
+ * entry (index < ceil(L / 16)) in [0, num_blocks).  Returns PKV_OK or
+ * PKV_ERR_RANGE; *bad_seq (if not NULL) receives the first offending
+ * sequence or -1. */
+int pkv_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                        int32_t* bad_seq, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,271 @@
+"""pkv: paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/pkv.h`` (``libpkv.so``, built
+in-tree by ``paged_kv_cache_434_amd.build``).  Functions take torch tensors
+that already live on the GPU and only marshal pointers, sizes and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3}
+BLOCK_SIZE = 16
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _load().pkv_strerror(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m paged_kv_cache_434_amd.build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        C = ctypes.POINTER(CacheDesc)
+        sig = {
+            "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "pkv_version": (ctypes.c_int, []),
+            "pkv_pool_bytes": (ctypes.c_uint64, [I32, I32, I32, I32, I32]),
+            "pkv_slot_mapping": (ctypes.c_int, [P, I32, P, I32, P, P]),
+            "pkv_cache_write": (ctypes.c_int, [C, P, P, P, I32, P]),
+            "pkv_decode_workspace_bytes": (ctypes.c_size_t, [I32, I32, I32, I32, I32]),
+            "pkv_decode_default_partition": (I32, [I32, I32, I32]),
+            "pkv_attention_decode": (ctypes.c_int, [C, P, I32, P, I32, P, I32, I32, F, I32, P,
+                                                    ctypes.c_size_t, P, I32, P]),
+            "pkv_quantize": (ctypes.c_int, [C, C, P, I32, P]),
+            "pkv_gather": (ctypes.c_int, [C, P, I32, P, P, I32, P, P, P]),
+            "pkv_validate_tables": (ctypes.c_int, [P, I32, P, I32, I32,
+                                                   ctypes.POINTER(I32), P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _load()
+
+
+EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_mapping",
+                    "pkv_cache_write", "pkv_decode_workspace_bytes",
+                    "pkv_decode_default_partition", "pkv_attention_decode", "pkv_quantize",
+                    "pkv_gather", "pkv_validate_tables")
+
+
+def _check(fn: str, status: int):
+    if status != PKV_OK:
+        raise PkvError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _storage_dtype(name: str):
+    torch = _torch()
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8,
+            "fp8": torch.uint8}[name]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+class PagedCache:
+    """One layer's K and V pools ([num_blocks][Hkv][16][D]) and, for 8-bit
+    pools, their [num_blocks][Hkv] binary32 scales.  Holds references so the
+    tensors outlive the descriptor."""
+
+    def __init__(self, k_cache, v_cache, kv_dtype: str, k_scale=None, v_scale=None):
+        torch = _torch()
+        sd = _storage_dtype(kv_dtype)
+        if kv_dtype == "fp8" and k_cache.dtype == torch.float8_e4m3fn:
+            k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
+        _need(k_cache, "k_cache", sd, 4)
+        _need(v_cache, "v_cache", sd, 4)
+        if k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache shapes differ")
+        if kv_dtype in ("i8", "fp8"):
+            _need(k_scale, "k_scale", torch.float32, 2)
+            _need(v_scale, "v_scale", torch.float32, 2)
+        NB, Hkv, bs, D = k_cache.shape
+        self.k_cache, self.v_cache, self.k_scale, self.v_scale = k_cache, v_cache, k_scale, v_scale
+        self.kv_dtype = kv_dtype
+        self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = NB, Hkv, bs, D
+        self.desc = CacheDesc(NB, Hkv, bs, D, DTYPE_CODES[kv_dtype], k_cache.data_ptr(),
+                              v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale))
+
+
+def pool_bytes(num_blocks, num_kv_heads, head_dim, dtype, block_size=BLOCK_SIZE) -> int:
+    return int(_load().pkv_pool_bytes(num_blocks, num_kv_heads, block_size, head_dim,
+                                      DTYPE_CODES[dtype]))
+
+
+def slot_mapping(block_tables, context_lens, out=None, stream=None):
+    torch = _torch()
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=context_lens.device)
+    _need(out, "slot_mapping", torch.int32, 1)
+    _check("pkv_slot_mapping",
+           _load().pkv_slot_mapping(_ptr(block_tables), block_tables.shape[1],
+                                    _ptr(context_lens), B, _ptr(out), _stream(stream)))
+    return out
+
+
+def cache_write(cache: PagedCache, k, v, slot_mapping, stream=None):
+    torch = _torch()
+    sd = _storage_dtype(cache.kv_dtype)
+    _need(k, "k", sd, 3)
+    _need(v, "v", sd, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    n = slot_mapping.shape[0]
+    if tuple(k.shape) != (n, cache.num_kv_heads, cache.head_dim) or k.shape != v.shape:
+        raise ValueError("k/v must be [n][num_kv_heads][head_dim]")
+    _check("pkv_cache_write",
+           _load().pkv_cache_write(ctypes.byref(cache.desc), _ptr(k), _ptr(v),
+                                   _ptr(slot_mapping), n, _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                           partition_tokens) -> int:
+    return int(_load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                  max_blocks_per_seq, partition_tokens))
+
+
+def default_partition(num_seqs, num_kv_heads, max_blocks_per_seq) -> int:
+    return int(_load().pkv_decode_default_partition(num_seqs, num_kv_heads, max_blocks_per_seq))
+
+
+def alloc_workspace(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, partition_tokens,
+                    device="cuda"):
+    torch = _torch()
+    nbytes = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                                    partition_tokens)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                     partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
+                     stream=None):
+    """out[s][h] = softmax(scale q k^T) v over each sequence's paged context."""
+    torch = _torch()
+    qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if qd is None:
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", None, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("q, block_tables and context_lens disagree on the batch size")
+    od = out_dtype or (out.dtype if out is not None else q.dtype)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=od, device=q.device)
+    _need(out, "out", od, 3)
+    odn = {torch.float32: "f32", torch.bfloat16: "bf16"}[od]
+    maxb = block_tables.shape[1]
+    ws_need = decode_workspace_bytes(B, Hq, D, maxb, partition_tokens)
+    if ws_need and workspace is None:
+        workspace = alloc_workspace(B, Hq, D, maxb, partition_tokens, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attention_decode",
+           _load().pkv_attention_decode(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd],
+                                        _ptr(block_tables), maxb, _ptr(context_lens), B, Hq,
+                                        ctypes.c_float(scale), partition_tokens,
+                                        _ptr(workspace), ws_bytes, _ptr(out), DTYPE_CODES[odn],
+                                        _stream(stream)))
+    return out
+
+
+def quantize(src: PagedCache, dst: PagedCache, block_ids=None, stream=None):
+    torch = _torch()
+    n = 0
+    if block_ids is not None:
+        _need(block_ids, "block_ids", torch.int32, 1)
+        n = block_ids.shape[0]
+    _check("pkv_quantize",
+           _load().pkv_quantize(ctypes.byref(src.desc), ctypes.byref(dst.desc), _ptr(block_ids),
+                                n, _stream(stream)))
+
+
+def gather(cache: PagedCache, block_tables, context_lens, cu_seqlens, total_tokens: int,
+           stream=None):
+    torch = _torch()
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    B = context_lens.shape[0]
+    shape = (total_tokens, cache.num_kv_heads, cache.head_dim)
+    ko = torch.empty(shape, dtype=cache.k_cache.dtype, device=cache.k_cache.device)
+    vo = torch.empty(shape, dtype=cache.k_cache.dtype, device=cache.k_cache.device)
+    _check("pkv_gather",
+           _load().pkv_gather(ctypes.byref(cache.desc), _ptr(block_tables), block_tables.shape[1],
+                              _ptr(context_lens), _ptr(cu_seqlens), B, _ptr(ko), _ptr(vo),
+                              _stream(stream)))
+    return ko, vo
+
+
+def validate_tables(block_tables, context_lens, num_blocks, stream=None):
+    """Debug check (synchronises): returns (status, first bad sequence or -1)."""
+    bad = ctypes.c_int32(-1)
+    rc = _load().pkv_validate_tables(_ptr(block_tables), block_tables.shape[1],
+                                     _ptr(context_lens), context_lens.shape[0], num_blocks,
+                                     ctypes.byref(bad), _stream(stream))
+    return rc, bad.value

@@ -1,0 +1,220 @@
+// C ABI entry points (include/pkv.h): argument checks on the host, then one
+// or two kernel launches on the caller's stream.  Nothing here allocates
+// device memory or synchronises, except pkv_validate_tables (a debug check).
+#include <limits.h>
+#include <stdlib.h>
+
+#include "common.hpp"
+
+using namespace pkv;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const pkv_cache_t* c) {
+  if (!c) return PKV_ERR_NULL;
+  if (elem_bytes(c->kv_dtype) == 0) return PKV_ERR_DTYPE;
+  if (c->block_size != PKV_BLOCK_SIZE || c->num_blocks < 0 || c->num_kv_heads <= 0 ||
+      c->head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!c->k_cache || !c->v_cache) return PKV_ERR_NULL;
+  if ((c->kv_dtype == PKV_I8 || c->kv_dtype == PKV_FP8_E4M3) && (!c->k_scale || !c->v_scale))
+    return PKV_ERR_NULL;
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+int n_parts_of(int max_blocks, int partition_tokens) {
+  int part_blocks = partition_tokens > 0 ? partition_tokens / PKV_BLOCK_SIZE : max_blocks;
+  return (max_blocks + part_blocks - 1) / part_blocks;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_strerror(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid or inconsistent size";
+    case PKV_ERR_DTYPE: return "unknown or unsupported dtype combination";
+    case PKV_ERR_RANGE: return "table or length value out of range";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_UNSUPPORTED: return "request outside what this build implements";
+    case PKV_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+uint64_t pkv_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                        int32_t head_dim, int32_t dtype) {
+  size_t eb = elem_bytes(dtype);
+  if (eb == 0 || num_blocks < 0 || num_kv_heads < 0 || block_size < 0 || head_dim < 0) return 0;
+  return (uint64_t)num_blocks * num_kv_heads * block_size * head_dim * eb;
+}
+
+int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t* slot_mapping,
+                     void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !slot_mapping) return PKV_ERR_NULL;
+  return launch_slot_mapping(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                             slot_mapping, static_cast<hipStream_t>(stream));
+}
+
+int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
+                    const int32_t* slot_mapping, int32_t n, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  if (cache->kv_dtype != PKV_F32 && cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (n < 0) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)n * cache->num_kv_heads * cache->head_dim > (int64_t)UINT_MAX) return PKV_ERR_SHAPE;
+  return launch_cache_write(*cache, k, v, slot_mapping, n, static_cast<hipStream_t>(stream));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      partition_tokens <= 0 || partition_tokens % PKV_BLOCK_SIZE != 0)
+    return 0;
+  int np = n_parts_of(max_blocks_per_seq, partition_tokens);
+  if (np <= 1) return 0;
+  return decode_workspace_layout((int64_t)num_seqs * num_q_heads, np, head_dim, nullptr, nullptr);
+}
+
+int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                     int32_t max_blocks_per_seq) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
+  const int64_t max_ctx = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  // smallest power-of-two split >= 256 tokens that keeps the launch within
+  // 16384 wavefronts (64 per CU); no split when one partition covers the context
+  int64_t part = 256;
+  while (part < max_ctx && units * ((max_ctx + part - 1) / part) > 16384) part *= 2;
+  return part >= max_ctx ? 0 : (int32_t)part;
+}
+
+int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* out, int32_t out_dtype, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  if (elem_bytes(q_dtype) == 0 || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
+    return PKV_ERR_DTYPE;
+  const int kv = cache->kv_dtype;
+  const bool pair_ok = (q_dtype == PKV_F32 && kv == PKV_F32) ||
+                       (q_dtype == PKV_BF16 &&
+                        (kv == PKV_BF16 || kv == PKV_I8 || kv == PKV_FP8_E4M3));
+  if (!pair_ok) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_tokens < 0 ||
+      partition_tokens % PKV_BLOCK_SIZE != 0 || max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (num_q_heads / cache->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out)) return PKV_ERR_UNSUPPORTED;
+  const int np = n_parts_of(max_blocks_per_seq, partition_tokens);
+  if ((int64_t)num_seqs * cache->num_kv_heads * np > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
+  if (np > 1) {
+    size_t need = decode_workspace_layout((int64_t)num_seqs * num_q_heads, np, cache->head_dim,
+                                          nullptr, nullptr);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
+  }
+  DecodeArgs a{cache, q, q_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+               num_q_heads, scale, partition_tokens, workspace, out, out_dtype};
+  return launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,
+                 int32_t n_ids, void* stream) {
+  int rc = check_cache(src);
+  if (rc != PKV_OK) return rc;
+  rc = check_cache(dst);
+  if (rc != PKV_OK) return rc;
+  if ((src->kv_dtype != PKV_F32 && src->kv_dtype != PKV_BF16) ||
+      (dst->kv_dtype != PKV_I8 && dst->kv_dtype != PKV_FP8_E4M3))
+    return PKV_ERR_DTYPE;
+  if (src->num_blocks != dst->num_blocks || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim)
+    return PKV_ERR_SHAPE;
+  if (block_ids && n_ids < 0) return PKV_ERR_SHAPE;
+  const int64_t n = block_ids ? n_ids : src->num_blocks;
+  if (n * src->num_kv_heads > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
+  return launch_quantize(*src, *dst, block_ids, n_ids, static_cast<hipStream_t>(stream));
+}
+
+int pkv_gather(const pkv_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* context_lens, const int32_t* cu_seqlens, int32_t num_seqs,
+               void* k_out, void* v_out, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !cu_seqlens || !k_out || !v_out) return PKV_ERR_NULL;
+  if (!aligned16(k_out) || !aligned16(v_out)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * max_blocks_per_seq > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
+  return launch_gather(*cache, block_tables, max_blocks_per_seq, context_lens, cu_seqlens,
+                       num_seqs, k_out, v_out, static_cast<hipStream_t>(stream));
+}
+
+int pkv_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                        int32_t* bad_seq, void* stream) {
+  if (bad_seq) *bad_seq = -1;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks < 0 ||
+      max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens) return PKV_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  size_t nt = (size_t)num_seqs * max_blocks_per_seq;
+  int32_t* ht = static_cast<int32_t*>(malloc(nt * sizeof(int32_t)));
+  int32_t* hl = static_cast<int32_t*>(malloc((size_t)num_seqs * sizeof(int32_t)));
+  int rc = PKV_OK;
+  if (!ht || !hl) {
+    rc = PKV_ERR_HIP;
+  } else if (hipMemcpyAsync(ht, block_tables, nt * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+                 hipSuccess ||
+             hipMemcpyAsync(hl, context_lens, (size_t)num_seqs * sizeof(int32_t),
+                            hipMemcpyDeviceToHost, st) != hipSuccess ||
+             hipStreamSynchronize(st) != hipSuccess) {
+    rc = PKV_ERR_HIP;
+  } else {
+    for (int s = 0; s < num_seqs && rc == PKV_OK; ++s) {
+      int L = hl[s];
+      if (L < 0 || L > max_blocks_per_seq * PKV_BLOCK_SIZE) {
+        rc = PKV_ERR_RANGE;
+      } else {
+        int nb = (L + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+        for (int b = 0; b < nb; ++b) {
+          int32_t id = ht[(size_t)s * max_blocks_per_seq + b];
+          if (id < 0 || id >= num_blocks) {
+            rc = PKV_ERR_RANGE;
+            break;
+          }
+        }
+      }
+      if (rc != PKV_OK && bad_seq) *bad_seq = s;
+    }
+  }
+  free(ht);
+  free(hl);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal helpers shared by the pkv HIP sources (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "pkv.h"
+
+namespace pkv {
+
+constexpr int kBlock = PKV_BLOCK_SIZE;  // tokens per KV block
+constexpr int kWave = 64;               // CDNA wavefront width
+
+inline size_t elem_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_I8: return 1;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+// Launch through hipLaunchKernel so the launch status comes back directly
+// instead of through the thread's sticky last-error slot.
+template <typename... KArgs, typename... Args>
+inline int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  Args&&... args) {
+  std::tuple<KArgs...> packed(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... a) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&a)), ...);
+  }, packed);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0,
+                                 stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ---- device-side helpers ---------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---- launchers (defined in the .hip sources) --------------------------------
+
+int launch_slot_mapping(const int32_t* tables, int max_blocks, const int32_t* lens, int n,
+                        int32_t* slots, hipStream_t st);
+int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,
+                       int n, hipStream_t st);
+int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
+                  const int32_t* lens, const int32_t* cu, int num_seqs, void* ko, void* vo,
+                  hipStream_t st);
+int launch_quantize(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n_ids,
+                    hipStream_t st);
+
+struct DecodeArgs {
+  const pkv_cache_t* cache;
+  const void* q;
+  int q_dtype;
+  const int32_t* tables;
+  int max_blocks;
+  const int32_t* lens;
+  int num_seqs;
+  int num_q_heads;
+  float scale;
+  int partition_tokens;
+  void* workspace;
+  void* out;
+  int out_dtype;
+};
+int launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// Bytes of the split-context workspace and the offsets of its m and l parts.
+size_t decode_workspace_layout(int64_t rows, int n_parts, int D, size_t* off_m, size_t* off_l);
+
+}  // namespace pkv

@@ -1,0 +1,537 @@
+// Paged decode attention for gfx950.
+//
+// out[s][h] = sum_{t < L_s} softmax_t(scale * q[s][h] . k_t) v_t, with k_t and
+// v_t found through the block table (16-token blocks, page "LLM 推理优化深度
+// 解析", section "PagedAttention：vLLM 的显存碎片治理") and the G = Hq/Hkv query
+// heads of a group sharing KV head h / G (same page, section "MQA 与 GQA").
+//
+// Work split.  One wavefront per (sequence, KV head, partition of the context).
+// All G query heads of the group are handled by that wavefront, so every KV
+// byte is read from HBM once.  The launch index is decoded KV-head-fastest:
+// consecutive workgroups go to consecutive XCDs, so with 8 KV heads every
+// wavefront of one KV head runs on the same XCD and blocks shared between
+// sequences (a common prefix) are served by that XCD's L2.
+//
+// Per 16-token block (bf16 / 8-bit KV, MFMA kernel):
+//   1. the K and V tiles ([16][D], contiguous per (block, head)) are read with
+//      coalesced 16-byte loads -- lane l takes bytes [16 l, 16 l + 16) of each
+//      1 KiB slice -- one block ahead of the compute (register prefetch);
+//   2. 8-bit codes are widened to bf16 (exact), then both tiles are written to
+//      LDS with the 16-byte chunks of row t XOR-swizzled by t, so the
+//      row-per-lane and column-per-lane reads below are free of bank conflicts;
+//   3. S = K q^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = K rows
+//      (token m = lane % 16) and B = the group's queries (head n = lane % 16,
+//      zero for n >= G), D/32 instructions;
+//   4. online softmax in base 2: S is scaled by scale*log2(e) (times the
+//      block's K scale for 8-bit KV), masked past L by selection, the block
+//      maximum per head is shuffled across the four lanes holding that head,
+//      and the running maximum only moves (rescaling the accumulator) when the
+//      block maximum exceeds it by more than 8, so p <= 2^8;
+//   5. O^T += V^T P on the matrix cores: v_mfma_f32_16x16x16_bf16 with A = V^T
+//      read transposed from LDS and B = P, which the QK^T result already holds
+//      in the B-operand layout (4 consecutive tokens per lane, head = lane % 16);
+//      for 8-bit KV, P is multiplied by the block's V scale first.
+// The head index of a lane is lane % 16 in S, P and O alike, so the running
+// maximum and sum stay lane-local.
+//
+// Split context: with partition_tokens > 0 each wavefront writes its
+// partition's (max, sum, normalised output) to the workspace and a second
+// kernel combines them with the log-sum-exp rule; a sequence that fits in one
+// partition is written directly.
+#include "common.hpp"
+
+namespace pkv {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+
+enum { KV_BF16 = 0, KV_I8 = 1, KV_FP8 = 2 };
+enum { OUT_F32 = 0, OUT_BF16 = 1 };
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of bf16
+// rows of D elements, chunks XOR-swizzled by the row index.
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  constexpr int kChunks = D / 8;
+  return row * (D * 2) + ((chunk ^ (row & (kChunks - 1))) << 4);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_of_int(float lo, float hi) {
+  // lo and hi are small integers: their binary32 upper halves are exact bf16
+  return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+}
+
+// 16 8-bit codes -> 16 bf16 values (two 16-byte chunks), exact.
+template <int KV>
+__device__ __forceinline__ void widen16(uint4 c, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (KV == KV_I8) {
+      const float f0 = (float)(int8_t)(w[i] & 0xFF);
+      const float f1 = (float)(int8_t)((w[i] >> 8) & 0xFF);
+      const float f2 = (float)(int8_t)((w[i] >> 16) & 0xFF);
+      const float f3 = (float)(int8_t)(w[i] >> 24);
+      o[2 * i] = pack_bf16_of_int(f0, f1);
+      o[2 * i + 1] = pack_bf16_of_int(f2, f3);
+    } else {
+      bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+      bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+      o[2 * i] = __builtin_bit_cast(uint32_t, a);
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
+    }
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+template <int D, int OUT>
+__device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v) {
+  if constexpr (OUT == OUT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+  } else {
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel: q bf16; KV bf16, int8 or E4M3; D = 64 or 128; G <= 16.
+template <int D, int KV, int OUT>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ vc, const float* __restrict__ ksc,
+    const float* __restrict__ vsc, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ lens, int hq, int hkv, int G, int num_blocks, float scale_log2,
+    int part_blocks, int n_parts, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o, void* __restrict__ out) {
+  constexpr int kEsz = (KV == KV_BF16) ? 2 : 1;
+  constexpr int kTile = kBlock * D * kEsz;  // bytes of one (block, head) tile in HBM
+  constexpr int kLoads = kTile / 1024;      // 16-byte loads per lane per tile
+  constexpr int kRowB = D * 2;              // bytes of one bf16 row in LDS
+  constexpr int kNKK = D / 32;              // QK^T instructions per block
+  constexpr int kNT = D / 16;               // PV instructions per block
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * kRowB];
+
+  const int lane = threadIdx.x;
+  const int j = lane >> 4;   // token quad (rows 4j..4j+3 of S) / k-slice
+  const int n = lane & 15;   // head column
+  const int g = blockIdx.x % hkv;
+  const int r = blockIdx.x / hkv;
+  const int p = r % n_parts;
+  const int s = r / n_parts;
+  int L = lens[s];
+  if (L < 0 || L > max_blocks * kBlock) L = 0;
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int parts_s = (nblk + part_blocks - 1) / part_blocks;
+  const int b0 = p * part_blocks;
+  const int b1 = min(b0 + part_blocks, nblk);
+  const int h = g * G + n;
+  const bool has_head = n < G;
+
+  f32x4 acc[kNT];
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (b0 >= b1) {
+    if (p == 0 && has_head) {  // empty sequence: zero row
+#pragma unroll
+      for (int t = 0; t < kNT; ++t)
+        store_out4<D, OUT>(out, ((size_t)s * hq + h) * D + 16 * t + 4 * j, acc[t]);
+    }
+    return;
+  }
+
+  // queries of this group as the B operand of S = K q^T: lane (j, n) holds
+  // q[h][32 kk + 8 j .. + 8] for each kk
+  bf16x8 qop[kNKK];
+  {
+    const uint16_t* qrow = q + ((size_t)s * hq + (has_head ? h : g * G)) * D;
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * j);
+      qop[kk] = has_head ? v : bf16x8{};
+    }
+  }
+
+  const int32_t* trow = tables + (size_t)s * max_blocks;
+  const size_t blk_stride = (size_t)hkv * kTile;
+  const uint8_t* kbase = kc + (size_t)g * kTile;
+  const uint8_t* vbase = vc + (size_t)g * kTile;
+
+  float m = -INFINITY;  // running reference maximum (log2 units)
+  float lsum = 0.f;     // this lane's share of the softmax denominator
+
+  uint4 kr[kLoads], vr[kLoads];
+  int phys = trow[b0];
+  bool phys_ok = phys >= 0 && phys < num_blocks;
+  if (phys_ok) {
+    const uint8_t* kp = kbase + (size_t)phys * blk_stride;
+    const uint8_t* vp = vbase + (size_t)phys * blk_stride;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      kr[i] = *reinterpret_cast<const uint4*>(kp + i * 1024 + lane * 16);
+      vr[i] = *reinterpret_cast<const uint4*>(vp + i * 1024 + lane * 16);
+    }
+  }
+
+  for (int b = b0; b < b1; ++b) {
+    const int cur = phys;
+    const bool cur_ok = phys_ok;
+    const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
+
+    // ---- stage the current tiles into LDS as bf16 (V rows past L zeroed)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      if constexpr (KV == KV_BF16) {
+        const int chunk = i * 64 + lane;          // 16-byte chunk of the tile
+        const int row = chunk / (D / 8), ch = chunk % (D / 8);
+        *reinterpret_cast<uint4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
+        *reinterpret_cast<uint4*>(lds_v + lds_off<D>(row, ch)) =
+            row < valid ? vr[i] : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        const int byte = (i * 64 + lane) * 16;    // first code of this chunk
+        const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
+        uint4 klo, khi, vlo, vhi;
+        widen16<KV>(kr[i], klo, khi);
+        widen16<KV>(vr[i], vlo, vhi);
+        if (row >= valid) vlo = vhi = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
+        *reinterpret_cast<uint4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
+        *reinterpret_cast<uint4*>(lds_v + lds_off<D>(row, col / 8)) = vlo;
+        *reinterpret_cast<uint4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
+      }
+    }
+    float kscale = 1.f, vscale = 1.f;
+    if constexpr (KV != KV_BF16) {
+      if (cur_ok) {
+        kscale = ksc[(size_t)cur * hkv + g];
+        vscale = vsc[(size_t)cur * hkv + g];
+      }
+    }
+
+    // ---- prefetch the next block's tiles
+    if (b + 1 < b1) {
+      phys = trow[b + 1];
+      phys_ok = phys >= 0 && phys < num_blocks;
+      if (phys_ok) {
+        const uint8_t* kp = kbase + (size_t)phys * blk_stride;
+        const uint8_t* vp = vbase + (size_t)phys * blk_stride;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          kr[i] = *reinterpret_cast<const uint4*>(kp + i * 1024 + lane * 16);
+          vr[i] = *reinterpret_cast<const uint4*>(vp + i * 1024 + lane * 16);
+        }
+      }
+    }
+
+    // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
+    f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk) {
+      bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
+      sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
+    }
+
+    // ---- online softmax (base 2)
+    const float cb = scale_log2 * kscale;
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (4 * j + i < valid) ? sv[i] * cb : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const bool bump = mx > m + kRescaleSlack;
+    if (__any(bump)) {
+      const float mnew = bump ? mx : m;
+      const float alpha = exp2f(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
+      m = mnew;
+    }
+    bf16x4 pop;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pe = exp2f(x[i] - m);
+      lsum += pe;
+      pop[i] = static_cast<__bf16>(pe * vscale);
+    }
+
+    // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n]
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      const int d = 16 * t + n;
+      u16x4 vv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vv[i] = *reinterpret_cast<const uint16_t*>(lds_v + lds_off<D>(4 * j + i, d >> 3) +
+                                                   (d & 7) * 2);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pop,
+                                                        acc[t], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
+  float lt = lsum + __shfl_xor(lsum, 16, kWave);
+  lt += __shfl_xor(lt, 32, kWave);
+  if (!has_head) return;
+  const float inv = 1.0f / lt;
+  if (parts_s == 1) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+      store_out4<D, OUT>(out, ((size_t)s * hq + h) * D + 16 * t + 4 * j, acc[t] * inv);
+  } else {
+    const size_t row = ((size_t)s * hq + h) * n_parts + p;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+      *reinterpret_cast<f32x4*>(ws_o + row * D + 16 * t + 4 * j) = acc[t] * inv;
+    if (j == 0) {
+      ws_m[row] = m;
+      ws_l[row] = lt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (q and KV binary32): one wavefront per (sequence, KV head,
+// partition); tokens are taken one at a time, each dot product reduced across
+// the wavefront, accumulation in binary32.
+template <int D, int OUT, int MAXG>
+__global__ __launch_bounds__(64) void decode_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens, int hq,
+    int hkv, int G, int num_blocks, float scale_log2, int part_blocks, int n_parts,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+    void* __restrict__ out) {
+  constexpr int kPer = D / kWave;
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % hkv;
+  const int r = blockIdx.x / hkv;
+  const int p = r % n_parts;
+  const int s = r / n_parts;
+  int L = lens[s];
+  if (L < 0 || L > max_blocks * kBlock) L = 0;
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int parts_s = (nblk + part_blocks - 1) / part_blocks;
+  const int b0 = p * part_blocks;
+  const int b1 = min(b0 + part_blocks, nblk);
+
+  float qv[MAXG][kPer], acc[MAXG][kPer], m[MAXG], l[MAXG];
+#pragma unroll
+  for (int hh = 0; hh < MAXG; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      acc[hh][e] = 0.f;
+      qv[hh][e] = 0.f;
+      if (hh < G) qv[hh][e] = q[((size_t)s * hq + g * G + hh) * D + lane * kPer + e];
+    }
+  }
+  if (b0 >= b1) {
+    if (p == 0) {
+#pragma unroll
+      for (int hh = 0; hh < MAXG; ++hh)
+        if (hh < G)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            const size_t o = ((size_t)s * hq + g * G + hh) * D + lane * kPer + e;
+            if constexpr (OUT == OUT_F32) static_cast<float*>(out)[o] = 0.f;
+            else static_cast<uint16_t*>(out)[o] = 0;
+          }
+    }
+    return;
+  }
+  const int32_t* trow = tables + (size_t)s * max_blocks;
+  for (int b = b0; b < b1; ++b) {
+    const int phys = trow[b];
+    if (phys < 0 || phys >= num_blocks) continue;
+    const int valid = min(kBlock, L - b * kBlock);
+    for (int o = 0; o < valid; ++o) {
+      const size_t base = (((size_t)phys * hkv + g) * kBlock + o) * D + lane * kPer;
+      float kv[kPer], vv[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        kv[e] = kc[base + e];
+        vv[e] = vc[base + e];
+      }
+#pragma unroll
+      for (int hh = 0; hh < MAXG; ++hh) {
+        if (hh >= G) break;
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) dot += qv[hh][e] * kv[e];
+        const float xl = wave_sum(dot) * scale_log2;
+        const float mn = fmaxf(m[hh], xl);
+        const float alpha = exp2f(m[hh] - mn);
+        const float pe = exp2f(xl - mn);
+        l[hh] = l[hh] * alpha + pe;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[hh][e] = acc[hh][e] * alpha + pe * vv[e];
+        m[hh] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < MAXG; ++hh) {
+    if (hh >= G) break;
+    const size_t row = (size_t)s * hq + g * G + hh;
+    const float inv = 1.0f / l[hh];
+    if (parts_s == 1) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const size_t o = row * D + lane * kPer + e;
+        if constexpr (OUT == OUT_F32) static_cast<float*>(out)[o] = acc[hh][e] * inv;
+        else static_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(acc[hh][e] * inv);
+      }
+    } else {
+      const size_t pr = row * n_parts + p;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) ws_o[pr * D + lane * kPer + e] = acc[hh][e] * inv;
+      if (lane == 0) {
+        ws_m[pr] = m[hh];
+        ws_l[pr] = l[hh];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-partition combine: one wavefront per (sequence, query head) row with
+// more than one partition; M = max_p m_p, w_p = 2^(m_p - M) l_p,
+// out = sum_p w_p o_p / sum_p w_p.
+template <int D, int OUT>
+__global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws_m,
+                                                    const float* __restrict__ ws_l,
+                                                    const float* __restrict__ ws_o,
+                                                    const int32_t* __restrict__ lens,
+                                                    int max_blocks, int hq, int part_blocks,
+                                                    int n_parts, void* __restrict__ out) {
+  constexpr int kPer = D / kWave;
+  const int row = blockIdx.x;
+  const int s = row / hq;
+  const int lane = threadIdx.x;
+  int L = lens[s];
+  if (L < 0 || L > max_blocks * kBlock) L = 0;
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int parts = (nblk + part_blocks - 1) / part_blocks;
+  if (parts <= 1) return;
+  const float* mrow = ws_m + (size_t)row * n_parts;
+  const float* lrow = ws_l + (size_t)row * n_parts;
+  float M = -INFINITY;
+  for (int pp = 0; pp < parts; ++pp) M = fmaxf(M, mrow[pp]);
+  float a[kPer] = {}, den = 0.f;
+  for (int pp = 0; pp < parts; ++pp) {
+    const float w = exp2f(mrow[pp] - M) * lrow[pp];
+    den += w;
+    const float* o = ws_o + ((size_t)row * n_parts + pp) * D + lane * kPer;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) a[e] += w * o[e];
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const size_t o = (size_t)row * D + lane * kPer + e;
+    if constexpr (OUT == OUT_F32) static_cast<float*>(out)[o] = a[e] * inv;
+    else static_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(a[e] * inv);
+  }
+}
+
+struct Plan {
+  int part_blocks, n_parts;
+  float *ws_m, *ws_l, *ws_o;
+};
+
+template <int D, int OUT>
+int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
+  const pkv_cache_t& c = *a.cache;
+  const int hkv = c.num_kv_heads, hq = a.num_q_heads, G = hq / hkv;
+  const float sl2 = a.scale * kLog2e;
+  dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts)), block(kWave);
+  int rc;
+  switch (c.kv_dtype) {
+    case PKV_F32:
+      rc = launch(decode_f32_kernel<D, OUT, 16>, grid, block, st, (const float*)a.q,
+                  (const float*)c.k_cache, (const float*)c.v_cache, a.tables, a.max_blocks,
+                  a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
+                  pl.ws_l, pl.ws_o, a.out);
+      break;
+    case PKV_BF16:
+      rc = launch(decode_mfma_kernel<D, KV_BF16, OUT>, grid, block, st, (const uint16_t*)a.q,
+                  (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache, (const float*)nullptr,
+                  (const float*)nullptr, a.tables, a.max_blocks, a.lens, hq, hkv, G,
+                  c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m, pl.ws_l, pl.ws_o,
+                  a.out);
+      break;
+    case PKV_I8:
+      rc = launch(decode_mfma_kernel<D, KV_I8, OUT>, grid, block, st, (const uint16_t*)a.q,
+                  (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache,
+                  (const float*)c.k_scale, (const float*)c.v_scale, a.tables, a.max_blocks,
+                  a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
+                  pl.ws_l, pl.ws_o, a.out);
+      break;
+    default:
+      rc = launch(decode_mfma_kernel<D, KV_FP8, OUT>, grid, block, st, (const uint16_t*)a.q,
+                  (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache,
+                  (const float*)c.k_scale, (const float*)c.v_scale, a.tables, a.max_blocks,
+                  a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
+                  pl.ws_l, pl.ws_o, a.out);
+      break;
+  }
+  if (rc != PKV_OK || pl.n_parts <= 1) return rc;
+  dim3 rgrid((unsigned)((int64_t)a.num_seqs * hq));
+  return launch(reduce_kernel<D, OUT>, rgrid, block, st, (const float*)pl.ws_m,
+                (const float*)pl.ws_l, (const float*)pl.ws_o, a.lens, a.max_blocks, hq,
+                pl.part_blocks, pl.n_parts, a.out);
+}
+
+}  // namespace
+
+// Workspace layout for a split launch with P partitions and R = B * Hq rows:
+// o [R][P][D] binary32, then m [R][P], then l [R][P], each 256-byte aligned.
+size_t decode_workspace_layout(int64_t rows, int n_parts, int D, size_t* off_m, size_t* off_l) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t o_bytes = up((size_t)rows * n_parts * D * 4);
+  size_t m_bytes = up((size_t)rows * n_parts * 4);
+  if (off_m) *off_m = o_bytes;
+  if (off_l) *off_l = o_bytes + m_bytes;
+  return o_bytes + 2 * m_bytes;
+}
+
+int launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const pkv_cache_t& c = *a.cache;
+  Plan pl;
+  pl.part_blocks = a.partition_tokens > 0 ? a.partition_tokens / kBlock : a.max_blocks;
+  pl.n_parts = (a.max_blocks + pl.part_blocks - 1) / pl.part_blocks;
+  pl.ws_m = pl.ws_l = pl.ws_o = nullptr;
+  if (pl.n_parts > 1) {
+    size_t om, ol;
+    decode_workspace_layout((int64_t)a.num_seqs * a.num_q_heads, pl.n_parts, c.head_dim, &om, &ol);
+    uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+    pl.ws_o = reinterpret_cast<float*>(ws);
+    pl.ws_m = reinterpret_cast<float*>(ws + om);
+    pl.ws_l = reinterpret_cast<float*>(ws + ol);
+  }
+  const bool bf16_out = a.out_dtype == PKV_BF16;
+  if (c.head_dim == 128)
+    return bf16_out ? run_d_out<128, OUT_BF16>(a, pl, st) : run_d_out<128, OUT_F32>(a, pl, st);
+  return bf16_out ? run_d_out<64, OUT_BF16>(a, pl, st) : run_d_out<64, OUT_F32>(a, pl, st);
+}
+
+}  // namespace pkv

@@ -224,3 +224,34 @@ def make(cfg: int, seed: Optional[int] = None, quant: Optional[str] = None, **ov
                     k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, q=q,
                     scale=np.float32(1.0 / math.sqrt(D)), partition_tokens=spec["part"],
                     quant=quant if cfg == 5 else None)
+
+
+def to_device(wl: Workload, device="cuda") -> dict:
+    """Copy a workload's arrays to the GPU as torch tensors (bf16 bit patterns
+    become torch.bfloat16)."""
+    import torch
+
+    def dev(a, kind):
+        if a is None:
+            return None
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return dict(q=dev(wl.q, wl.q_dtype), k_pool=dev(wl.k_pool, wl.kv_dtype),
+                v_pool=dev(wl.v_pool, wl.kv_dtype), k_new=dev(wl.k_new, wl.kv_dtype),
+                v_new=dev(wl.v_new, wl.kv_dtype), tables=dev(wl.tables, "i32"),
+                lens=dev(wl.lens, "i32"))
+
+
+def from_device(t) -> np.ndarray:
+    """torch tensor -> numpy in storage dtype (bf16 as uint16 bit patterns)."""
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
