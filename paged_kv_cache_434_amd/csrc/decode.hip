@@ -15,7 +15,10 @@
 // Per 16-token block (bf16 / 8-bit KV, MFMA kernel):
 //   1. the K and V tiles ([16][D], contiguous per (block, head)) are read with
 //      coalesced 16-byte loads -- lane l takes bytes [16 l, 16 l + 16) of each
-//      1 KiB slice -- one block ahead of the compute (register prefetch);
+//      1 KiB slice -- two blocks ahead of the compute (two register buffers);
+//      the partition's block-table entries are loaded once, 64 per vector
+//      load, and broadcast from a lane, so no table read sits in front of a
+//      tile load;
 //   2. 8-bit codes are widened to bf16 (exact), then both tiles are written to
 //      LDS with the 16-byte chunks of row t XOR-swizzled by t, so the
 //      row-per-lane and column-per-lane reads below are free of bank conflicts;
@@ -49,12 +52,30 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+// native clang vector (HIP's u32x4 is a wrapper struct that can keep arrays of
+// it out of registers)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// initial running maximum: finite, so exp2(x - m) of a masked logit (-inf)
+// is 0 even before the first valid token
+constexpr float kNoMax = -3.0e38f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 
 enum { KV_BF16 = 0, KV_I8 = 1, KV_FP8 = 2 };
 enum { OUT_F32 = 0, OUT_BF16 = 1 };
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes); loads past `bytes` return
+// zero and do not access memory.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of bf16
 // rows of D elements, chunks XOR-swizzled by the row index.
@@ -71,8 +92,8 @@ __device__ __forceinline__ uint32_t pack_bf16_of_int(float lo, float hi) {
 
 // 16 8-bit codes -> 16 bf16 values (two 16-byte chunks), exact.
 template <int KV>
-__device__ __forceinline__ void widen16(uint4 c, uint4& lo, uint4& hi) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+__device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
+  const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -90,8 +111,8 @@ __device__ __forceinline__ void widen16(uint4 c, uint4& lo, uint4& hi) {
       o[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
     }
   }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+  hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
 template <int D, int OUT>
@@ -171,119 +192,140 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const uint8_t* kbase = kc + (size_t)g * kTile;
   const uint8_t* vbase = vc + (size_t)g * kTile;
 
-  float m = -INFINITY;  // running reference maximum (log2 units)
-  float lsum = 0.f;     // this lane's share of the softmax denominator
+  float m = kNoMax;   // running reference maximum (log2 units)
+  float lsum = 0.f;   // this lane's share of the softmax denominator
 
-  uint4 kr[kLoads], vr[kLoads];
-  int phys = trow[b0];
-  bool phys_ok = phys >= 0 && phys < num_blocks;
-  if (phys_ok) {
-    const uint8_t* kp = kbase + (size_t)phys * blk_stride;
-    const uint8_t* vp = vbase + (size_t)phys * blk_stride;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      kr[i] = *reinterpret_cast<const uint4*>(kp + i * 1024 + lane * 16);
-      vr[i] = *reinterpret_cast<const uint4*>(vp + i * 1024 + lane * 16);
-    }
-  }
-
-  for (int b = b0; b < b1; ++b) {
-    const int cur = phys;
-    const bool cur_ok = phys_ok;
-    const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
-
-    // ---- stage the current tiles into LDS as bf16 (V rows past L zeroed)
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      if constexpr (KV == KV_BF16) {
-        const int chunk = i * 64 + lane;          // 16-byte chunk of the tile
-        const int row = chunk / (D / 8), ch = chunk % (D / 8);
-        *reinterpret_cast<uint4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
-        *reinterpret_cast<uint4*>(lds_v + lds_off<D>(row, ch)) =
-            row < valid ? vr[i] : make_uint4(0u, 0u, 0u, 0u);
-      } else {
-        const int byte = (i * 64 + lane) * 16;    // first code of this chunk
-        const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
-        uint4 klo, khi, vlo, vhi;
-        widen16<KV>(kr[i], klo, khi);
-        widen16<KV>(vr[i], vlo, vhi);
-        if (row >= valid) vlo = vhi = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
-        *reinterpret_cast<uint4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
-        *reinterpret_cast<uint4*>(lds_v + lds_off<D>(row, col / 8)) = vlo;
-        *reinterpret_cast<uint4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
-      }
-    }
-    float kscale = 1.f, vscale = 1.f;
+  // The partition is walked in chunks of up to 64 blocks.  Per chunk, lane i
+  // loads block-table entry i (and, for 8-bit KV, that block's two scales);
+  // each block's id is then broadcast from its lane.  Tile loads go through
+  // buffer descriptors built per block: a block past the chunk or with an
+  // id outside the pool gets a zero-length descriptor, so its loads return
+  // zeros without touching memory.  Every iteration therefore issues the
+  // same loads and the wait counts stay exact: while block b is computed,
+  // the loads of blocks b+1 and b+2 are in flight in two register buffers.
+  for (int c0 = b0; c0 < b1; c0 += 64) {
+    const int c1 = min(c0 + 64, b1);
+    const int tab = (c0 + lane < c1) ? trow[c0 + lane] : -1;
+    float ks_l = 1.f, vs_l = 1.f;
     if constexpr (KV != KV_BF16) {
-      if (cur_ok) {
-        kscale = ksc[(size_t)cur * hkv + g];
-        vscale = vsc[(size_t)cur * hkv + g];
+      if (tab >= 0 && tab < num_blocks) {
+        ks_l = ksc[(size_t)tab * hkv + g];
+        vs_l = vsc[(size_t)tab * hkv + g];
       }
     }
-
-    // ---- prefetch the next block's tiles
-    if (b + 1 < b1) {
-      phys = trow[b + 1];
-      phys_ok = phys >= 0 && phys < num_blocks;
-      if (phys_ok) {
-        const uint8_t* kp = kbase + (size_t)phys * blk_stride;
-        const uint8_t* vp = vbase + (size_t)phys * blk_stride;
+    auto phys_of = [&](int b) -> int {
+      return b < c1 ? __builtin_amdgcn_readlane(tab, b - c0) : -1;
+    };
+    auto load_tile = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], int ph) {
+      const bool in = ph >= 0 && ph < num_blocks;
+      const size_t off = in ? (size_t)ph * blk_stride : 0;
+      const rsrc_t rk = make_rsrc(kbase + off, in ? kTile : 0);
+      const rsrc_t rv = make_rsrc(vbase + off, in ? kTile : 0);
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-          kr[i] = *reinterpret_cast<const uint4*>(kp + i * 1024 + lane * 16);
-          vr[i] = *reinterpret_cast<const uint4*>(vp + i * 1024 + lane * 16);
+      for (int i = 0; i < kLoads; ++i) {
+        kr[i] = buffer_load16(rk, i * 1024 + lane * 16);
+        vr[i] = buffer_load16(rv, i * 1024 + lane * 16);
+      }
+    };
+
+    // Stage block b from (kr, vr) into LDS, refill the buffer with block
+    // b+2, then run QK^T, the softmax update and PV for block b.
+    auto process = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], int& ph, int b) {
+      const int cur = ph;
+      const bool cur_ok = cur >= 0 && cur < num_blocks;
+      const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
+
+      // ---- stage into LDS as bf16 (V rows past L zeroed)
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        if constexpr (KV == KV_BF16) {
+          const int chunk = i * 64 + lane;          // 16-byte chunk of the tile
+          const int row = chunk / (D / 8), ch = chunk % (D / 8);
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) =
+              row < valid ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          const int byte = (i * 64 + lane) * 16;    // first code of this chunk
+          const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
+          u32x4 klo, khi, vlo, vhi;
+          widen16<KV>(kr[i], klo, khi);
+          widen16<KV>(vr[i], vlo, vhi);
+          if (row >= valid) vlo = vhi = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
         }
       }
-    }
+      float kscale = 1.f, vscale = 1.f;
+      if constexpr (KV != KV_BF16) {
+        if (b < c1) {
+          kscale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ks_l), b - c0));
+          vscale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs_l), b - c0));
+        }
+      }
 
-    // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
-    f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < kNKK; ++kk) {
-      bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
-      sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
-    }
+      // ---- refill this buffer with block b+2 (zero-length if absent)
+      ph = phys_of(b + 2);
+      load_tile(kr, vr, ph);
 
-    // ---- online softmax (base 2)
-    const float cb = scale_log2 * kscale;
-    float x[4];
-    float mx = -INFINITY;
+      // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
+      f32x4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (4 * j + i < valid) ? sv[i] * cb : -INFINITY;
-      mx = fmaxf(mx, x[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const bool bump = mx > m + kRescaleSlack;
-    if (__any(bump)) {
-      const float mnew = bump ? mx : m;
-      const float alpha = exp2f(m - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
-      m = mnew;
-    }
-    bf16x4 pop;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pe = exp2f(x[i] - m);
-      lsum += pe;
-      pop[i] = static_cast<__bf16>(pe * vscale);
-    }
+      for (int kk = 0; kk < kNKK; ++kk) {
+        bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
+      }
 
-    // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n]
+      // ---- online softmax (base 2)
+      const float cb = scale_log2 * kscale;
+      float x[4];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-      const int d = 16 * t + n;
-      u16x4 vv;
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (4 * j + i < valid) ? sv[i] * cb : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const bool bump = mx > m + kRescaleSlack;
+      if (__any(bump)) {
+        const float mnew = bump ? mx : m;
+        const float alpha = exp2f(m - mnew);
+        lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vv[i] = *reinterpret_cast<const uint16_t*>(lds_v + lds_off<D>(4 * j + i, d >> 3) +
-                                                   (d & 7) * 2);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pop,
-                                                        acc[t], 0, 0, 0);
+        for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
+        m = mnew;
+      }
+      bf16x4 pop;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = exp2f(x[i] - m);
+        lsum += pe;
+        pop[i] = static_cast<__bf16>(pe * vscale);
+      }
+
+      // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n]
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        const int d = 16 * t + n;
+        u16x4 vv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vv[i] = *reinterpret_cast<const uint16_t*>(lds_v + lds_off<D>(4 * j + i, d >> 3) +
+                                                     (d & 7) * 2);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pop,
+                                                          acc[t], 0, 0, 0);
+      }
+    };
+
+    u32x4 kr0[kLoads], vr0[kLoads], kr1[kLoads], vr1[kLoads];
+    int ph0 = phys_of(c0), ph1 = phys_of(c0 + 1);
+    load_tile(kr0, vr0, ph0);
+    load_tile(kr1, vr1, ph1);
+    for (int b = c0; b < c1; b += 2) {
+      process(kr0, vr0, ph0, b);
+      process(kr1, vr1, ph1, b + 1);   // past c1: masked, no memory traffic
     }
   }
 
