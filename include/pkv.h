@@ -118,10 +118,11 @@ int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
 int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
                     const int32_t* slot_mapping, int32_t n, void* stream);
 
-/* Workspace bytes pkv_attention_decode needs for a split-context launch
- * (partition_tokens > 0): per (sequence, query head, partition) a running
+/* Workspace bytes pkv_attention_decode / pkv_decode_step need for a
+ * split-context launch: per (sequence, query head, partition) a running
  * maximum, a sum and a head_dim output row, all binary32, plus alignment.
- * Returns 0 when partition_tokens == 0 (no workspace needed). */
+ * Returns 0 when no split happens (partition_tokens == 0, or one partition
+ * covers max_blocks_per_seq * 16 tokens): no workspace needed then. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_tokens);
 
@@ -152,6 +153,23 @@ int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                          float scale, int32_t partition_tokens, void* workspace,
                          size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
+
+/* One decode step for one layer, in a single attention launch: appends each
+ * sequence's new token at position t = context_lens[s] - 1 (slot
+ * block_tables[s][t / 16] * 16 + t % 16, [MGMT] section 二 append_slot) and
+ * then computes the same attention as pkv_attention_decode, with the new
+ * token included.  Equivalent to pkv_slot_mapping + pkv_cache_write +
+ * pkv_attention_decode, and leaves the pool in the same state.
+ *   k, v: device [num_seqs][num_kv_heads][head_dim] of cache->kv_dtype (the
+ *     new token of each sequence; ignored for sequences with length 0)
+ * kv_dtype must be PKV_F32 or PKV_BF16; other arguments as for
+ * pkv_attention_decode.  Tables must not map the new token's slot of two
+ * sequences to the same physical row. */
+int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, const void* k,
+                    const void* v, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    float scale, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
 
 /* KV quantization ([MGMT] section 四, with one symmetric binary32 scale per
  * (block, KV head) tile): for each listed block b and KV head g, with

@@ -63,6 +63,8 @@ def _load():
             "pkv_decode_default_partition": (I32, [I32, I32, I32]),
             "pkv_attention_decode": (ctypes.c_int, [C, P, I32, P, I32, P, I32, I32, F, I32, P,
                                                     ctypes.c_size_t, P, I32, P]),
+            "pkv_decode_step": (ctypes.c_int, [C, P, I32, P, P, P, I32, P, I32, I32, F, I32, P,
+                                               ctypes.c_size_t, P, I32, P]),
             "pkv_quantize": (ctypes.c_int, [C, C, P, I32, P]),
             "pkv_gather": (ctypes.c_int, [C, P, I32, P, P, I32, P, P, P]),
             "pkv_validate_tables": (ctypes.c_int, [P, I32, P, I32, I32,
@@ -83,7 +85,8 @@ def lib():
 
 EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_mapping",
                     "pkv_cache_write", "pkv_decode_workspace_bytes",
-                    "pkv_decode_default_partition", "pkv_attention_decode", "pkv_quantize",
+                    "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
+                    "pkv_quantize",
                     "pkv_gather", "pkv_validate_tables")
 
 
@@ -203,7 +206,7 @@ def alloc_workspace(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, partiti
 
 def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: float,
                      partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
-                     stream=None):
+                     stream=None, _append=None):
     """out[s][h] = softmax(scale q k^T) v over each sequence's paged context."""
     torch = _torch()
     qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
@@ -225,13 +228,34 @@ def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: fl
     if ws_need and workspace is None:
         workspace = alloc_workspace(B, Hq, D, maxb, partition_tokens, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("pkv_attention_decode",
-           _load().pkv_attention_decode(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd],
-                                        _ptr(block_tables), maxb, _ptr(context_lens), B, Hq,
-                                        ctypes.c_float(scale), partition_tokens,
-                                        _ptr(workspace), ws_bytes, _ptr(out), DTYPE_CODES[odn],
-                                        _stream(stream)))
+    common = (_ptr(block_tables), maxb, _ptr(context_lens), B, Hq, ctypes.c_float(scale),
+              partition_tokens, _ptr(workspace), ws_bytes, _ptr(out), DTYPE_CODES[odn],
+              _stream(stream))
+    if _append is None:
+        _check("pkv_attention_decode",
+               _load().pkv_attention_decode(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd],
+                                            *common))
+    else:
+        _check("pkv_decode_step",
+               _load().pkv_decode_step(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd],
+                                       _ptr(_append[0]), _ptr(_append[1]), *common))
     return out
+
+
+def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, scale: float,
+                partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
+                stream=None):
+    """Append each sequence's new token at position context_lens - 1, then
+    attention over the whole context (one attention launch)."""
+    torch = _torch()
+    sd = _storage_dtype(cache.kv_dtype)
+    _need(k_new, "k_new", sd, 3)
+    _need(v_new, "v_new", sd, 3)
+    B = q.shape[0]
+    if tuple(k_new.shape) != (B, cache.num_kv_heads, cache.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
+    return attention_decode(cache, q, block_tables, context_lens, scale, partition_tokens,
+                            workspace, out, out_dtype, stream, _append=(k_new, v_new))
 
 
 def quantize(src: PagedCache, dst: PagedCache, block_ids=None, stream=None):

@@ -104,11 +104,12 @@ int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
   return part >= max_ctx ? 0 : (int32_t)part;
 }
 
-int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
-                         const int32_t* block_tables, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                         float scale, int32_t partition_tokens, void* workspace,
-                         size_t workspace_bytes, void* out, int32_t out_dtype, void* stream) {
+static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         const void* k_new, const void* v_new, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, float scale,
+                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                         void* out, int32_t out_dtype, void* stream, bool append) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   if (elem_bytes(q_dtype) == 0 || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
@@ -124,6 +125,11 @@ int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
+  if (append) {
+    if (cache->kv_dtype != PKV_F32 && cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (!k_new || !v_new) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_UNSUPPORTED;
+  }
   if (!q || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(out)) return PKV_ERR_UNSUPPORTED;
   const int np = n_parts_of(max_blocks_per_seq, partition_tokens);
@@ -134,9 +140,31 @@ int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
   }
-  DecodeArgs a{cache, q, q_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-               num_q_heads, scale, partition_tokens, workspace, out, out_dtype};
+  DecodeArgs a{cache,     q,          q_dtype,   block_tables,     max_blocks_per_seq,
+               context_lens, num_seqs, num_q_heads, scale,          partition_tokens,
+               workspace, out,        out_dtype, append ? k_new : nullptr,
+               append ? v_new : nullptr};
   return launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* out, int32_t out_dtype, void* stream) {
+  return decode_common(cache, q, q_dtype, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, partition_tokens, workspace,
+                       workspace_bytes, out, out_dtype, stream, false);
+}
+
+int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, const void* k,
+                    const void* v, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    float scale, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, void* out, int32_t out_dtype, void* stream) {
+  return decode_common(cache, q, q_dtype, k, v, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, partition_tokens, workspace, workspace_bytes,
+                       out, out_dtype, stream, true);
 }
 
 int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,

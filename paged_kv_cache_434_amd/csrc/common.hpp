@@ -90,6 +90,8 @@ struct DecodeArgs {
   void* workspace;
   void* out;
   int out_dtype;
+  const void* k_new;   // fused append of position L-1 (decode step), or nullptr
+  const void* v_new;
 };
 int launch_decode(const DecodeArgs& a, hipStream_t st);
 

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const float* __restrict__ vsc, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ lens, int hq, int hkv, int G, int num_blocks, float scale_log2,
     int part_blocks, int n_parts, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o, void* __restrict__ out) {
+    float* __restrict__ ws_o, void* __restrict__ out, const uint8_t* __restrict__ kn,
+    const uint8_t* __restrict__ vn, uint8_t* __restrict__ kc_w, uint8_t* __restrict__ vc_w) {
   constexpr int kEsz = (KV == KV_BF16) ? 2 : 1;
   constexpr int kTile = kBlock * D * kEsz;  // bytes of one (block, head) tile in HBM
   constexpr int kLoads = kTile / 1024;      // 16-byte loads per lane per tile
@@ -191,6 +192,33 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const size_t blk_stride = (size_t)hkv * kTile;
   const uint8_t* kbase = kc + (size_t)g * kTile;
   const uint8_t* vbase = vc + (size_t)g * kTile;
+
+  // Fused append (decode step): the new token is position L-1, row L-1 mod 16
+  // of logical block (L-1)/16.  The wavefront whose partition holds that
+  // block writes the token's K/V row for its KV head into the pool and puts
+  // it into the staged tile, so it attends over the new token without a
+  // separate cache-write launch; no other wavefront reads that block.
+  constexpr int kRowChunks = D * 2 / 16;   // 16-byte chunks of one bf16 row
+  int new_b = -1, new_r = 0;
+  u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
+  if constexpr (KV == KV_BF16) {
+    if (kn != nullptr && (L - 1) / kBlock >= b0 && (L - 1) / kBlock < b1) {
+      new_b = (L - 1) / kBlock;
+      new_r = (L - 1) % kBlock;
+      if (lane < kRowChunks) {
+        const size_t src = ((size_t)s * hkv + g) * (D * 2) + lane * 16;
+        knew = *reinterpret_cast<const u32x4*>(kn + src);
+        vnew = *reinterpret_cast<const u32x4*>(vn + src);
+        const int ph = trow[new_b];
+        if (ph >= 0 && ph < num_blocks) {
+          const size_t dst = (size_t)ph * blk_stride + (size_t)g * kTile + new_r * (D * 2) +
+                             lane * 16;
+          *reinterpret_cast<u32x4*>(kc_w + dst) = knew;
+          *reinterpret_cast<u32x4*>(vc_w + dst) = vnew;
+        }
+      }
+    }
+  }
 
   float m = kNoMax;   // running reference maximum (log2 units)
   float lsum = 0.f;   // this lane's share of the softmax denominator
@@ -255,6 +283,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
+        }
+      }
+      if constexpr (KV == KV_BF16) {
+        if (b == new_b && lane < kRowChunks) {   // the appended token's row
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(new_r, lane)) = knew;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(new_r, lane)) = vnew;
         }
       }
       float kscale = 1.f, vscale = 1.f;
@@ -360,7 +394,8 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens, int hq,
     int hkv, int G, int num_blocks, float scale_log2, int part_blocks, int n_parts,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-    void* __restrict__ out) {
+    void* __restrict__ out, const float* __restrict__ kn, const float* __restrict__ vn,
+    float* __restrict__ kc_w, float* __restrict__ vc_w) {
   constexpr int kPer = D / kWave;
   const int lane = threadIdx.x;
   const int g = blockIdx.x % hkv;
@@ -401,17 +436,41 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
     return;
   }
   const int32_t* trow = tables + (size_t)s * max_blocks;
+  // fused append: the partition holding position L-1 writes the new token
+  // into the pool and uses it for that position
+  const bool app = kn != nullptr && (L - 1) / kBlock >= b0 && (L - 1) / kBlock < b1;
+  float kx[kPer], vx[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) kx[e] = vx[e] = 0.f;
+  if (app) {
+    const size_t src = ((size_t)s * hkv + g) * D + lane * kPer;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      kx[e] = kn[src + e];
+      vx[e] = vn[src + e];
+    }
+    const int ph = trow[(L - 1) / kBlock];
+    if (ph >= 0 && ph < num_blocks) {
+      const size_t dst = (((size_t)ph * hkv + g) * kBlock + (L - 1) % kBlock) * D + lane * kPer;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        kc_w[dst + e] = kx[e];
+        vc_w[dst + e] = vx[e];
+      }
+    }
+  }
   for (int b = b0; b < b1; ++b) {
     const int phys = trow[b];
     if (phys < 0 || phys >= num_blocks) continue;
     const int valid = min(kBlock, L - b * kBlock);
     for (int o = 0; o < valid; ++o) {
       const size_t base = (((size_t)phys * hkv + g) * kBlock + o) * D + lane * kPer;
+      const bool is_new = app && b * kBlock + o == L - 1;
       float kv[kPer], vv[kPer];
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
-        kv[e] = kc[base + e];
-        vv[e] = vc[base + e];
+        kv[e] = is_new ? kx[e] : kc[base + e];
+        vv[e] = is_new ? vx[e] : vc[base + e];
       }
 #pragma unroll
       for (int hh = 0; hh < MAXG; ++hh) {
@@ -457,7 +516,10 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 // ---------------------------------------------------------------------------
 // Cross-partition combine: one wavefront per (sequence, query head) row with
 // more than one partition; M = max_p m_p, w_p = 2^(m_p - M) l_p,
-// out = sum_p w_p o_p / sum_p w_p.
+// out = sum_p w_p o_p / sum_p w_p.  Lane p holds partition p's weight (64
+// partitions at a time); the partial rows are read D/4 lanes per row, several
+// rows per load instruction, through a descriptor bounded to this row's
+// partitions so that every load is issued unconditionally.
 template <int D, int OUT>
 __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws_m,
                                                     const float* __restrict__ ws_l,
@@ -465,7 +527,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
                                                     const int32_t* __restrict__ lens,
                                                     int max_blocks, int hq, int part_blocks,
                                                     int n_parts, void* __restrict__ out) {
-  constexpr int kPer = D / kWave;
+  constexpr int kCols = D / 4;             // lanes per partial row (16-byte pieces)
+  constexpr int kRowsPerLoad = kWave / kCols;
   const int row = blockIdx.x;
   const int s = row / hq;
   const int lane = threadIdx.x;
@@ -477,22 +540,31 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   const float* mrow = ws_m + (size_t)row * n_parts;
   const float* lrow = ws_l + (size_t)row * n_parts;
   float M = -INFINITY;
-  for (int pp = 0; pp < parts; ++pp) M = fmaxf(M, mrow[pp]);
-  float a[kPer] = {}, den = 0.f;
-  for (int pp = 0; pp < parts; ++pp) {
-    const float w = exp2f(mrow[pp] - M) * lrow[pp];
-    den += w;
-    const float* o = ws_o + ((size_t)row * n_parts + pp) * D + lane * kPer;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) a[e] += w * o[e];
+  for (int c = 0; c < parts; c += kWave)
+    if (c + lane < parts) M = fmaxf(M, mrow[c + lane]);
+  M = wave_max(M);
+  const int sub = lane / kCols, col = lane % kCols;
+  const rsrc_t ro = make_rsrc(ws_o + (size_t)row * n_parts * D, parts * D * 4);
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int c = 0; c < parts; c += kWave) {
+    const float wp = (c + lane < parts) ? exp2f(mrow[c + lane] - M) * lrow[c + lane] : 0.f;
+    den += wp;
+    const int cnt = min(kWave, parts - c);
+#pragma unroll 4
+    for (int q = 0; q < cnt; q += kRowsPerLoad) {
+      const int pp = q + sub;              // partition within this group of 64
+      const float w = __shfl(wp, pp & (kWave - 1), kWave);
+      const u32x4 v = buffer_load16(ro, ((c + pp) * D + col * 4) * 4);
+      a += w * __builtin_bit_cast(f32x4, v);
+    }
   }
-  const float inv = 1.0f / den;
+  den = wave_sum(den);
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const size_t o = (size_t)row * D + lane * kPer + e;
-    if constexpr (OUT == OUT_F32) static_cast<float*>(out)[o] = a[e] * inv;
-    else static_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(a[e] * inv);
-  }
+  for (int o = kCols; o < kWave; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], o, kWave);
+  if (sub == 0) store_out4<D, OUT>(out, (size_t)row * D + col * 4, a * (1.0f / den));
 }
 
 struct Plan {
@@ -512,28 +584,32 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
       rc = launch(decode_f32_kernel<D, OUT, 16>, grid, block, st, (const float*)a.q,
                   (const float*)c.k_cache, (const float*)c.v_cache, a.tables, a.max_blocks,
                   a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
-                  pl.ws_l, pl.ws_o, a.out);
+                  pl.ws_l, pl.ws_o, a.out, (const float*)a.k_new, (const float*)a.v_new,
+                  (float*)c.k_cache, (float*)c.v_cache);
       break;
     case PKV_BF16:
       rc = launch(decode_mfma_kernel<D, KV_BF16, OUT>, grid, block, st, (const uint16_t*)a.q,
                   (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache, (const float*)nullptr,
                   (const float*)nullptr, a.tables, a.max_blocks, a.lens, hq, hkv, G,
                   c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m, pl.ws_l, pl.ws_o,
-                  a.out);
+                  a.out, (const uint8_t*)a.k_new, (const uint8_t*)a.v_new, (uint8_t*)c.k_cache,
+                  (uint8_t*)c.v_cache);
       break;
     case PKV_I8:
       rc = launch(decode_mfma_kernel<D, KV_I8, OUT>, grid, block, st, (const uint16_t*)a.q,
                   (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache,
                   (const float*)c.k_scale, (const float*)c.v_scale, a.tables, a.max_blocks,
                   a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
-                  pl.ws_l, pl.ws_o, a.out);
+                  pl.ws_l, pl.ws_o, a.out, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
+                  (uint8_t*)nullptr, (uint8_t*)nullptr);
       break;
     default:
       rc = launch(decode_mfma_kernel<D, KV_FP8, OUT>, grid, block, st, (const uint16_t*)a.q,
                   (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache,
                   (const float*)c.k_scale, (const float*)c.v_scale, a.tables, a.max_blocks,
                   a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
-                  pl.ws_l, pl.ws_o, a.out);
+                  pl.ws_l, pl.ws_o, a.out, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
+                  (uint8_t*)nullptr, (uint8_t*)nullptr);
       break;
   }
   if (rc != PKV_OK || pl.n_parts <= 1) return rc;

@@ -357,3 +357,54 @@ def test_validate_tables_reports_bad_entries():
     t[2, 1] = wl.num_blocks      # used entry of sequence 2 (L = 64) out of range
     rc, bad = pkv.validate_tables(torch.from_numpy(t).cuda(), d["lens"], wl.num_blocks)
     assert rc == 4 and bad == 2
+
+
+# ------------------------------------------------------------- fused decode step
+
+STEP_CASES = [
+    (1, {}, 0),
+    (1, {}, 32),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 0),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 64),
+    (3, dict(B=20, median=300, lo=1, hi=1200), 256),
+    (2, dict(B=4, lo=1, hi=400, pool=200, D=64), 128),
+]
+
+
+@pytest.mark.parametrize("cfg,over,part", STEP_CASES)
+def test_decode_step_matches_write_then_attention(cfg, over, part):
+    wl = W.make(cfg, **over)
+    _say(f"decode step: {wl.name} {over} part={part}")
+    od = torch.float32
+    # separate launches
+    d1 = W.to_device(wl)
+    out1, _ = _step(wl, d1, part, od)
+    # fused
+    d2 = W.to_device(wl)
+    cache = _dev_cache(d2, wl)
+    out2 = pkv.decode_step(cache, d2["q"], d2["k_new"], d2["v_new"], d2["tables"], d2["lens"],
+                           float(wl.scale), partition_tokens=part, out_dtype=od)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    # the pool afterwards equals the oracle's cache write, byte for byte
+    k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    oracle.cache_write(k, v, wl.kv_dtype, wl.k_new, wl.v_new,
+                       oracle.slot_mapping(wl.tables, wl.lens))
+    assert np.array_equal(W.from_device(d2["k_pool"]), k)
+    assert np.array_equal(W.from_device(d2["v_pool"]), v)
+    ref, _ = _oracle_step(wl)
+    _cmp(_out_np(out2), ref, TOL[wl.kv_dtype], "f32", f"step {wl.name}")
+
+
+@pytest.mark.parametrize("cfg,part", [(2, 256), (3, 1024), (4, 512)])
+def test_decode_step_full_size(cfg, part):
+    wl = _full_workload(cfg)
+    _say(f"decode step full: {wl.name} part={part}")
+    d = W.to_device(wl)
+    cache = _dev_cache(d, wl)
+    out = pkv.decode_step(cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"],
+                          float(wl.scale), partition_tokens=part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _ = _oracle_step(wl)
+    err = _cmp(_out_np(out), ref, TOL[wl.kv_dtype], "bf16", wl.name)
+    _say(f"  max abs err {err:.3e}")
