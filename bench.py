@@ -56,12 +56,12 @@ def algorithmic_bytes(wl, part_blocks_unused=None):
 
 
 class Replica:
-    def __init__(self, wl, part):
+    def __init__(self, wl, part, layout):
         import torch
         import paged_kv_cache_434_amd as pkv
         from paged_kv_cache_434_amd import workloads as W
 
-        d = W.to_device(wl)
+        d = W.to_device(wl, layout=layout)
         self.d = d
         self.cache = pkv.PagedCache(d["k_pool"], d["v_pool"], wl.kv_dtype)
         self.slots = torch.empty(wl.B, dtype=torch.int32, device="cuda")
@@ -110,8 +110,12 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--partition", type=int, default=-1,
-                    help="split size in tokens (-1: the library's default, 0: no split)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split: tokens per partition, 0 for none, -1 for the balanced split "
+                         "(default: the library's recommendation)")
+    ap.add_argument("--layout", choices=("blocks", "split"), default="blocks",
+                    help="pool layout: one [NB][2][Hkv][16][D] tensor (blocks) or two dense "
+                         "[NB][Hkv][16][D] pools (split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -126,9 +130,9 @@ def main():
 
     torch.cuda.set_device(0)
     wl = W.make(2)
-    part = args.partition if args.partition >= 0 else pkv.default_partition(
+    part = args.partition if args.partition is not None else pkv.default_partition(
         wl.B, wl.Hkv, wl.max_blocks)
-    reps = [Replica(wl, part) for _ in range(max(1, args.replicas))]
+    reps = [Replica(wl, part, args.layout) for _ in range(max(1, args.replicas))]
     print(f"# workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
           f"sum(L)={int(wl.lens.sum())} pool={wl.num_blocks} partition={part} "
           f"replicas={len(reps)}", file=sys.stderr, flush=True)
@@ -170,6 +174,8 @@ def main():
                    "num_kv_heads": wl.Hkv, "head_dim": wl.D, "block_size": 16,
                    "context_lens": "uniform[512,4096]", "sum_context": int(wl.lens.sum()),
                    "pool_blocks": wl.num_blocks, "partition_tokens": part,
+                   "split": "balanced" if part == pkv.SPLIT_BALANCED else "fixed",
+                   "layout": args.layout,
                    "step": "decode step: slot of position L-1 + cache write + paged "
                            "attention (one launch) + partition combine",
                    "replicas": len(reps)},

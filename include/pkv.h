@@ -64,11 +64,28 @@ enum {
 
 #define PKV_BLOCK_SIZE 16
 
+/* partition_tokens value selecting the balanced split (see
+ * pkv_attention_decode). */
+#define PKV_SPLIT_BALANCED (-1)
+
 /* A paged KV pool for one layer.
- *   k_cache, v_cache: [num_blocks][num_kv_heads][block_size][head_dim] of
- *     kv_dtype -- one block holds every KV head's [block_size][head_dim] tile,
- *     the per-block layout of [MGMT] section 二; each (block, head) tile is
- *     contiguous (4 KiB for bf16 x 16 x 128).
+ *   K of block b, KV head g, row t, element d is
+ *     k_cache[b * block_stride + (g * block_size + t) * head_dim + d]
+ *   and V the same from v_cache: within a block, one KV head's
+ *   [block_size][head_dim] tile is contiguous (4 KiB for bf16 x 16 x 128) and the
+ *   heads follow one another, the per-block layout of [MGMT] section 二
+ *   (KVCacheBlock: [heads][block_size][head_dim]).
+ *   block_stride: elements from one block to the next; 0 means
+ *     num_kv_heads * block_size * head_dim, i.e. K and V in two separate
+ *     dense pools [num_blocks][num_kv_heads][block_size][head_dim].  With one
+ *     allocation [num_blocks][2][num_kv_heads][block_size][head_dim] (a block
+ *     holds every head's K, then every head's V, as KVCacheBlock does), pass
+ *     k_cache = base, v_cache = base + num_kv_heads * block_size * head_dim
+ *     and block_stride = 2 * num_kv_heads * block_size * head_dim; that
+ *     layout reads fastest on MI355X (the eight heads' K and V of one block
+ *     are one contiguous run).  Must be 0 or at least num_kv_heads *
+ *     block_size * head_dim, with block_stride * element size a multiple of
+ *     16 bytes; the K and V regions of all blocks must not overlap.
  *   k_scale, v_scale: [num_blocks][num_kv_heads] binary32 scales, required for
  *     PKV_I8 / PKV_FP8_E4M3 and ignored otherwise.
  * block_size must be 16 ([KVC] "PagedAttention"); head_dim must be 64 or 128. */
@@ -82,6 +99,7 @@ typedef struct pkv_cache_t {
   void* v_cache;
   float* k_scale;
   float* v_scale;
+  int64_t block_stride;
 } pkv_cache_t;
 
 /* Human-readable text for a status code (static storage). */
@@ -118,16 +136,20 @@ int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
 int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
                     const int32_t* slot_mapping, int32_t n, void* stream);
 
-/* Workspace bytes pkv_attention_decode / pkv_decode_step need for a
- * split-context launch: per (sequence, query head, partition) a running
- * maximum, a sum and a head_dim output row, all binary32, plus alignment.
- * Returns 0 when no split happens (partition_tokens == 0, or one partition
- * covers max_blocks_per_seq * 16 tokens): no workspace needed then. */
+/* Workspace bytes pkv_attention_decode / pkv_decode_step need for the given
+ * split: per (sequence, query head) and partial slot a running maximum, a sum
+ * and a head_dim output row, all binary32, plus one int32 per sequence, each
+ * part 256-byte aligned.  Fixed split (partition_tokens > 0, a multiple of
+ * 16): one slot per partition; returns 0 when one partition covers
+ * max_blocks_per_seq * 16 tokens or partition_tokens == 0 (no workspace
+ * needed).  Balanced split (PKV_SPLIT_BALANCED): ceil(max_blocks_per_seq / 8)
+ * + 1 slots.  Returns 0 for invalid sizes. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_tokens);
 
-/* A split size for the given geometry: a multiple of 16 (or 0 for no split)
- * that gives enough independent work units to fill the GPU. */
+/* The split this library recommends for the given geometry: always
+ * PKV_SPLIT_BALANCED (one generation of wavefronts with equal shares of the
+ * blocks), or 0 for invalid sizes. */
 int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
                                      int32_t max_blocks_per_seq);
 
@@ -139,12 +161,20 @@ int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
  *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; entries past
  *     ceil(L / 16) are never read
  *   context_lens: device int32 [num_seqs], 0 <= L <= max_blocks_per_seq * 16
- *   partition_tokens: 0 = one pass per (sequence, KV head); otherwise a
- *     positive multiple of 16: the context is cut into partitions of that many
- *     tokens, each gives a partial (max, sum, output) and a second kernel
- *     combines them with the log-sum-exp rule
+ *   partition_tokens: how the context is split over wavefronts.
+ *     0: one pass per (sequence, KV head), no split.
+ *     a positive multiple of 16 (fixed split): the context is cut into
+ *       partitions of that many tokens, each gives a partial (max, sum,
+ *       output) and a second kernel combines them with the log-sum-exp rule.
+ *     PKV_SPLIT_BALANCED: for each KV head the blocks of all sequences, laid
+ *       end to end, are cut into equal ranges, one per wavefront of a grid
+ *       that fills the GPU once (at least 8 blocks per range); pieces of a
+ *       sequence are combined as above.  With the fixed split, results are
+ *       reproducible for given inputs; with the balanced split they are
+ *       reproducible for given inputs and GPU model (the ranges depend on the
+ *       compute-unit count).
  *   workspace: device memory of at least pkv_decode_workspace_bytes(...) when
- *     partition_tokens > 0 (contents need not be initialised), else may be NULL
+ *     that is nonzero (contents need not be initialised), else may be NULL
  *   out: device [num_seqs][num_q_heads][head_dim] of out_dtype.
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8),
  * (BF16, FP8_E4M3); out_dtype F32 or BF16 (bf16 rounded to nearest even). */

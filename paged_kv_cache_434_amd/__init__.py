@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
+SPLIT_BALANCED = -1     # partition_tokens value: balanced split (PKV_SPLIT_BALANCED)
 DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3}
 BLOCK_SIZE = 16
 
@@ -41,6 +42,7 @@ class CacheDesc(ctypes.Structure):
         ("v_cache", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("block_stride", ctypes.c_int64),
     ]
 
 
@@ -129,28 +131,53 @@ def _need(t, name, dtype=None, ndim=None):
 
 
 class PagedCache:
-    """One layer's K and V pools ([num_blocks][Hkv][16][D]) and, for 8-bit
-    pools, their [num_blocks][Hkv] binary32 scales.  Holds references so the
-    tensors outlive the descriptor."""
+    """One layer's K and V pools and, for 8-bit pools, their [num_blocks][Hkv]
+    binary32 scales.  ``k_cache`` / ``v_cache`` are [num_blocks][Hkv][16][D]
+    tensors whose last three dimensions are dense; the block dimension may be
+    strided, so both separate dense pools and the two halves of one
+    [num_blocks][2][Hkv][16][D] allocation (see ``from_blocks``) are accepted.
+    Holds references so the tensors outlive the descriptor."""
 
     def __init__(self, k_cache, v_cache, kv_dtype: str, k_scale=None, v_scale=None):
         torch = _torch()
         sd = _storage_dtype(kv_dtype)
         if kv_dtype == "fp8" and k_cache.dtype == torch.float8_e4m3fn:
             k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
-        _need(k_cache, "k_cache", sd, 4)
-        _need(v_cache, "v_cache", sd, 4)
-        if k_cache.shape != v_cache.shape:
-            raise ValueError("k_cache and v_cache shapes differ")
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+            if t.dtype != sd:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected {sd}")
+            if t.dim() != 4:
+                raise ValueError(f"{name} must have 4 dims")
+            _, H, bs, D = t.shape
+            if tuple(t.stride()[1:]) != (bs * D, D, 1):
+                raise ValueError(f"{name}: the last three dimensions must be dense")
+        if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+            raise ValueError("k_cache and v_cache shapes or strides differ")
         if kv_dtype in ("i8", "fp8"):
             _need(k_scale, "k_scale", torch.float32, 2)
             _need(v_scale, "v_scale", torch.float32, 2)
         NB, Hkv, bs, D = k_cache.shape
+        stride = int(k_cache.stride(0))
+        self.block_stride = 0 if stride == Hkv * bs * D else stride
         self.k_cache, self.v_cache, self.k_scale, self.v_scale = k_cache, v_cache, k_scale, v_scale
         self.kv_dtype = kv_dtype
         self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = NB, Hkv, bs, D
         self.desc = CacheDesc(NB, Hkv, bs, D, DTYPE_CODES[kv_dtype], k_cache.data_ptr(),
-                              v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale))
+                              v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), self.block_stride)
+
+    @classmethod
+    def from_blocks(cls, kv, kv_dtype: str, k_scale=None, v_scale=None):
+        """A pool held as one [num_blocks][2][Hkv][16][D] tensor: each block
+        holds every head's K, then every head's V."""
+        torch = _torch()
+        if kv_dtype == "fp8" and kv.dtype == torch.float8_e4m3fn:
+            kv = kv.view(torch.uint8)
+        _need(kv, "kv", _storage_dtype(kv_dtype), 5)
+        if kv.shape[1] != 2:
+            raise ValueError("kv must be [num_blocks][2][num_kv_heads][block_size][head_dim]")
+        return cls(kv[:, 0], kv[:, 1], kv_dtype, k_scale, v_scale)
 
 
 def pool_bytes(num_blocks, num_kv_heads, head_dim, dtype, block_size=BLOCK_SIZE) -> int:

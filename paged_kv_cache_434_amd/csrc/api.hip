@@ -23,12 +23,16 @@ int check_cache(const pkv_cache_t* c) {
   if ((c->kv_dtype == PKV_I8 || c->kv_dtype == PKV_FP8_E4M3) && (!c->k_scale || !c->v_scale))
     return PKV_ERR_NULL;
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_UNSUPPORTED;
+  if (c->block_stride != 0) {
+    if (c->block_stride < block_elems(*c)) return PKV_ERR_SHAPE;
+    if ((c->block_stride * (int64_t)elem_bytes(c->kv_dtype)) % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  }
   return PKV_OK;
 }
 
-int n_parts_of(int max_blocks, int partition_tokens) {
-  int part_blocks = partition_tokens > 0 ? partition_tokens / PKV_BLOCK_SIZE : max_blocks;
-  return (max_blocks + part_blocks - 1) / part_blocks;
+bool split_ok(int32_t partition_tokens) {
+  return partition_tokens == PKV_SPLIT_BALANCED ||
+         (partition_tokens >= 0 && partition_tokens % PKV_BLOCK_SIZE == 0);
 }
 
 }  // namespace
@@ -85,23 +89,18 @@ int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_tokens) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      partition_tokens <= 0 || partition_tokens % PKV_BLOCK_SIZE != 0)
+      max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE || !split_ok(partition_tokens))
     return 0;
-  int np = n_parts_of(max_blocks_per_seq, partition_tokens);
-  if (np <= 1) return 0;
-  return decode_workspace_layout((int64_t)num_seqs * num_q_heads, np, head_dim, nullptr, nullptr);
+  const int k = decode_slots(max_blocks_per_seq, partition_tokens);
+  if (k <= 1) return 0;
+  return decode_workspace_layout((int64_t)num_seqs * num_q_heads, k, head_dim, num_seqs, nullptr,
+                                 nullptr, nullptr);
 }
 
 int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
                                      int32_t max_blocks_per_seq) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
-  const int64_t max_ctx = (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE;
-  const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  // smallest power-of-two split >= 256 tokens that keeps the launch within
-  // 16384 wavefronts (64 per CU); no split when one partition covers the context
-  int64_t part = 256;
-  while (part < max_ctx && units * ((max_ctx + part - 1) / part) > 16384) part *= 2;
-  return part >= max_ctx ? 0 : (int32_t)part;
+  return PKV_SPLIT_BALANCED;
 }
 
 static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
@@ -119,8 +118,8 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                        (q_dtype == PKV_BF16 &&
                         (kv == PKV_BF16 || kv == PKV_I8 || kv == PKV_FP8_E4M3));
   if (!pair_ok) return PKV_ERR_DTYPE;
-  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_tokens < 0 ||
-      partition_tokens % PKV_BLOCK_SIZE != 0 || max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || !split_ok(partition_tokens) ||
+      max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
     return PKV_ERR_SHAPE;
   if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
@@ -132,11 +131,13 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   }
   if (!q || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(out)) return PKV_ERR_UNSUPPORTED;
-  const int np = n_parts_of(max_blocks_per_seq, partition_tokens);
+  const int np = decode_slots(max_blocks_per_seq, partition_tokens);
   if ((int64_t)num_seqs * cache->num_kv_heads * np > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
+  // balanced split: flat block positions (and a range past the last) fit in int
+  if ((int64_t)num_seqs * max_blocks_per_seq > (int64_t)(INT_MAX / 2)) return PKV_ERR_SHAPE;
   if (np > 1) {
     size_t need = decode_workspace_layout((int64_t)num_seqs * num_q_heads, np, cache->head_dim,
-                                          nullptr, nullptr);
+                                          num_seqs, nullptr, nullptr, nullptr);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
   }

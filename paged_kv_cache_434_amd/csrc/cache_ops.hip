@@ -30,7 +30,7 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int max_
 __global__ void cache_write_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                    const uint8_t* __restrict__ kn, const uint8_t* __restrict__ vn,
                                    const int32_t* __restrict__ slots, int n, int hkv,
-                                   int row_chunks, int64_t num_slots) {
+                                   int row_chunks, int64_t num_slots, size_t blk_bytes) {
   int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t per_tok = (int64_t)hkv * row_chunks;
   if (tid >= (int64_t)n * per_tok) return;
@@ -42,7 +42,7 @@ __global__ void cache_write_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict
   if (slot < 0 || slot >= num_slots) return;
   int64_t blk = slot / kBlock, off = slot % kBlock;
   size_t row_bytes = (size_t)row_chunks * 16;
-  size_t dst = (((size_t)blk * hkv + g) * kBlock + off) * row_bytes + (size_t)c * 16;
+  size_t dst = (size_t)blk * blk_bytes + ((size_t)g * kBlock + off) * row_bytes + (size_t)c * 16;
   size_t src = ((size_t)i * hkv + g) * row_bytes + (size_t)c * 16;
   *reinterpret_cast<uint4*>(kc + dst) = *reinterpret_cast<const uint4*>(kn + src);
   *reinterpret_cast<uint4*>(vc + dst) = *reinterpret_cast<const uint4*>(vn + src);
@@ -53,8 +53,8 @@ __global__ void cache_write_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict
 __global__ void gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                               const int32_t* __restrict__ tables, int max_blocks,
                               const int32_t* __restrict__ lens, const int32_t* __restrict__ cu,
-                              int hkv, int row_chunks, int num_blocks, uint8_t* __restrict__ ko,
-                              uint8_t* __restrict__ vo) {
+                              int hkv, int row_chunks, int num_blocks, size_t blk_bytes,
+                              uint8_t* __restrict__ ko, uint8_t* __restrict__ vo) {
   const int b = blockIdx.x % max_blocks, s = blockIdx.x / max_blocks;
   int L = lens[s];
   if (L < 0 || L > max_blocks * kBlock) return;
@@ -71,7 +71,7 @@ __global__ void gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __r
     int o = x / per_tok;
     int rem = x % per_tok;
     int g = rem / row_chunks, c = rem % row_chunks;
-    size_t src = (((size_t)phys * hkv + g) * kBlock + o) * row_bytes + (size_t)c * 16;
+    size_t src = (size_t)phys * blk_bytes + ((size_t)g * kBlock + o) * row_bytes + (size_t)c * 16;
     size_t dst = ((out0 + o) * hkv + g) * row_bytes + (size_t)c * 16;
     *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(kc + src);
     *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(vc + src);
@@ -93,7 +93,7 @@ int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const
   dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   return launch(cache_write_kernel, grid, block, st, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache,
                 (const uint8_t*)k, (const uint8_t*)v, slots, n, c.num_kv_heads, row_chunks,
-                (int64_t)c.num_blocks * kBlock);
+                (int64_t)c.num_blocks * kBlock, block_stride_bytes(c));
 }
 
 int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
@@ -103,7 +103,7 @@ int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
   dim3 grid((unsigned)((int64_t)max_blocks * num_seqs)), block(256);
   return launch(gather_kernel, grid, block, st, (const uint8_t*)c.k_cache,
                 (const uint8_t*)c.v_cache, tables, max_blocks, lens, cu, c.num_kv_heads,
-                row_chunks, c.num_blocks, (uint8_t*)ko, (uint8_t*)vo);
+                row_chunks, c.num_blocks, block_stride_bytes(c), (uint8_t*)ko, (uint8_t*)vo);
 }
 
 }  // namespace pkv

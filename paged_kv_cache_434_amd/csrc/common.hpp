@@ -24,6 +24,17 @@ inline size_t elem_bytes(int dtype) {
   }
 }
 
+// Elements of one block of one pool (every KV head's tile).
+inline int64_t block_elems(const pkv_cache_t& c) {
+  return (int64_t)c.num_kv_heads * c.block_size * c.head_dim;
+}
+
+// Bytes from one block to the next in k_cache / v_cache.
+inline size_t block_stride_bytes(const pkv_cache_t& c) {
+  const int64_t e = c.block_stride != 0 ? c.block_stride : block_elems(c);
+  return (size_t)e * elem_bytes(c.kv_dtype);
+}
+
 // Launch through hipLaunchKernel so the launch status comes back directly
 // instead of through the thread's sticky last-error slot.
 template <typename... KArgs, typename... Args>
@@ -95,7 +106,18 @@ struct DecodeArgs {
 };
 int launch_decode(const DecodeArgs& a, hipStream_t st);
 
-// Bytes of the split-context workspace and the offsets of its m and l parts.
-size_t decode_workspace_layout(int64_t rows, int n_parts, int D, size_t* off_m, size_t* off_l);
+// Balanced split: fewest blocks one wavefront takes.
+constexpr int kBalancedMinBlocks = 8;
+
+// Partial slots per (sequence, query head) row for a split setting.
+int decode_slots(int max_blocks, int partition_tokens);
+
+// Bytes of the split-context workspace and the offsets of its m, l and count
+// parts.
+size_t decode_workspace_layout(int64_t rows, int kslots, int D, int64_t num_seqs, size_t* off_m,
+                               size_t* off_l, size_t* off_count);
+
+// Compute units of the current device (cached per device), or -1.
+int device_cu_count();
 
 }  // namespace pkv

@@ -41,6 +41,10 @@
 // partition's (max, sum, normalised output) to the workspace and a second
 // kernel combines them with the log-sum-exp rule; a sequence that fits in one
 // partition is written directly.
+#include <atomic>
+#include <mutex>
+#include <unordered_map>
+
 #include "common.hpp"
 
 namespace pkv {
@@ -57,6 +61,7 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxDevices = 64;
 // initial running maximum: finite, so exp2(x - m) of a masked logit (-inf)
 // is 0 even before the first valid token
 constexpr float kNoMax = -3.0e38f;
@@ -128,38 +133,88 @@ __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel: q bf16; KV bf16, int8 or E4M3; D = 64 or 128; G <= 16.
-template <int D, int KV, int OUT>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
-    const uint8_t* __restrict__ vc, const float* __restrict__ ksc,
-    const float* __restrict__ vsc, const int32_t* __restrict__ tables, int max_blocks,
-    const int32_t* __restrict__ lens, int hq, int hkv, int G, int num_blocks, float scale_log2,
-    int part_blocks, int n_parts, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o, void* __restrict__ out, const uint8_t* __restrict__ kn,
-    const uint8_t* __restrict__ vn, uint8_t* __restrict__ kc_w, uint8_t* __restrict__ vc_w) {
+// MFMA path: q bf16; KV bf16, int8 or E4M3; D = 64 or 128; G <= 16.
+
+// Launch-wide arguments of the MFMA kernels.
+struct MfmaArgs {
+  const uint16_t* q;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const float* ksc;
+  const float* vsc;
+  const int32_t* tables;
+  const int32_t* lens;
+  int max_blocks;
+  int num_seqs;
+  int hq, hkv, G, num_blocks;
+  size_t blk_stride;  // bytes from one block to the next in each pool
+  float scale_log2;
+  float* ws_m;        // split partials: running maximum (log2 units)
+  float* ws_l;        //                 softmax denominator
+  float* ws_o;        //                 normalised output row
+  int32_t* ws_count;  // balanced split: segments of each sequence
+  int kstride;        // partial slots per (sequence, query head)
+  int part_blocks;    // fixed split: blocks per partition
+  int min_blocks;     // balanced split: fewest blocks one wavefront takes
+  void* out;
+  const uint8_t* kn;  // fused append (decode step): new K/V rows, or null
+  const uint8_t* vn;
+  uint8_t* kc_w;
+  uint8_t* vc_w;
+};
+
+__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+  return (L < 0 || L > max_blocks * kBlock) ? 0 : L;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the wavefront (lane order).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// Zero output rows of the query heads of KV head g for an empty sequence s.
+template <int D, int OUT>
+__device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g) {
+  const int lane = threadIdx.x;
+  const int j = lane >> 4, n = lane & 15;
+  if (n >= a.G) return;
+  const size_t row = (size_t)s * a.hq + g * a.G + n;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    store_out4<D, OUT>(a.out, row * D + 16 * t + 4 * j, f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
+// Attention of the G query heads of KV head g of sequence s (length L) over
+// its logical blocks [b0, b1).  `whole`: the range is the whole context, so the
+// normalised rows go to `out`; otherwise the partial (max, sum, output) goes
+// to partial slot `slot` of each row.
+template <int D, int KV, int OUT, int NST>
+__device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, int L, int b0,
+                                             int b1, int slot, bool whole, uint8_t* lds_k,
+                                             uint8_t* lds_v) {
   constexpr int kEsz = (KV == KV_BF16) ? 2 : 1;
   constexpr int kTile = kBlock * D * kEsz;  // bytes of one (block, head) tile in HBM
   constexpr int kLoads = kTile / 1024;      // 16-byte loads per lane per tile
-  constexpr int kRowB = D * 2;              // bytes of one bf16 row in LDS
   constexpr int kNKK = D / 32;              // QK^T instructions per block
   constexpr int kNT = D / 16;               // PV instructions per block
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * kRowB];
-
   const int lane = threadIdx.x;
   const int j = lane >> 4;   // token quad (rows 4j..4j+3 of S) / k-slice
   const int n = lane & 15;   // head column
-  const int g = blockIdx.x % hkv;
-  const int r = blockIdx.x / hkv;
-  const int p = r % n_parts;
-  const int s = r / n_parts;
-  int L = lens[s];
-  if (L < 0 || L > max_blocks * kBlock) L = 0;
-  const int nblk = (L + kBlock - 1) / kBlock;
-  const int parts_s = (nblk + part_blocks - 1) / part_blocks;
-  const int b0 = p * part_blocks;
-  const int b1 = min(b0 + part_blocks, nblk);
+  const int G = a.G, hq = a.hq, hkv = a.hkv, num_blocks = a.num_blocks;
   const int h = g * G + n;
   const bool has_head = n < G;
 
@@ -167,20 +222,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < kNT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (b0 >= b1) {
-    if (p == 0 && has_head) {  // empty sequence: zero row
-#pragma unroll
-      for (int t = 0; t < kNT; ++t)
-        store_out4<D, OUT>(out, ((size_t)s * hq + h) * D + 16 * t + 4 * j, acc[t]);
-    }
-    return;
-  }
-
   // queries of this group as the B operand of S = K q^T: lane (j, n) holds
   // q[h][32 kk + 8 j .. + 8] for each kk
   bf16x8 qop[kNKK];
   {
-    const uint16_t* qrow = q + ((size_t)s * hq + (has_head ? h : g * G)) * D;
+    const uint16_t* qrow = a.q + ((size_t)s * hq + (has_head ? h : g * G)) * D;
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * j);
@@ -188,33 +234,33 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     }
   }
 
-  const int32_t* trow = tables + (size_t)s * max_blocks;
-  const size_t blk_stride = (size_t)hkv * kTile;
-  const uint8_t* kbase = kc + (size_t)g * kTile;
-  const uint8_t* vbase = vc + (size_t)g * kTile;
+  const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
+  const size_t blk_stride = a.blk_stride;
+  const uint8_t* kbase = a.kc + (size_t)g * kTile;
+  const uint8_t* vbase = a.vc + (size_t)g * kTile;
 
   // Fused append (decode step): the new token is position L-1, row L-1 mod 16
-  // of logical block (L-1)/16.  The wavefront whose partition holds that
-  // block writes the token's K/V row for its KV head into the pool and puts
-  // it into the staged tile, so it attends over the new token without a
-  // separate cache-write launch; no other wavefront reads that block.
+  // of logical block (L-1)/16.  The wavefront whose range holds that block
+  // writes the token's K/V row for its KV head into the pool and puts it into
+  // the staged tile, so it attends over the new token without a separate
+  // cache-write launch; no other wavefront reads that block.
   constexpr int kRowChunks = D * 2 / 16;   // 16-byte chunks of one bf16 row
   int new_b = -1, new_r = 0;
   u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
   if constexpr (KV == KV_BF16) {
-    if (kn != nullptr && (L - 1) / kBlock >= b0 && (L - 1) / kBlock < b1) {
+    if (a.kn != nullptr && (L - 1) / kBlock >= b0 && (L - 1) / kBlock < b1) {
       new_b = (L - 1) / kBlock;
       new_r = (L - 1) % kBlock;
       if (lane < kRowChunks) {
         const size_t src = ((size_t)s * hkv + g) * (D * 2) + lane * 16;
-        knew = *reinterpret_cast<const u32x4*>(kn + src);
-        vnew = *reinterpret_cast<const u32x4*>(vn + src);
+        knew = *reinterpret_cast<const u32x4*>(a.kn + src);
+        vnew = *reinterpret_cast<const u32x4*>(a.vn + src);
         const int ph = trow[new_b];
         if (ph >= 0 && ph < num_blocks) {
           const size_t dst = (size_t)ph * blk_stride + (size_t)g * kTile + new_r * (D * 2) +
                              lane * 16;
-          *reinterpret_cast<u32x4*>(kc_w + dst) = knew;
-          *reinterpret_cast<u32x4*>(vc_w + dst) = vnew;
+          *reinterpret_cast<u32x4*>(a.kc_w + dst) = knew;
+          *reinterpret_cast<u32x4*>(a.vc_w + dst) = vnew;
         }
       }
     }
@@ -223,7 +269,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   float m = kNoMax;   // running reference maximum (log2 units)
   float lsum = 0.f;   // this lane's share of the softmax denominator
 
-  // The partition is walked in chunks of up to 64 blocks.  Per chunk, lane i
+  // The range is walked in chunks of up to 64 blocks.  Per chunk, lane i
   // loads block-table entry i (and, for 8-bit KV, that block's two scales);
   // each block's id is then broadcast from its lane.  Tile loads go through
   // buffer descriptors built per block: a block past the chunk or with an
@@ -237,8 +283,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     float ks_l = 1.f, vs_l = 1.f;
     if constexpr (KV != KV_BF16) {
       if (tab >= 0 && tab < num_blocks) {
-        ks_l = ksc[(size_t)tab * hkv + g];
-        vs_l = vsc[(size_t)tab * hkv + g];
+        ks_l = a.ksc[(size_t)tab * hkv + g];
+        vs_l = a.vsc[(size_t)tab * hkv + g];
       }
     }
     auto phys_of = [&](int b) -> int {
@@ -299,8 +345,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         }
       }
 
-      // ---- refill this buffer with block b+2 (zero-length if absent)
-      ph = phys_of(b + 2);
+      // ---- refill this buffer with block b+NST (zero-length if absent)
+      ph = phys_of(b + NST);
       load_tile(kr, vr, ph);
 
       // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
@@ -312,7 +358,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       }
 
       // ---- online softmax (base 2)
-      const float cb = scale_log2 * kscale;
+      const float cb = a.scale_log2 * kscale;
       float x[4];
       float mx = -INFINITY;
 #pragma unroll
@@ -353,13 +399,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       }
     };
 
-    u32x4 kr0[kLoads], vr0[kLoads], kr1[kLoads], vr1[kLoads];
-    int ph0 = phys_of(c0), ph1 = phys_of(c0 + 1);
-    load_tile(kr0, vr0, ph0);
-    load_tile(kr1, vr1, ph1);
-    for (int b = c0; b < c1; b += 2) {
-      process(kr0, vr0, ph0, b);
-      process(kr1, vr1, ph1, b + 1);   // past c1: masked, no memory traffic
+    // NST register buffers in a ring: buffer i holds block b with b % NST == i
+    u32x4 kr[NST][kLoads], vr[NST][kLoads];
+    int ph[NST];
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      ph[i] = phys_of(c0 + i);
+      load_tile(kr[i], vr[i], ph[i]);
+    }
+    for (int b = c0; b < c1; b += NST) {
+#pragma unroll
+      for (int i = 0; i < NST; ++i)
+        process(kr[i], vr[i], ph[i], b + i);   // past c1: masked, no memory traffic
     }
   }
 
@@ -368,19 +419,138 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   lt += __shfl_xor(lt, 32, kWave);
   if (!has_head) return;
   const float inv = 1.0f / lt;
-  if (parts_s == 1) {
+  if (whole) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
-      store_out4<D, OUT>(out, ((size_t)s * hq + h) * D + 16 * t + 4 * j, acc[t] * inv);
+      store_out4<D, OUT>(a.out, ((size_t)s * hq + h) * D + 16 * t + 4 * j, acc[t] * inv);
   } else {
-    const size_t row = ((size_t)s * hq + h) * n_parts + p;
+    const size_t row = ((size_t)s * hq + h) * a.kstride + slot;
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
-      *reinterpret_cast<f32x4*>(ws_o + row * D + 16 * t + 4 * j) = acc[t] * inv;
+      *reinterpret_cast<f32x4*>(a.ws_o + row * D + 16 * t + 4 * j) = acc[t] * inv;
     if (j == 0) {
-      ws_m[row] = m;
-      ws_l[row] = lt;
+      a.ws_m[row] = m;
+      a.ws_l[row] = lt;
     }
+  }
+}
+
+// Fixed split: one wavefront per (sequence, KV head, partition of
+// part_blocks blocks); the launch index is decoded KV-head-fastest.
+template <int D, int KV, int OUT>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
+  const int g = blockIdx.x % a.hkv;
+  const int r = blockIdx.x / a.hkv;
+  const int p = r % n_parts;
+  const int s = r / n_parts;
+  const int L = clamp_len(a.lens[s], a.max_blocks);
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int parts_s = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const int b0 = p * a.part_blocks;
+  const int b1 = min(b0 + a.part_blocks, nblk);
+  if (b0 >= b1) {
+    if (p == 0) zero_rows<D, OUT>(a, s, g);   // empty sequence
+    return;
+  }
+  mfma_segment<D, KV, OUT, 2>(a, s, g, L, b0, b1, p, parts_s == 1, lds_k, lds_v);
+}
+
+// Balanced split: a persistent grid of V wavefronts per KV head, one
+// generation on the GPU.  For KV head g, the blocks of all sequences are laid
+// end to end (sequence 0's blocks, then sequence 1's, ...; T in all) and
+// wavefront v takes the range [v P, v P + P) with P = max(ceil(T / V),
+// min_blocks), so every wavefront moves the same number of bytes and all of
+// them finish together.  A range that covers a sequence's blocks only in part
+// yields a partial in slot v - floor(R0 / P) of that sequence (R0: the
+// sequence's first position in the flat order); the sequence has
+// floor((R1 - 1) / P) - floor(R0 / P) + 1 pieces, which the wavefront holding
+// its first block records for the combine kernel.  The eight wavefronts of one
+// v are consecutive launch indices, so they run side by side on different XCDs
+// and read the eight heads of the same blocks at the same time.
+#ifndef PKV_BAL_STAGES
+#define PKV_BAL_STAGES 2
+#define PKV_BAL_WAVES 2
+#endif
+template <int D, int KV, int OUT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_BAL_WAVES))) void
+decode_mfma_balanced_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % a.hkv;
+  const int v = blockIdx.x / a.hkv;
+  const int V = gridDim.x / a.hkv;
+  const int B = a.num_seqs;
+
+  // pass 1: total blocks per KV head; zero rows of empty sequences
+  int total = 0;
+  for (int base = 0; base < B; base += kWave) {
+    const int si = base + lane;
+    const int Ll = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+    total += wave_sum_i((Ll + kBlock - 1) / kBlock);
+    if (v == 0) {
+      uint64_t empty = __ballot(si < B && Ll == 0);
+      while (empty) {
+        const int e = __ffsll((unsigned long long)empty) - 1;
+        empty &= empty - 1;
+        zero_rows<D, OUT>(a, base + e, g);
+      }
+    }
+  }
+  const int per = max((total + V - 1) / V, a.min_blocks);
+  const int x0 = v * per;
+  if (x0 >= total) return;
+  const int x1 = min(x0 + per, total);
+
+  // pass 2: the sequence holding flat position x0; the lanes keep the lengths
+  // and inclusive prefix of a 64-sequence chunk for the walk below
+  int base = 0, carry = 0, s = -1, R0 = 0, Lreg = 0, incl = 0;
+  for (; base < B; base += kWave) {
+    const int si = base + lane;
+    Lreg = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+    const int nb = (Lreg + kBlock - 1) / kBlock;
+    incl = wave_incl_scan(nb) + carry;
+    const uint64_t hit = __ballot(nb > 0 && incl - nb <= x0 && x0 < incl);
+    if (hit) {
+      const int hl = __ffsll((unsigned long long)hit) - 1;
+      s = base + hl;
+      R0 = readlane_i(incl - nb, hl);
+      break;
+    }
+    carry = readlane_i(incl, kWave - 1);
+  }
+  if (s < 0) return;   // unreachable while x0 < total
+
+  int x = x0;
+  while (true) {
+    const int L = readlane_i(Lreg, s - base);
+    const int R1 = R0 + (L + kBlock - 1) / kBlock;
+    const int e = min(x1, R1);
+    const int vf = R0 / per;
+    const int K = (R1 - 1) / per - vf + 1;
+    const int slot = v - vf;
+    if (g == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
+    mfma_segment<D, KV, OUT, PKV_BAL_STAGES>(a, s, g, L, x - R0, e - R0, slot, K == 1, lds_k,
+                                             lds_v);
+    if (e >= x1) break;
+    x = e;
+    R0 = R1;
+    // next sequence with at least one block (one exists: x < x1 <= total)
+    int Lnext = 0;
+    while (Lnext == 0 && s + 1 < B) {
+      ++s;
+      if (s - base >= kWave) {
+        carry = readlane_i(incl, kWave - 1);
+        base += kWave;
+        const int si = base + lane;
+        Lreg = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+        incl = wave_incl_scan((Lreg + kBlock - 1) / kBlock) + carry;
+      }
+      Lnext = readlane_i(Lreg, s - base);
+    }
+    if (Lnext == 0) break;
   }
 }
 
@@ -392,7 +562,8 @@ template <int D, int OUT, int MAXG>
 __global__ __launch_bounds__(64) void decode_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens, int hq,
-    int hkv, int G, int num_blocks, float scale_log2, int part_blocks, int n_parts,
+    int hkv, int G, int num_blocks, size_t bstride, float scale_log2, int part_blocks, int n_parts,
+    int kstride,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
     void* __restrict__ out, const float* __restrict__ kn, const float* __restrict__ vn,
     float* __restrict__ kc_w, float* __restrict__ vc_w) {
@@ -451,7 +622,8 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
     }
     const int ph = trow[(L - 1) / kBlock];
     if (ph >= 0 && ph < num_blocks) {
-      const size_t dst = (((size_t)ph * hkv + g) * kBlock + (L - 1) % kBlock) * D + lane * kPer;
+      const size_t dst = (size_t)ph * bstride + ((size_t)g * kBlock + (L - 1) % kBlock) * D +
+                         lane * kPer;
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
         kc_w[dst + e] = kx[e];
@@ -464,7 +636,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
     if (phys < 0 || phys >= num_blocks) continue;
     const int valid = min(kBlock, L - b * kBlock);
     for (int o = 0; o < valid; ++o) {
-      const size_t base = (((size_t)phys * hkv + g) * kBlock + o) * D + lane * kPer;
+      const size_t base = (size_t)phys * bstride + ((size_t)g * kBlock + o) * D + lane * kPer;
       const bool is_new = app && b * kBlock + o == L - 1;
       float kv[kPer], vv[kPer];
 #pragma unroll
@@ -502,7 +674,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
         else static_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(acc[hh][e] * inv);
       }
     } else {
-      const size_t pr = row * n_parts + p;
+      const size_t pr = row * kstride + p;
 #pragma unroll
       for (int e = 0; e < kPer; ++e) ws_o[pr * D + lane * kPer + e] = acc[hh][e] * inv;
       if (lane == 0) {
@@ -515,18 +687,21 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 
 // ---------------------------------------------------------------------------
 // Cross-partition combine: one wavefront per (sequence, query head) row with
-// more than one partition; M = max_p m_p, w_p = 2^(m_p - M) l_p,
-// out = sum_p w_p o_p / sum_p w_p.  Lane p holds partition p's weight (64
-// partitions at a time); the partial rows are read D/4 lanes per row, several
+// more than one partial; M = max_p m_p, w_p = 2^(m_p - M) l_p,
+// out = sum_p w_p o_p / sum_p w_p.  Lane p holds partial p's weight (64
+// partials at a time); the partial rows are read D/4 lanes per row, several
 // rows per load instruction, through a descriptor bounded to this row's
-// partitions so that every load is issued unconditionally.
+// partials so that every load is issued unconditionally.  The number of
+// partials is ceil(blocks / part_blocks) for a fixed split, or the count the
+// decode kernel recorded per sequence for a balanced split (`counts`).
 template <int D, int OUT>
 __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws_m,
                                                     const float* __restrict__ ws_l,
                                                     const float* __restrict__ ws_o,
+                                                    const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ lens,
                                                     int max_blocks, int hq, int part_blocks,
-                                                    int n_parts, void* __restrict__ out) {
+                                                    int kstride, void* __restrict__ out) {
   constexpr int kCols = D / 4;             // lanes per partial row (16-byte pieces)
   constexpr int kRowsPerLoad = kWave / kCols;
   const int row = blockIdx.x;
@@ -534,17 +709,23 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   const int lane = threadIdx.x;
   int L = lens[s];
   if (L < 0 || L > max_blocks * kBlock) L = 0;
-  const int nblk = (L + kBlock - 1) / kBlock;
-  const int parts = (nblk + part_blocks - 1) / part_blocks;
+  if (L == 0) return;
+  int parts;
+  if (counts != nullptr) {
+    parts = min(counts[s], kstride);
+  } else {
+    const int nblk = (L + kBlock - 1) / kBlock;
+    parts = (nblk + part_blocks - 1) / part_blocks;
+  }
   if (parts <= 1) return;
-  const float* mrow = ws_m + (size_t)row * n_parts;
-  const float* lrow = ws_l + (size_t)row * n_parts;
+  const float* mrow = ws_m + (size_t)row * kstride;
+  const float* lrow = ws_l + (size_t)row * kstride;
   float M = -INFINITY;
   for (int c = 0; c < parts; c += kWave)
     if (c + lane < parts) M = fmaxf(M, mrow[c + lane]);
   M = wave_max(M);
   const int sub = lane / kCols, col = lane % kCols;
-  const rsrc_t ro = make_rsrc(ws_o + (size_t)row * n_parts * D, parts * D * 4);
+  const rsrc_t ro = make_rsrc(ws_o + (size_t)row * kstride * D, parts * D * 4);
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int c = 0; c < parts; c += kWave) {
@@ -553,7 +734,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
     const int cnt = min(kWave, parts - c);
 #pragma unroll 4
     for (int q = 0; q < cnt; q += kRowsPerLoad) {
-      const int pp = q + sub;              // partition within this group of 64
+      const int pp = q + sub;              // partial within this group of 64
       const float w = __shfl(wp, pp & (kWave - 1), kWave);
       const u32x4 v = buffer_load16(ro, ((c + pp) * D + col * 4) * 4);
       a += w * __builtin_bit_cast(f32x4, v);
@@ -567,9 +748,30 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   if (sub == 0) store_out4<D, OUT>(out, (size_t)row * D + col * 4, a * (1.0f / den));
 }
 
+// One-wavefront workgroups of `kernel` that fit on a compute unit at once
+// (register and LDS limits); looked up once per kernel.
+int resident_waves_per_cu(const void* kernel) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kWave, 0) != hipSuccess)
+    return -1;
+  cache.emplace(kernel, blocks);
+  return blocks;
+}
+
+// Launch geometry of one decode call.
 struct Plan {
-  int part_blocks, n_parts;
+  bool balanced;      // balanced split (MFMA path)
+  int part_blocks;    // fixed split: blocks per partition
+  int n_parts;        // fixed split: partitions per sequence
+  int kstride;        // partial slots per row in the workspace
+  int cus;            // balanced split: compute units of the device
   float *ws_m, *ws_l, *ws_o;
+  int32_t* ws_count;
 };
 
 template <int D, int OUT>
@@ -577,74 +779,146 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
   const pkv_cache_t& c = *a.cache;
   const int hkv = c.num_kv_heads, hq = a.num_q_heads, G = hq / hkv;
   const float sl2 = a.scale * kLog2e;
-  dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts)), block(kWave);
+  dim3 block(kWave);
   int rc;
-  switch (c.kv_dtype) {
-    case PKV_F32:
-      rc = launch(decode_f32_kernel<D, OUT, 16>, grid, block, st, (const float*)a.q,
-                  (const float*)c.k_cache, (const float*)c.v_cache, a.tables, a.max_blocks,
-                  a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
-                  pl.ws_l, pl.ws_o, a.out, (const float*)a.k_new, (const float*)a.v_new,
-                  (float*)c.k_cache, (float*)c.v_cache);
-      break;
-    case PKV_BF16:
-      rc = launch(decode_mfma_kernel<D, KV_BF16, OUT>, grid, block, st, (const uint16_t*)a.q,
-                  (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache, (const float*)nullptr,
-                  (const float*)nullptr, a.tables, a.max_blocks, a.lens, hq, hkv, G,
-                  c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m, pl.ws_l, pl.ws_o,
-                  a.out, (const uint8_t*)a.k_new, (const uint8_t*)a.v_new, (uint8_t*)c.k_cache,
-                  (uint8_t*)c.v_cache);
-      break;
-    case PKV_I8:
-      rc = launch(decode_mfma_kernel<D, KV_I8, OUT>, grid, block, st, (const uint16_t*)a.q,
-                  (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache,
-                  (const float*)c.k_scale, (const float*)c.v_scale, a.tables, a.max_blocks,
-                  a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
-                  pl.ws_l, pl.ws_o, a.out, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
-                  (uint8_t*)nullptr, (uint8_t*)nullptr);
-      break;
-    default:
-      rc = launch(decode_mfma_kernel<D, KV_FP8, OUT>, grid, block, st, (const uint16_t*)a.q,
-                  (const uint8_t*)c.k_cache, (const uint8_t*)c.v_cache,
-                  (const float*)c.k_scale, (const float*)c.v_scale, a.tables, a.max_blocks,
-                  a.lens, hq, hkv, G, c.num_blocks, sl2, pl.part_blocks, pl.n_parts, pl.ws_m,
-                  pl.ws_l, pl.ws_o, a.out, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
-                  (uint8_t*)nullptr, (uint8_t*)nullptr);
-      break;
+  if (c.kv_dtype == PKV_F32) {
+    dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts));
+    rc = launch(decode_f32_kernel<D, OUT, 16>, grid, block, st, (const float*)a.q,
+                (const float*)c.k_cache, (const float*)c.v_cache, a.tables, a.max_blocks,
+                a.lens, hq, hkv, G, c.num_blocks, block_stride_bytes(c) / sizeof(float), sl2,
+                pl.part_blocks, pl.n_parts, pl.kstride,
+                pl.ws_m, pl.ws_l, pl.ws_o, a.out, (const float*)a.k_new, (const float*)a.v_new,
+                (float*)c.k_cache, (float*)c.v_cache);
+  } else {
+    MfmaArgs m;
+    m.q = (const uint16_t*)a.q;
+    m.kc = (const uint8_t*)c.k_cache;
+    m.vc = (const uint8_t*)c.v_cache;
+    const bool q8 = c.kv_dtype != PKV_BF16;
+    m.ksc = q8 ? c.k_scale : nullptr;
+    m.vsc = q8 ? c.v_scale : nullptr;
+    m.tables = a.tables;
+    m.lens = a.lens;
+    m.max_blocks = a.max_blocks;
+    m.num_seqs = a.num_seqs;
+    m.hq = hq;
+    m.hkv = hkv;
+    m.G = G;
+    m.num_blocks = c.num_blocks;
+    m.blk_stride = block_stride_bytes(c);
+    m.scale_log2 = sl2;
+    m.ws_m = pl.ws_m;
+    m.ws_l = pl.ws_l;
+    m.ws_o = pl.ws_o;
+    m.ws_count = pl.ws_count;
+    m.kstride = pl.kstride;
+    m.part_blocks = pl.part_blocks;
+    m.min_blocks = kBalancedMinBlocks;
+    m.out = a.out;
+    m.kn = q8 ? nullptr : (const uint8_t*)a.k_new;
+    m.vn = q8 ? nullptr : (const uint8_t*)a.v_new;
+    m.kc_w = (uint8_t*)c.k_cache;
+    m.vc_w = (uint8_t*)c.v_cache;
+    auto go = [&](auto fixed_kernel, auto balanced_kernel) {
+      if (pl.balanced) {
+        // one generation: as many wavefronts as the GPU holds at once
+        const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(balanced_kernel));
+        if (per_cu <= 0) return (int)PKV_ERR_HIP;
+        const int64_t waves = (int64_t)pl.cus * per_cu;
+        dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv));
+        return launch(balanced_kernel, grid, block, st, m);
+      }
+      dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts));
+      return launch(fixed_kernel, grid, block, st, m, pl.n_parts);
+    };
+    switch (c.kv_dtype) {
+      case PKV_BF16:
+        rc = go(decode_mfma_kernel<D, KV_BF16, OUT>, decode_mfma_balanced_kernel<D, KV_BF16, OUT>);
+        break;
+      case PKV_I8:
+        rc = go(decode_mfma_kernel<D, KV_I8, OUT>, decode_mfma_balanced_kernel<D, KV_I8, OUT>);
+        break;
+      default:
+        rc = go(decode_mfma_kernel<D, KV_FP8, OUT>, decode_mfma_balanced_kernel<D, KV_FP8, OUT>);
+        break;
+    }
   }
-  if (rc != PKV_OK || pl.n_parts <= 1) return rc;
+  if (rc != PKV_OK || pl.kstride <= 1) return rc;
   dim3 rgrid((unsigned)((int64_t)a.num_seqs * hq));
   return launch(reduce_kernel<D, OUT>, rgrid, block, st, (const float*)pl.ws_m,
-                (const float*)pl.ws_l, (const float*)pl.ws_o, a.lens, a.max_blocks, hq,
-                pl.part_blocks, pl.n_parts, a.out);
+                (const float*)pl.ws_l, (const float*)pl.ws_o,
+                (const int32_t*)(pl.balanced ? pl.ws_count : nullptr), a.lens, a.max_blocks, hq,
+                pl.part_blocks, pl.kstride, a.out);
 }
 
 }  // namespace
 
-// Workspace layout for a split launch with P partitions and R = B * Hq rows:
-// o [R][P][D] binary32, then m [R][P], then l [R][P], each 256-byte aligned.
-size_t decode_workspace_layout(int64_t rows, int n_parts, int D, size_t* off_m, size_t* off_l) {
+// Workspace layout for R = B * Hq rows and K partial slots per row:
+// o [R][K][D] binary32, then m [R][K], then l [R][K], then (balanced split)
+// one int32 count per sequence, each part 256-byte aligned.
+size_t decode_workspace_layout(int64_t rows, int kslots, int D, int64_t num_seqs, size_t* off_m,
+                               size_t* off_l, size_t* off_count) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  size_t o_bytes = up((size_t)rows * n_parts * D * 4);
-  size_t m_bytes = up((size_t)rows * n_parts * 4);
+  size_t o_bytes = up((size_t)rows * kslots * D * 4);
+  size_t m_bytes = up((size_t)rows * kslots * 4);
+  size_t c_bytes = up((size_t)num_seqs * 4);
   if (off_m) *off_m = o_bytes;
   if (off_l) *off_l = o_bytes + m_bytes;
-  return o_bytes + 2 * m_bytes;
+  if (off_count) *off_count = o_bytes + 2 * m_bytes;
+  return o_bytes + 2 * m_bytes + c_bytes;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int decode_slots(int max_blocks, int partition_tokens) {
+  if (partition_tokens == PKV_SPLIT_BALANCED)
+    return (max_blocks + kBalancedMinBlocks - 1) / kBalancedMinBlocks + 1;
+  const int part_blocks = partition_tokens > 0 ? partition_tokens / kBlock : max_blocks;
+  return (max_blocks + part_blocks - 1) / part_blocks;
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t st) {
   const pkv_cache_t& c = *a.cache;
   Plan pl;
-  pl.part_blocks = a.partition_tokens > 0 ? a.partition_tokens / kBlock : a.max_blocks;
+  pl.balanced = a.partition_tokens == PKV_SPLIT_BALANCED;
+  pl.kstride = decode_slots(a.max_blocks, a.partition_tokens);
+  if (pl.balanced) {
+    // fp32 pools (a parity path) take the fixed split at the same minimum size
+    pl.part_blocks = kBalancedMinBlocks;
+    if (c.kv_dtype == PKV_F32) pl.balanced = false;
+  } else {
+    pl.part_blocks = a.partition_tokens > 0 ? a.partition_tokens / kBlock : a.max_blocks;
+  }
   pl.n_parts = (a.max_blocks + pl.part_blocks - 1) / pl.part_blocks;
+  pl.cus = 0;
+  if (pl.balanced) {
+    pl.cus = device_cu_count();
+    if (pl.cus <= 0) return PKV_ERR_HIP;
+  }
   pl.ws_m = pl.ws_l = pl.ws_o = nullptr;
-  if (pl.n_parts > 1) {
-    size_t om, ol;
-    decode_workspace_layout((int64_t)a.num_seqs * a.num_q_heads, pl.n_parts, c.head_dim, &om, &ol);
+  pl.ws_count = nullptr;
+  if (pl.kstride > 1) {
+    size_t om, ol, oc;
+    decode_workspace_layout((int64_t)a.num_seqs * a.num_q_heads, pl.kstride, c.head_dim,
+                            a.num_seqs, &om, &ol, &oc);
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     pl.ws_o = reinterpret_cast<float*>(ws);
     pl.ws_m = reinterpret_cast<float*>(ws + om);
     pl.ws_l = reinterpret_cast<float*>(ws + ol);
+    pl.ws_count = reinterpret_cast<int32_t*>(ws + oc);
   }
   const bool bf16_out = a.out_dtype == PKV_BF16;
   if (c.head_dim == 128)

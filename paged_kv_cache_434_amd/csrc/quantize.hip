@@ -44,7 +44,8 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
                                                       float* __restrict__ kscale,
                                                       float* __restrict__ vscale,
                                                       const int32_t* __restrict__ ids,
-                                                      int hkv, int num_blocks) {
+                                                      int hkv, int num_blocks, int64_t src_stride,
+                                                      int64_t dst_stride) {
   constexpr int kElems = kBlock * D;             // values per tile
   constexpr int kPerLane = kElems / kWave;       // 16 (D=64) or 32 (D=128)
   constexpr int kVec = 16 / sizeof(SrcT);        // values per 16-byte load
@@ -55,8 +56,8 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
   const int b = ids ? ids[idx] : idx;
   if (b < 0 || b >= num_blocks) return;
   const bool is_v = blockIdx.y != 0;
-  const SrcT* src = (is_v ? vsrc : ksrc) + ((size_t)b * hkv + g) * kElems;
-  uint8_t* dst = (is_v ? vdst : kdst) + ((size_t)b * hkv + g) * kElems;
+  const SrcT* src = (is_v ? vsrc : ksrc) + (size_t)b * src_stride + (size_t)g * kElems;
+  uint8_t* dst = (is_v ? vdst : kdst) + (size_t)b * dst_stride + (size_t)g * kElems;
 
   // lane owns values [ld*64*kVec + lane*kVec, +kVec) for each load ld
   float x[kPerLane];
@@ -122,7 +123,8 @@ int launch_q(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids,
   dim3 grid((unsigned)(n * src.num_kv_heads), 2), block(kWave);
   return launch(quantize_kernel<SrcT, D, FP8>, grid, block, st, (const SrcT*)src.k_cache,
                 (const SrcT*)src.v_cache, (uint8_t*)dst.k_cache, (uint8_t*)dst.v_cache,
-                dst.k_scale, dst.v_scale, ids, src.num_kv_heads, src.num_blocks);
+                dst.k_scale, dst.v_scale, ids, src.num_kv_heads, src.num_blocks,
+                (int64_t)(block_stride_bytes(src) / sizeof(SrcT)), (int64_t)block_stride_bytes(dst));
 }
 
 template <typename SrcT, int D>

@@ -226,9 +226,11 @@ def make(cfg: int, seed: Optional[int] = None, quant: Optional[str] = None, **ov
                     quant=quant if cfg == 5 else None)
 
 
-def to_device(wl: Workload, device="cuda") -> dict:
+def to_device(wl: Workload, device="cuda", layout: str = "split") -> dict:
     """Copy a workload's arrays to the GPU as torch tensors (bf16 bit patterns
-    become torch.bfloat16)."""
+    become torch.bfloat16).  layout "split": K and V pools are two dense
+    [NB][Hkv][16][D] tensors; "blocks": one [NB][2][Hkv][16][D] tensor ``kv``
+    whose halves are returned as the (block-strided) ``k_pool`` / ``v_pool``."""
     import torch
 
     def dev(a, kind):
@@ -239,10 +241,23 @@ def to_device(wl: Workload, device="cuda") -> dict:
                 torch.bfloat16).to(device)
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
-    return dict(q=dev(wl.q, wl.q_dtype), k_pool=dev(wl.k_pool, wl.kv_dtype),
-                v_pool=dev(wl.v_pool, wl.kv_dtype), k_new=dev(wl.k_new, wl.kv_dtype),
-                v_new=dev(wl.v_new, wl.kv_dtype), tables=dev(wl.tables, "i32"),
-                lens=dev(wl.lens, "i32"))
+    out = dict(q=dev(wl.q, wl.q_dtype), k_new=dev(wl.k_new, wl.kv_dtype),
+               v_new=dev(wl.v_new, wl.kv_dtype), tables=dev(wl.tables, "i32"),
+               lens=dev(wl.lens, "i32"))
+    if layout == "split":
+        out["k_pool"] = dev(wl.k_pool, wl.kv_dtype)
+        out["v_pool"] = dev(wl.v_pool, wl.kv_dtype)
+    elif layout == "blocks":
+        k = dev(wl.k_pool, wl.kv_dtype)
+        kv = torch.empty((k.shape[0], 2) + tuple(k.shape[1:]), dtype=k.dtype, device=device)
+        kv[:, 0].copy_(k)
+        del k
+        kv[:, 1].copy_(dev(wl.v_pool, wl.kv_dtype))
+        out["kv"] = kv
+        out["k_pool"], out["v_pool"] = kv[:, 0], kv[:, 1]
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    return out
 
 
 def from_device(t) -> np.ndarray:

@@ -58,13 +58,20 @@ def test_workspace_sizes():
     rows, parts = 8 * 32, 64
     assert ws >= rows * parts * (128 + 2) * 4 and ws % 256 == 0
     assert lib.pkv_decode_workspace_bytes(8, 32, 128, 2048, 500) == 0    # not a multiple of 16
+    assert lib.pkv_decode_workspace_bytes(8, 32, 128, 2048, -2) == 0     # negative, not balanced
+    # balanced split: ceil(max_blocks / 8) + 1 slots per row, plus one count per sequence
+    wb = lib.pkv_decode_workspace_bytes(8, 32, 128, 2048, pkv.SPLIT_BALANCED)
+    slots = 2048 // 8 + 1
+    assert wb >= rows * slots * (128 + 2) * 4 + 8 * 4 and wb % 256 == 0
+    assert lib.pkv_decode_workspace_bytes(3, 4, 64, 1, pkv.SPLIT_BALANCED) > 0
 
 
 def test_default_partition_is_valid():
     lib = pkv.lib()
     for B, H, mb in [(64, 8, 256), (256, 8, 512), (8, 8, 2048), (1, 1, 1), (4, 2, 7)]:
         p = lib.pkv_decode_default_partition(B, H, mb)
-        assert p == 0 or (p % 16 == 0 and p > 0)
+        assert p == pkv.SPLIT_BALANCED
+    assert lib.pkv_decode_default_partition(0, 8, 256) == 0
 
 
 def _decode(cache, q=FAKE, q_dtype=1, tables=FAKE, maxb=4, lens=FAKE, B=2, Hq=4,
@@ -101,6 +108,8 @@ def test_decode_rejects_bad_arguments():
     assert _decode(c, out=None) == 1
     assert _decode(c, B=0) == 0                        # nothing to do, no launch
     assert _decode(c, maxb=64, part=256) == 5          # split needs a workspace
+    assert _decode(c, maxb=64, part=pkv.SPLIT_BALANCED) == 5
+    assert _decode(c, maxb=1, part=pkv.SPLIT_BALANCED) == 5
     need = pkv.lib().pkv_decode_workspace_bytes(2, 4, 128, 64, 256)
     assert _decode(c, maxb=64, part=256, ws=FAKE, ws_bytes=need - 1) == 5
     assert _decode(c, maxb=64, part=256, ws=FAKE + 16, ws_bytes=need) == 5   # alignment

@@ -54,19 +54,24 @@ def _dev_cache(d, wl, kv_dtype=None):
 
 
 def _step(wl, d, part, out_dtype, quant=None):
-    """cache write (if any) then attention on the GPU; returns (out, host pools)."""
+    """cache write (if any) then attention on the GPU; returns (out, device cache).
+    A device dict holding ``kv`` (per-block layout) gets quantized codes in the
+    same layout."""
     cache = _dev_cache(d, wl)
     if wl.write:
         slots = pkv.slot_mapping(d["tables"], d["lens"])
         pkv.cache_write(cache, d["k_new"], d["v_new"], slots)
     if quant:
         NB, Hkv, bs, D = d["k_pool"].shape
-        kq = torch.empty((NB, Hkv, bs, D), dtype=torch.int8 if quant == "i8" else torch.uint8,
-                         device="cuda")
-        vq = torch.empty_like(kq)
+        qt = torch.int8 if quant == "i8" else torch.uint8
         ks = torch.empty((NB, Hkv), dtype=torch.float32, device="cuda")
         vs = torch.empty_like(ks)
-        qcache = pkv.PagedCache(kq, vq, quant, ks, vs)
+        if "kv" in d:
+            qcache = pkv.PagedCache.from_blocks(
+                torch.empty((NB, 2, Hkv, bs, D), dtype=qt, device="cuda"), quant, ks, vs)
+        else:
+            kq = torch.empty((NB, Hkv, bs, D), dtype=qt, device="cuda")
+            qcache = pkv.PagedCache(kq, torch.empty_like(kq), quant, ks, vs)
         pkv.quantize(cache, qcache)
         cache = qcache
     out = pkv.attention_decode(cache, d["q"], d["tables"], d["lens"], float(wl.scale),
@@ -209,6 +214,16 @@ SMALL = [
     (2, dict(B=4, lo=1, hi=300, pool=200, Hq=6, Hkv=2), 0),          # G = 3
     (2, dict(B=6, lo=1, hi=500, pool=400, D=64), 128),               # bf16, D = 64
     (1, dict(D=128, lens=[1, 77, 300, 5]), 64),                      # fp32, D = 128
+    # balanced split (partition_tokens = -1)
+    (1, {}, -1),
+    (2, dict(B=9, lo=1, hi=700, pool=600), -1),
+    (2, dict(B=5, lens=[0, 1, 16, 17, 4096], hi=4096, pool=600), -1),
+    (3, dict(B=24, median=300, lo=1, hi=1000), -1),
+    (3, dict(B=150, median=40, lo=1, hi=300), -1),                   # ranges span many sequences
+    (4, dict(B=2, L=4096), -1),
+    (2, dict(B=4, lo=1, hi=300, pool=200, Hq=16, Hkv=1), -1),        # G = 16
+    (2, dict(B=4, lo=1, hi=300, pool=200, Hq=6, Hkv=2), -1),         # G = 3
+    (2, dict(B=6, lo=1, hi=500, pool=400, D=64), -1),                # bf16, D = 64
 ]
 
 
@@ -225,7 +240,7 @@ def test_attention_small(cfg, over, part, out_dtype):
 
 
 @pytest.mark.parametrize("quant", ["i8", "fp8"])
-@pytest.mark.parametrize("part", [0, 256])
+@pytest.mark.parametrize("part", [0, 256, -1])
 def test_attention_quant_small(quant, part):
     wl = W.make(5, B=10, prefix=256, suffix_hi=300, quant=quant)
     _say(f"attention quant small: {quant} part={part}")
@@ -263,7 +278,8 @@ def test_fp8_code_decode_exact():
 # ------------------------------------------------------------------ full-size runs
 
 FULL = [(1, None, 0), (2, None, 256), (2, None, 0), (3, None, 1024), (4, None, 512),
-        (5, "i8", 256), (5, "fp8", 256)]
+        (5, "i8", 256), (5, "fp8", 256),
+        (2, None, -1), (3, None, -1), (4, None, -1), (5, "i8", -1), (5, "fp8", -1)]
 
 
 @functools.lru_cache(maxsize=2)
@@ -287,12 +303,13 @@ def test_attention_full_size(cfg, quant, part):
 # ------------------------------------------------------------------- invariants
 
 
-def test_nan_in_unused_slots_and_entries_bit_identical():
+@pytest.mark.parametrize("part", [128, -1])
+def test_nan_in_unused_slots_and_entries_bit_identical(part):
     wl = W.make(2, B=8, lo=1, hi=600, pool=500)
     d = W.to_device(wl)
     cache = _dev_cache(d, wl)
     base = pkv.attention_decode(cache, d["q"], d["tables"], d["lens"], float(wl.scale),
-                                partition_tokens=128, out_dtype=torch.float32).clone()
+                                partition_tokens=part, out_dtype=torch.float32).clone()
     k, v = wl.k_pool.copy(), wl.v_pool.copy()
     used = np.zeros(wl.num_blocks, dtype=bool)
     tables = wl.tables.copy()
@@ -312,18 +329,19 @@ def test_nan_in_unused_slots_and_entries_bit_identical():
     wl2 = W.Workload(**{**wl.__dict__, "k_pool": k, "v_pool": v, "tables": tables})
     d2 = W.to_device(wl2)
     got = pkv.attention_decode(_dev_cache(d2, wl2), d2["q"], d2["tables"], d2["lens"],
-                               float(wl.scale), partition_tokens=128, out_dtype=torch.float32)
+                               float(wl.scale), partition_tokens=part, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(base, got)
 
 
-def test_block_permutation_invariance_and_determinism():
+@pytest.mark.parametrize("part", [256, -1])
+def test_block_permutation_invariance_and_determinism(part):
     wl = W.make(2, B=8, lo=1, hi=600, pool=500)
     d = W.to_device(wl)
     a = pkv.attention_decode(_dev_cache(d, wl), d["q"], d["tables"], d["lens"], float(wl.scale),
-                             partition_tokens=256, out_dtype=torch.float32).clone()
+                             partition_tokens=part, out_dtype=torch.float32).clone()
     b = pkv.attention_decode(_dev_cache(d, wl), d["q"], d["tables"], d["lens"], float(wl.scale),
-                             partition_tokens=256, out_dtype=torch.float32).clone()
+                             partition_tokens=part, out_dtype=torch.float32).clone()
     assert torch.equal(a, b)
     pi = np.random.default_rng(1).permutation(wl.num_blocks)
     k2 = np.empty_like(wl.k_pool)
@@ -334,7 +352,7 @@ def test_block_permutation_invariance_and_determinism():
                         "tables": pi[wl.tables].astype(np.int32)})
     d2 = W.to_device(wl2)
     c = pkv.attention_decode(_dev_cache(d2, wl2), d2["q"], d2["tables"], d2["lens"],
-                             float(wl.scale), partition_tokens=256, out_dtype=torch.float32)
+                             float(wl.scale), partition_tokens=part, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, c)
 
@@ -344,9 +362,9 @@ def test_split_and_unsplit_agree():
     d = W.to_device(wl)
     outs = [pkv.attention_decode(_dev_cache(d, wl), d["q"], d["tables"], d["lens"],
                                  float(wl.scale), partition_tokens=p,
-                                 out_dtype=torch.float32).cpu().numpy() for p in (0, 256, 512)]
-    assert np.max(np.abs(outs[0] - outs[1])) < 2e-3
-    assert np.max(np.abs(outs[0] - outs[2])) < 2e-3
+                                 out_dtype=torch.float32).cpu().numpy() for p in (0, 256, 512, -1)]
+    for o in outs[1:]:
+        assert np.max(np.abs(outs[0] - o)) < 2e-3
 
 
 def test_validate_tables_reports_bad_entries():
@@ -368,6 +386,9 @@ STEP_CASES = [
     (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 64),
     (3, dict(B=20, median=300, lo=1, hi=1200), 256),
     (2, dict(B=4, lo=1, hi=400, pool=200, D=64), 128),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), -1),
+    (3, dict(B=100, median=60, lo=1, hi=600), -1),
+    (1, {}, -1),
 ]
 
 
@@ -396,7 +417,7 @@ def test_decode_step_matches_write_then_attention(cfg, over, part):
     _cmp(_out_np(out2), ref, TOL[wl.kv_dtype], "f32", f"step {wl.name}")
 
 
-@pytest.mark.parametrize("cfg,part", [(2, 256), (3, 1024), (4, 512)])
+@pytest.mark.parametrize("cfg,part", [(2, 256), (3, 1024), (4, 512), (2, -1), (3, -1), (4, -1)])
 def test_decode_step_full_size(cfg, part):
     wl = _full_workload(cfg)
     _say(f"decode step full: {wl.name} part={part}")
@@ -404,6 +425,109 @@ def test_decode_step_full_size(cfg, part):
     cache = _dev_cache(d, wl)
     out = pkv.decode_step(cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"],
                           float(wl.scale), partition_tokens=part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _ = _oracle_step(wl)
+    err = _cmp(_out_np(out), ref, TOL[wl.kv_dtype], "bf16", wl.name)
+    _say(f"  max abs err {err:.3e}")
+
+
+# ------------------------------------------------ per-block layout [NB][2][Hkv][16][D]
+
+
+@pytest.mark.parametrize("cfg,over", [(1, {}), (2, dict(B=16, pool=None))])
+def test_blocks_layout_cache_write_and_gather_bit_exact(cfg, over):
+    wl = W.make(cfg, **over)
+    _say(f"blocks layout write/gather: {wl.name}")
+    d = W.to_device(wl, layout="blocks")
+    cache = _dev_cache(d, wl)
+    assert cache.block_stride == 2 * wl.Hkv * 16 * wl.D
+    slots = pkv.slot_mapping(d["tables"], d["lens"])
+    pkv.cache_write(cache, d["k_new"], d["v_new"], slots)
+    k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    oracle.cache_write(k, v, wl.kv_dtype, wl.k_new, wl.v_new,
+                       oracle.slot_mapping(wl.tables, wl.lens))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.from_device(d["k_pool"]), k)
+    assert np.array_equal(W.from_device(d["v_pool"]), v)
+    ko_ref, vo_ref, cu = oracle.gather(k, v, wl.kv_dtype, wl.tables, wl.lens)
+    ko, vo = pkv.gather(cache, d["tables"], d["lens"], torch.from_numpy(cu).cuda(), int(cu[-1]))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.from_device(ko), ko_ref)
+    assert np.array_equal(W.from_device(vo), vo_ref)
+
+
+@pytest.mark.parametrize("dst", ["i8", "fp8"])
+def test_blocks_layout_quantize_bit_exact(dst):
+    wl = W.make(5, B=6, prefix=64, suffix_hi=40)
+    d = W.to_device(wl, layout="blocks")
+    kc, ks = oracle.quantize(wl.k_pool, "bf16", dst)
+    vc, vs = oracle.quantize(wl.v_pool, "bf16", dst)
+    NB = wl.num_blocks
+    qt = torch.int8 if dst == "i8" else torch.uint8
+    kss = torch.empty((NB, wl.Hkv), dtype=torch.float32, device="cuda")
+    vss = torch.empty_like(kss)
+    kvq = torch.full((NB, 2, wl.Hkv, 16, wl.D), 7, dtype=qt, device="cuda")
+    pkv.quantize(_dev_cache(d, wl), pkv.PagedCache.from_blocks(kvq, dst, kss, vss))
+    torch.cuda.synchronize()
+    got = kvq.cpu().numpy()
+    assert np.array_equal(got[:, 0], kc) and np.array_equal(got[:, 1], vc)
+    assert np.array_equal(kss.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(vss.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+
+
+BLOCKS_CASES = [
+    (1, {}, None, 0),
+    (1, {}, None, -1),
+    (2, dict(B=9, lo=1, hi=700, pool=600), None, 256),
+    (2, dict(B=9, lo=1, hi=700, pool=600), None, -1),
+    (3, dict(B=40, median=200, lo=1, hi=900), None, -1),
+    (2, dict(B=6, lo=1, hi=500, pool=400, D=64), None, -1),
+    (5, dict(B=10, prefix=256, suffix_hi=300), "i8", -1),
+    (5, dict(B=10, prefix=256, suffix_hi=300), "fp8", 256),
+]
+
+
+@pytest.mark.parametrize("cfg,over,quant,part", BLOCKS_CASES)
+def test_blocks_layout_attention(cfg, over, quant, part):
+    wl = W.make(cfg, quant=quant, **over)
+    _say(f"blocks layout attention: {wl.name} {over} quant={quant} part={part}")
+    d = W.to_device(wl, layout="blocks")
+    out, _ = _step(wl, d, part, torch.float32, quant)
+    ref, _ = _oracle_step(wl, quant)
+    _cmp(_out_np(out), ref, TOL[quant or wl.kv_dtype], "f32", f"blocks {wl.name}")
+
+
+@pytest.mark.parametrize("cfg,over,part", [
+    (1, {}, -1),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), -1),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 64),
+])
+def test_blocks_layout_decode_step(cfg, over, part):
+    wl = W.make(cfg, **over)
+    _say(f"blocks layout decode step: {wl.name} {over} part={part}")
+    d = W.to_device(wl, layout="blocks")
+    out = pkv.decode_step(_dev_cache(d, wl), d["q"], d["k_new"], d["v_new"], d["tables"],
+                          d["lens"], float(wl.scale), partition_tokens=part,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    oracle.cache_write(k, v, wl.kv_dtype, wl.k_new, wl.v_new,
+                       oracle.slot_mapping(wl.tables, wl.lens))
+    assert np.array_equal(W.from_device(d["k_pool"]), k)
+    assert np.array_equal(W.from_device(d["v_pool"]), v)
+    ref, _ = _oracle_step(wl)
+    _cmp(_out_np(out), ref, TOL[wl.kv_dtype], "f32", f"blocks step {wl.name}")
+
+
+@pytest.mark.parametrize("cfg,part", [(2, -1), (3, -1), (4, -1)])
+def test_blocks_layout_decode_step_full_size(cfg, part):
+    """The bench configuration: full workload, per-block layout, balanced split."""
+    wl = _full_workload(cfg)
+    _say(f"blocks layout decode step full: {wl.name} part={part}")
+    d = W.to_device(wl, layout="blocks")
+    out = pkv.decode_step(_dev_cache(d, wl), d["q"], d["k_new"], d["v_new"], d["tables"],
+                          d["lens"], float(wl.scale), partition_tokens=part,
+                          out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref, _ = _oracle_step(wl)
     err = _cmp(_out_np(out), ref, TOL[wl.kv_dtype], "bf16", wl.name)
