@@ -241,9 +241,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
   // Fused append (decode step): the new token is position L-1, row L-1 mod 16
   // of logical block (L-1)/16.  The wavefront whose range holds that block
-  // writes the token's K/V row for its KV head into the pool and puts it into
-  // the staged tile, so it attends over the new token without a separate
-  // cache-write launch; no other wavefront reads that block.
+  // loads the token's K/V row for its KV head now; when it stages that block
+  // it puts the row into the LDS tile and stores it into the pool, so it
+  // attends over the new token without a separate cache-write launch.  No
+  // other wavefront reads that block's tile of this head.
   constexpr int kRowChunks = D * 2 / 16;   // 16-byte chunks of one bf16 row
   int new_b = -1, new_r = 0;
   u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
@@ -255,13 +256,6 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         const size_t src = ((size_t)s * hkv + g) * (D * 2) + lane * 16;
         knew = *reinterpret_cast<const u32x4*>(a.kn + src);
         vnew = *reinterpret_cast<const u32x4*>(a.vn + src);
-        const int ph = trow[new_b];
-        if (ph >= 0 && ph < num_blocks) {
-          const size_t dst = (size_t)ph * blk_stride + (size_t)g * kTile + new_r * (D * 2) +
-                             lane * 16;
-          *reinterpret_cast<u32x4*>(a.kc_w + dst) = knew;
-          *reinterpret_cast<u32x4*>(a.vc_w + dst) = vnew;
-        }
       }
     }
   }
@@ -335,6 +329,12 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         if (b == new_b && lane < kRowChunks) {   // the appended token's row
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(new_r, lane)) = knew;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(new_r, lane)) = vnew;
+          if (cur_ok) {
+            const size_t dst = (size_t)cur * blk_stride + (size_t)g * kTile + new_r * (D * 2) +
+                               lane * 16;
+            *reinterpret_cast<u32x4*>(a.kc_w + dst) = knew;
+            *reinterpret_cast<u32x4*>(a.vc_w + dst) = vnew;
+          }
         }
       }
       float kscale = 1.f, vscale = 1.f;
@@ -484,11 +484,34 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   const int V = gridDim.x / a.hkv;
   const int B = a.num_seqs;
 
+  // The lengths of the first kLenChunks * 64 sequences are loaded once, all
+  // at the same time, and kept in registers for both passes and the walk.
+  constexpr int kLenChunks = 4;
+  int lc[kLenChunks];
+#pragma unroll
+  for (int c = 0; c < kLenChunks; ++c) {
+    const int si = c * kWave + lane;
+    lc[c] = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+  }
+  // lengths of sequences base .. base+63 in lane order (base a multiple of 64)
+  auto len_chunk = [&](int base) -> int {
+    const int c = base / kWave;
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kLenChunks; ++i)
+      if (c == i) r = lc[i];
+    if (c >= kLenChunks) {
+      const int si = base + lane;
+      r = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+    }
+    return r;
+  };
+
   // pass 1: total blocks per KV head; zero rows of empty sequences
   int total = 0;
   for (int base = 0; base < B; base += kWave) {
     const int si = base + lane;
-    const int Ll = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+    const int Ll = len_chunk(base);
     total += wave_sum_i((Ll + kBlock - 1) / kBlock);
     if (v == 0) {
       uint64_t empty = __ballot(si < B && Ll == 0);
@@ -499,6 +522,10 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
       }
     }
   }
+  // the sums above are equal in every lane; say so, so that everything derived
+  // from them (ranges, block indices, buffer descriptors) stays in scalar
+  // registers instead of being treated as per-lane values
+  total = __builtin_amdgcn_readfirstlane(total);
   const int per = max((total + V - 1) / V, a.min_blocks);
   const int x0 = v * per;
   if (x0 >= total) return;
@@ -508,8 +535,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   // and inclusive prefix of a 64-sequence chunk for the walk below
   int base = 0, carry = 0, s = -1, R0 = 0, Lreg = 0, incl = 0;
   for (; base < B; base += kWave) {
-    const int si = base + lane;
-    Lreg = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+    Lreg = len_chunk(base);
     const int nb = (Lreg + kBlock - 1) / kBlock;
     incl = wave_incl_scan(nb) + carry;
     const uint64_t hit = __ballot(nb > 0 && incl - nb <= x0 && x0 < incl);
@@ -544,8 +570,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
       if (s - base >= kWave) {
         carry = readlane_i(incl, kWave - 1);
         base += kWave;
-        const int si = base + lane;
-        Lreg = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+        Lreg = len_chunk(base);
         incl = wave_incl_scan((Lreg + kBlock - 1) / kBlock) + carry;
       }
       Lnext = readlane_i(Lreg, s - base);
@@ -707,21 +732,26 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   const int row = blockIdx.x;
   const int s = row / hq;
   const int lane = threadIdx.x;
+  const float* mrow = ws_m + (size_t)row * kstride;
+  const float* lrow = ws_l + (size_t)row * kstride;
+  // issued together: the length, the piece count and the first 64 partial
+  // maxima and sums (slots past the count hold stale values and are masked)
   int L = lens[s];
+  const int cnt = counts != nullptr ? counts[s] : 0;
+  const float m0 = lane < kstride ? mrow[lane] : -INFINITY;
+  const float l0 = lane < kstride ? lrow[lane] : 0.f;
   if (L < 0 || L > max_blocks * kBlock) L = 0;
   if (L == 0) return;
   int parts;
   if (counts != nullptr) {
-    parts = min(counts[s], kstride);
+    parts = min(cnt, kstride);
   } else {
     const int nblk = (L + kBlock - 1) / kBlock;
     parts = (nblk + part_blocks - 1) / part_blocks;
   }
   if (parts <= 1) return;
-  const float* mrow = ws_m + (size_t)row * kstride;
-  const float* lrow = ws_l + (size_t)row * kstride;
-  float M = -INFINITY;
-  for (int c = 0; c < parts; c += kWave)
+  float M = lane < parts ? m0 : -INFINITY;
+  for (int c = kWave; c < parts; c += kWave)
     if (c + lane < parts) M = fmaxf(M, mrow[c + lane]);
   M = wave_max(M);
   const int sub = lane / kCols, col = lane % kCols;
@@ -729,11 +759,13 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int c = 0; c < parts; c += kWave) {
-    const float wp = (c + lane < parts) ? exp2f(mrow[c + lane] - M) * lrow[c + lane] : 0.f;
+    float wp = 0.f;
+    if (c + lane < parts)
+      wp = c == 0 ? exp2f(m0 - M) * l0 : exp2f(mrow[c + lane] - M) * lrow[c + lane];
     den += wp;
-    const int cnt = min(kWave, parts - c);
+    const int n64 = min(kWave, parts - c);
 #pragma unroll 4
-    for (int q = 0; q < cnt; q += kRowsPerLoad) {
+    for (int q = 0; q < n64; q += kRowsPerLoad) {
       const int pp = q + sub;              // partial within this group of 64
       const float w = __shfl(wp, pp & (kWave - 1), kWave);
       const u32x4 v = buffer_load16(ro, ((c + pp) * D + col * 4) * 4);
