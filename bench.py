@@ -1,26 +1,35 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
-A step is the whole hot path for one layer of the Llama-3-8B-shaped workload
-(batch 64, 32 query / 8 KV heads, head dim 128, bf16, context lengths uniform
-in [512, 4096], 16-token blocks from a 20,000-block pool): slot mapping of
-each sequence's newest position, the cache write of the new K/V token, and
-paged attention (partition kernel + log-sum-exp combine).  The library's
-decode-step entry runs the first three in the attention launch itself.
+A step is the whole hot path for one layer of a workload (default: the
+Llama-3-8B layer shape -- batch 64, 32 query / 8 KV heads, head dim 128, bf16,
+context lengths uniform in [512, 4096], 16-token blocks from a 20,000-block
+pool): the slot of each sequence's newest position, the cache write of the new
+K/V token and paged attention, which the library's decode-step entry runs in
+one launch, then the log-sum-exp combine of split contexts.  The
+quantized-prefix workload has no new token: its step is attention over a pool
+quantized once before timing.
 
 Inputs are resident in HBM before timing.  To keep the 256 MB Infinity Cache
 from serving a step out of the previous one, the step cycles over R
-independent copies of the inputs (R * 1.3 GB of pools), so the copy a step
-reads was last touched R-1 steps (>= 1.8 GB of other traffic) earlier.
+independent copies of the inputs, so the copy a step reads was last touched
+R-1 steps (>= 1.3 GB of other traffic for the default workload) earlier.
 
-Prints one JSON line.  `value` is KV GB/s of the whole step (algorithmic
-bytes / wall time per step); the roofline object reports the attention call
-(its kernels timed with HIP events on the stream they run on) against the
-8 TB/s HBM peak.  The CPU baseline is the oracle on the host, timed on the
-same workload.
+Prints one JSON line.  `value` is the algorithmic bytes of a step divided by
+the wall time per step (GB/s); `roofline` divides the same bytes by the
+average duration of the step's kernels, measured with HIP events recorded on
+the stream they run on, against the 8 TB/s HBM peak; `traffic` is the HBM
+bytes per step that rocprofv3 counters measured for the current kernel source
+(recorded under profiles/), or null.  The CPU baseline is the oracle on the
+host, timed on the same workload.
+
+    python bench.py                     # headline: Llama-3-8B shape
+    python bench.py --workload 3        # other workloads (1..5; 5 takes --quant)
+    python bench.py --copy-calibration  # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -33,10 +42,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV HBM GB/s (% of peak) + seq-steps/s, Llama-3-8B shape"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("paged_kv_cache_434_amd/csrc/decode.hip", "paged_kv_cache_434_amd/csrc/common.hpp")
 
 
-def algorithmic_bytes(wl, part_blocks_unused=None):
-    """Bytes the method must move for one step (see module docstring)."""
+def algorithmic_bytes(wl):
+    """Bytes the method must move for one step: K/V of every context token,
+    the used block-table entries, 8-bit scales, q in and out, lengths, and for
+    workloads with a new token its K/V row read and written plus its slot."""
     import numpy as np
 
     e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[wl.quant or wl.kv_dtype]
@@ -49,59 +63,121 @@ def algorithmic_bytes(wl, part_blocks_unused=None):
     q_out = wl.B * wl.Hq * wl.D * 2 * e_q
     lens = wl.B * 4
     attention = kv + tables + scales + q_out + lens
-    write = (wl.B * wl.Hkv * wl.D * 2 * e_kv * 2 + wl.B * 4) if wl.write else 0
-    slots = (wl.B * 4 * 2 + wl.B * 4) if wl.write else 0   # lens + one table entry in, slot out
-    return dict(attention=attention, kv=kv, write=write, slots=slots,
-                step=attention + write + slots)
+    write = (wl.B * wl.Hkv * wl.D * 2 * e_kv * 2) if wl.write else 0
+    return dict(attention=attention, kv=kv, write=write, step=attention + write)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(key: str):
+    """HBM bytes per step recorded from rocprofv3 counters for this workload,
+    if they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_step")
 
 
 class Replica:
+    """One independent copy of the workload's device inputs plus a prepared
+    step call."""
+
     def __init__(self, wl, part, layout):
         import torch
         import paged_kv_cache_434_amd as pkv
         from paged_kv_cache_434_amd import workloads as W
 
         d = W.to_device(wl, layout=layout)
-        self.d = d
-        self.cache = pkv.PagedCache(d["k_pool"], d["v_pool"], wl.kv_dtype)
-        self.slots = torch.empty(wl.B, dtype=torch.int32, device="cuda")
-        self.out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.bfloat16, device="cuda")
-        self.ws = pkv.alloc_workspace(wl.B, wl.Hq, wl.D, wl.max_blocks, part)
-        self.part = part
-        self.scale = float(wl.scale)
-
-
-def run_step(pkv, rep, ev=None):
-    """One decode step: append of the new token fused into the attention
-    launch (slot of position L-1 + cache write + attention), then the
-    cross-partition combine when the context is split."""
-    d = rep.d
-    if ev is not None:
-        ev[0].record()
-    pkv.decode_step(rep.cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"],
-                    rep.scale, partition_tokens=rep.part, workspace=rep.ws, out=rep.out)
-    if ev is not None:
-        ev[1].record()
+        cache = pkv.PagedCache(d["k_pool"], d["v_pool"], wl.kv_dtype)
+        if wl.quant:
+            # quantized once, before timing
+            NB, Hkv, bs, D = d["k_pool"].shape
+            qt = torch.int8 if wl.quant == "i8" else torch.uint8
+            ks = torch.empty((NB, Hkv), dtype=torch.float32, device="cuda")
+            vs = torch.empty_like(ks)
+            if layout == "blocks":
+                qcache = pkv.PagedCache.from_blocks(
+                    torch.empty((NB, 2, Hkv, bs, D), dtype=qt, device="cuda"), wl.quant, ks, vs)
+            else:
+                kq = torch.empty((NB, Hkv, bs, D), dtype=qt, device="cuda")
+                qcache = pkv.PagedCache(kq, torch.empty_like(kq), wl.quant, ks, vs)
+            pkv.quantize(cache, qcache)
+            for k in ("kv", "k_pool", "v_pool"):
+                d.pop(k, None)
+            cache = qcache
+        out_dtype = torch.float32 if wl.q_dtype == "f32" else torch.bfloat16
+        ws = pkv.alloc_workspace(wl.B, wl.Hq, wl.D, wl.max_blocks, part)
+        if wl.write:
+            self.call, self.out = pkv.prepare_decode_step(
+                cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"], float(wl.scale),
+                partition_tokens=part, workspace=ws, out_dtype=out_dtype)
+        else:
+            self.call, self.out = pkv.prepare_attention_decode(
+                cache, d["q"], d["tables"], d["lens"], float(wl.scale), partition_tokens=part,
+                workspace=ws, out_dtype=out_dtype)
+        self.d, self.cache = d, cache
 
 
 def cpu_baseline(wl, budget_s=10.0):
-    """The oracle (as it stands) timed on the host: cache write + decode of the
-    whole workload, repeated until about budget_s seconds have passed."""
-    import numpy as np
+    """The oracle (as it stands) timed on the host over the whole workload:
+    slot mapping + cache write + decode (or quantize once + decode for the
+    quantized workload), repeated until about budget_s seconds have passed."""
     import oracle
 
     k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    ks = vs = None
+    kvd = wl.kv_dtype
+    if wl.quant:
+        k, ks = oracle.quantize(k, wl.kv_dtype, wl.quant)
+        v, vs = oracle.quantize(v, wl.kv_dtype, wl.quant)
+        kvd = wl.quant
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        slots = oracle.slot_mapping(wl.tables, wl.lens)
-        oracle.cache_write(k, v, wl.kv_dtype, wl.k_new, wl.v_new, slots)
-        oracle.decode(wl.q, wl.q_dtype, k, v, wl.kv_dtype, wl.tables, wl.lens, wl.scale)
+        if wl.write:
+            slots = oracle.slot_mapping(wl.tables, wl.lens)
+            oracle.cache_write(k, v, wl.kv_dtype, wl.k_new, wl.v_new, slots)
+        oracle.decode(wl.q, wl.q_dtype, k, v, kvd, wl.tables, wl.lens, wl.scale,
+                      k_scale=ks, v_scale=vs)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s or len(times) >= 50:
             break
     return statistics.median(times), len(times), oracle.max_threads()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, five times: under rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE it gives the counters' reading for a known
+    number of bytes (1 GiB read and 1 GiB written per dispatch)."""
+    import torch
+
+    torch.cuda.set_device(0)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b) / 1e3)
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "ms": round(min(t) * 1e3, 4),
+                      "GBps_read_plus_write": round(2 * n / min(t) / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -109,7 +185,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--workload", type=int, default=2, choices=(1, 2, 3, 4, 5))
+    ap.add_argument("--quant", choices=("i8", "fp8"), default="i8",
+                    help="code type of the quantized-prefix workload (5)")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="input copies cycled through (0: enough for 1.3 GB of pools)")
     ap.add_argument("--partition", type=int, default=None,
                     help="split: tokens per partition, 0 for none, -1 for the balanced split "
                          "(default: the library's recommendation)")
@@ -117,48 +197,66 @@ def main():
                     help="pool layout: one [NB][2][Hkv][16][D] tensor (blocks) or two dense "
                          "[NB][Hkv][16][D] pools (split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU; runs on more than one GPU are not part of this "
               "library (the design notes describe how the path would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import paged_kv_cache_434_amd as pkv
     from paged_kv_cache_434_amd import workloads as W
 
     torch.cuda.set_device(0)
-    wl = W.make(2)
+    wl = W.make(args.workload, quant=args.quant if args.workload == 5 else None)
     part = args.partition if args.partition is not None else pkv.default_partition(
         wl.B, wl.Hkv, wl.max_blocks)
-    reps = [Replica(wl, part, args.layout) for _ in range(max(1, args.replicas))]
+    e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[wl.quant or wl.kv_dtype]
+    pool_bytes = wl.num_blocks * wl.Hkv * 16 * wl.D * 2 * e_kv
+    n_rep = args.replicas or max(2, min(8, math.ceil(1.3e9 / pool_bytes) + 1))
+    reps = [Replica(wl, part, args.layout) for _ in range(n_rep)]
     print(f"# workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
-          f"sum(L)={int(wl.lens.sum())} pool={wl.num_blocks} partition={part} "
-          f"replicas={len(reps)}", file=sys.stderr, flush=True)
+          f"sum(L)={int(wl.lens.sum())} pool={wl.num_blocks} quant={wl.quant} "
+          f"partition={part} layout={args.layout} replicas={len(reps)}",
+          file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
-        run_step(pkv, reps[i % len(reps)])
+        reps[i % len(reps)].call()
     torch.cuda.synchronize()
 
+    # wall time of K back-to-back steps
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        run_step(pkv, reps[i % len(reps)], evs[i])
+        reps[i % len(reps)].call()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_s = (t1 - t0) / K
-    step_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_s = statistics.mean(step_ms) / 1e3
+    step_s = (time.perf_counter() - t0) / K
+
+    # kernel time of each step: HIP events on the stream the kernels run on
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i in range(K):
+        evs[i][0].record(stream)
+        reps[i % len(reps)].call()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_s = statistics.mean(a.elapsed_time(b) for a, b in evs) / 1e3
 
     ab = algorithmic_bytes(wl)
     value = ab["step"] / step_s / 1e9
-    achieved = ab["step"] / attn_s / 1e9
+    achieved = ab["step"] / kern_s / 1e9
+    key = f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/{part}"
+    traffic = recorded_traffic(key)
+    e_q = {"f32": "f32", "bf16": "bf16"}[wl.q_dtype]
     line = {
-        "metric": "paged decode KV HBM GB/s (% of peak) + seq-steps/s, Llama-3-8B shape",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -168,33 +266,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": e_q if not wl.quant else f"{e_q}/{wl.quant}",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "num_q_heads": wl.Hq,
                    "num_kv_heads": wl.Hkv, "head_dim": wl.D, "block_size": 16,
-                   "context_lens": "uniform[512,4096]", "sum_context": int(wl.lens.sum()),
+                   "kv_dtype": wl.quant or wl.kv_dtype, "sum_context": int(wl.lens.sum()),
                    "pool_blocks": wl.num_blocks, "partition_tokens": part,
                    "split": "balanced" if part == pkv.SPLIT_BALANCED else "fixed",
-                   "layout": args.layout,
-                   "step": "decode step: slot of position L-1 + cache write + paged "
-                           "attention (one launch) + partition combine",
-                   "replicas": len(reps)},
+                   "layout": args.layout, "replicas": len(reps),
+                   "step": ("decode step: slot of position L-1 + cache write + paged attention "
+                            "(one launch) + partition combine") if wl.write else
+                           "paged attention over a quantized pool + partition combine"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(wl.B / step_s, 1),
-        "gpu_step_ms": round(attn_s * 1e3, 4),
+        "kernel_ms_per_step": round(kern_s * 1e3, 4),
+        "bytes_per_step": ab["step"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "decode step call (fused append + attention, combine)",
+                     "traffic": traffic,
+                     "kernel": "the step's kernels (decode attention, then the combine)",
                      "bytes_per_launch": ab["step"]},
     }
     if not args.no_cpu_baseline:
-        med, reps_done, threads = cpu_baseline(wl)
-        line["cpu_baseline"] = {"value": round(ab["step"] / med / 1e9, 3), "unit": "GB/s",
-                                "cores": threads, "kind": "oracle",
-                                "sample": f"whole workload (slot mapping + cache write + decode "
-                                          f"of all {wl.B} sequences), median of {reps_done} "
-                                          f"runs, {med:.2f} s each"}
+        med, runs, threads = cpu_baseline(wl)
+        line["cpu_baseline"] = {
+            "value": round(ab["step"] / med / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the whole workload ({wl.B} sequences, {int(wl.lens.sum())} context "
+                       f"tokens) per run, median of {runs} runs of {med:.3f} s; "
+                       f"{wl.B / med:.1f} seq-steps/s")}
     print(json.dumps(line), flush=True)
 
 

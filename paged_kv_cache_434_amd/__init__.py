@@ -231,10 +231,10 @@ def alloc_workspace(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, partiti
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: float,
-                     partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
-                     stream=None, _append=None):
-    """out[s][h] = softmax(scale q k^T) v over each sequence's paged context."""
+def _decode_call(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                 partition_tokens: int, workspace, out, out_dtype, stream, append):
+    """Checks and marshals one decode call; returns (name, function, args, out,
+    workspace) so the call can be made now or kept and repeated."""
     torch = _torch()
     qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
     if qd is None:
@@ -245,6 +245,14 @@ def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: fl
     B, Hq, D = q.shape
     if context_lens.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("q, block_tables and context_lens disagree on the batch size")
+    if append is not None:
+        sd = _storage_dtype(cache.kv_dtype)
+        k_new, v_new = append
+        _need(k_new, "k_new", sd, 3)
+        _need(v_new, "v_new", sd, 3)
+        if (tuple(k_new.shape) != (B, cache.num_kv_heads, cache.head_dim)
+                or k_new.shape != v_new.shape):
+            raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
     od = out_dtype or (out.dtype if out is not None else q.dtype)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=od, device=q.device)
@@ -258,14 +266,23 @@ def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: fl
     common = (_ptr(block_tables), maxb, _ptr(context_lens), B, Hq, ctypes.c_float(scale),
               partition_tokens, _ptr(workspace), ws_bytes, _ptr(out), DTYPE_CODES[odn],
               _stream(stream))
-    if _append is None:
-        _check("pkv_attention_decode",
-               _load().pkv_attention_decode(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd],
-                                            *common))
-    else:
-        _check("pkv_decode_step",
-               _load().pkv_decode_step(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd],
-                                       _ptr(_append[0]), _ptr(_append[1]), *common))
+    lib = _load()
+    if append is None:
+        return ("pkv_attention_decode", lib.pkv_attention_decode,
+                (ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd]) + common, out, workspace)
+    return ("pkv_decode_step", lib.pkv_decode_step,
+            (ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd], _ptr(append[0]),
+             _ptr(append[1])) + common, out, workspace)
+
+
+def attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                     partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
+                     stream=None):
+    """out[s][h] = softmax(scale q k^T) v over each sequence's paged context."""
+    name, fn, args, out, _ = _decode_call(cache, q, block_tables, context_lens, scale,
+                                          partition_tokens, workspace, out, out_dtype, stream,
+                                          None)
+    _check(name, fn(*args))
     return out
 
 
@@ -274,15 +291,48 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, 
                 stream=None):
     """Append each sequence's new token at position context_lens - 1, then
     attention over the whole context (one attention launch)."""
-    torch = _torch()
-    sd = _storage_dtype(cache.kv_dtype)
-    _need(k_new, "k_new", sd, 3)
-    _need(v_new, "v_new", sd, 3)
-    B = q.shape[0]
-    if tuple(k_new.shape) != (B, cache.num_kv_heads, cache.head_dim) or k_new.shape != v_new.shape:
-        raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
-    return attention_decode(cache, q, block_tables, context_lens, scale, partition_tokens,
-                            workspace, out, out_dtype, stream, _append=(k_new, v_new))
+    name, fn, args, out, _ = _decode_call(cache, q, block_tables, context_lens, scale,
+                                          partition_tokens, workspace, out, out_dtype, stream,
+                                          (k_new, v_new))
+    _check(name, fn(*args))
+    return out
+
+
+class PreparedCall:
+    """A decode call whose arguments were checked and marshalled once; calling
+    it launches the same work again on the same stream with the tensors given
+    at preparation (which it keeps alive).  For loops that repeat one call
+    shape: the per-call host cost is one foreign-function call."""
+
+    def __init__(self, name, fn, args, keep):
+        self.name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != PKV_OK:
+            raise PkvError(self.name, status)
+
+
+def prepare_decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens,
+                        scale: float, partition_tokens: int = 0, workspace=None, out=None,
+                        out_dtype=None, stream=None):
+    """decode_step, prepared: returns (PreparedCall, out)."""
+    name, fn, args, out, ws = _decode_call(cache, q, block_tables, context_lens, scale,
+                                           partition_tokens, workspace, out, out_dtype, stream,
+                                           (k_new, v_new))
+    keep = (cache, q, k_new, v_new, block_tables, context_lens, ws, out)
+    return PreparedCall(name, fn, args, keep), out
+
+
+def prepare_attention_decode(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                             partition_tokens: int = 0, workspace=None, out=None,
+                             out_dtype=None, stream=None):
+    """attention_decode, prepared: returns (PreparedCall, out)."""
+    name, fn, args, out, ws = _decode_call(cache, q, block_tables, context_lens, scale,
+                                           partition_tokens, workspace, out, out_dtype, stream,
+                                           None)
+    keep = (cache, q, block_tables, context_lens, ws, out)
+    return PreparedCall(name, fn, args, keep), out
 
 
 def quantize(src: PagedCache, dst: PagedCache, block_ids=None, stream=None):
