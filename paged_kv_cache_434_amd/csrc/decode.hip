@@ -740,6 +740,16 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   const int cnt = counts != nullptr ? counts[s] : 0;
   const float m0 = lane < kstride ? mrow[lane] : -INFINITY;
   const float l0 = lane < kstride ? lrow[lane] : 0.f;
+  // the first kSpec partial rows (most sequences have no more pieces), read
+  // before the count is known through a descriptor bounded to the row's slots
+  constexpr int kSpec = 8;
+  constexpr int kSpecLoads = kSpec / kRowsPerLoad;
+  const int sub0 = lane / kCols, col0 = lane % kCols;
+  const rsrc_t rspec = make_rsrc(ws_o + (size_t)row * kstride * D, kstride * D * 4);
+  u32x4 spec[kSpecLoads];
+#pragma unroll
+  for (int i = 0; i < kSpecLoads; ++i)
+    spec[i] = buffer_load16(rspec, ((i * kRowsPerLoad + sub0) * D + col0 * 4) * 4);
   if (L < 0 || L > max_blocks * kBlock) L = 0;
   if (L == 0) return;
   int parts;
@@ -764,8 +774,20 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
       wp = c == 0 ? exp2f(m0 - M) * l0 : exp2f(mrow[c + lane] - M) * lrow[c + lane];
     den += wp;
     const int n64 = min(kWave, parts - c);
+    int q0 = 0;
+    if (c == 0) {
+      // partial rows already loaded; rows past the count are stale memory
+      // (possibly NaN bits), so they are left out by selection
+#pragma unroll
+      for (int i = 0; i < kSpecLoads; ++i) {
+        const int pp = i * kRowsPerLoad + sub;
+        const float w = __shfl(wp, pp, kWave);
+        if (pp < parts) a += w * __builtin_bit_cast(f32x4, spec[i]);
+      }
+      q0 = kSpec;
+    }
 #pragma unroll 4
-    for (int q = 0; q < n64; q += kRowsPerLoad) {
+    for (int q = q0; q < n64; q += kRowsPerLoad) {
       const int pp = q + sub;              // partial within this group of 64
       const float w = __shfl(wp, pp & (kWave - 1), kWave);
       const u32x4 v = buffer_load16(ro, ((c + pp) * D + col * 4) * 4);
