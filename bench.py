@@ -25,6 +25,7 @@ host, timed on the same workload.
     python bench.py                     # headline: Llama-3-8B shape
     python bench.py --workload 3        # other workloads (1..5; 5 takes --quant)
     python bench.py --copy-calibration  # plain 1 GiB device copy, for counter scaling
+    python bench.py --op quantize       # pkv_quantize / pkv_copy_blocks bandwidth
 """
 from __future__ import annotations
 
@@ -180,6 +181,63 @@ def copy_calibration():
                       "GBps_read_plus_write": round(2 * n / min(t) / 1e9, 1)}), flush=True)
 
 
+def op_bench(args):
+    """Bandwidth of the operations outside the decode step, on the workload's
+    pool: pkv_quantize of the whole pool (bf16 source -> 8-bit codes + scales)
+    and pkv_copy_blocks of half the pool's blocks into the other half.  One
+    JSON line; bytes are what the operation must read and write."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_434_amd as pkv
+    from paged_kv_cache_434_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    wl = W.make(args.workload)
+    d = W.to_device(wl, layout=args.layout)
+    cache = pkv.PagedCache(d["k_pool"], d["v_pool"], wl.kv_dtype)
+    NB, Hkv, bs, D = d["k_pool"].shape
+    e = {"f32": 4, "bf16": 2}[wl.kv_dtype]
+    if args.op == "quantize":
+        qt = torch.int8 if args.quant == "i8" else torch.uint8
+        ks = torch.empty((NB, Hkv), dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        dst = pkv.PagedCache.from_blocks(
+            torch.empty((NB, 2, Hkv, bs, D), dtype=qt, device="cuda"), args.quant, ks, vs)
+        fn = lambda: pkv.quantize(cache, dst)
+        nbytes = 2 * NB * Hkv * bs * D * (e + 1) + 2 * NB * Hkv * 4
+        what = f"pkv_quantize {wl.kv_dtype}->{args.quant}, all {NB} blocks"
+    else:
+        rng = np.random.default_rng(0)
+        ids = rng.permutation(NB).astype(np.int32)
+        n = NB // 2
+        pairs = torch.from_numpy(np.stack([ids[:n], ids[n:2 * n]], 1)).cuda()
+        fn = lambda: pkv.copy_blocks(cache, pairs)
+        nbytes = 2 * 2 * n * Hkv * bs * D * e
+        what = f"pkv_copy_blocks, {n} block pairs"
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = statistics.mean(a.elapsed_time(b) for a, b in evs) / 1e3
+    gbs = nbytes / t / 1e9
+    print(json.dumps({"metric": f"{args.op} HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
+                      "dtype": wl.kv_dtype, "data": "synthetic",
+                      "config": {"workload": wl.name, "op": what, "layout": args.layout},
+                      "bytes_per_launch": nbytes,
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +256,8 @@ def main():
                          "[NB][Hkv][16][D] pools (split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--op", choices=("step", "quantize", "copy_blocks"), default="step",
+                    help="what to time: the decode step (default) or another operation")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -206,6 +266,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op != "step":
+        op_bench(args)
         return
 
     import torch

@@ -215,6 +215,19 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
 int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,
                  int32_t n_ids, void* stream);
 
+/* Block copy for copy-on-write ([CSDN] section 二 "写时复制": branches of a
+ * beam search or of parallel sampling share their history blocks and a block
+ * is copied only when a new token is written into it; [KVC] "意外的收获：prefix
+ * sharing": shared blocks are reference-counted and copied on write).  For
+ * each i < n with (src, dst) = (pairs[2i], pairs[2i+1]): every KV head's K and
+ * V tile of block dst becomes a bit-exact copy of block src's, and for 8-bit
+ * pools k_scale / v_scale rows too.
+ *   pairs: device int32 [n][2]; a pair with an id outside [0, num_blocks) is
+ *     skipped.  Destinations must be distinct and no destination may also be
+ *     a source (the result would depend on the order of the copies).
+ * The caller updates its block tables; the library keeps no reference counts. */
+int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t n, void* stream);
+
 /* Gather (diagnostic): copies each sequence's K and V, in logical order, into
  * contiguous rows k_out[cu_seqlens[s] + t][g][:] for t < context_lens[s].
  * Bit-exact copy of the stored elements (codes for 8-bit pools).

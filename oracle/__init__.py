@@ -63,6 +63,8 @@ def _load():
         lib.orc_slot_mapping.argtypes = [P, I, P, I, I, P]
         lib.orc_cache_write.restype = None
         lib.orc_cache_write.argtypes = [P, P, I, I, I, I, I, P, P, P, I]
+        lib.orc_copy_blocks.restype = None
+        lib.orc_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, P, I]
         lib.orc_gather.restype = None
         lib.orc_gather.argtypes = [P, P, I, I, I, I, P, I, P, P, I, P, P]
         lib.orc_decode.restype = I
@@ -139,6 +141,19 @@ def cache_write(k_cache, v_cache, dtype, k_new, v_new, slot_mapping):
     sm = _c(slot_mapping, np.int32)
     _load().orc_cache_write(_ptr(k_cache), _ptr(v_cache), DTYPES[dtype], NB, Hkv, bs, D,
                             _ptr(kn), _ptr(vn), _ptr(sm), sm.shape[0])
+
+
+def copy_blocks(k_cache, v_cache, dtype, pairs, k_scale=None, v_scale=None):
+    """In-place copy-on-write block copies (page on KV cache / PagedAttention,
+    section 二, and the vLLM deep-dive page, "prefix sharing"): pairs [n][2] of
+    (src, dst) physical block ids, applied in order."""
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    NB, Hkv, bs, D = k_cache.shape
+    pr = _c(pairs, np.int32).reshape(-1, 2)
+    for sc in (k_scale, v_scale):
+        assert sc is None or (sc.dtype == np.float32 and sc.flags.c_contiguous)
+    _load().orc_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                            DTYPES[dtype], NB, Hkv, bs, D, _ptr(pr), pr.shape[0])
 
 
 def gather(k_cache, v_cache, dtype, block_tables, context_lens):

@@ -206,6 +206,29 @@ void orc_cache_write(void* k_cache, void* v_cache, int dtype, int num_blocks, in
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block copy for copy-on-write ([CSDN] section 二 "写时复制"; [KVC]
+ * "意外的收获：prefix sharing"): a branch that shares a block with another and
+ * is about to write into it first gets its own copy.  Pair i copies every
+ * element of physical block src = pairs[2i] (all KV heads, K and V) into
+ * block dst = pairs[2i+1], and the per-(block, head) scales when given.
+ * Pairs are applied in order; ids outside [0, num_blocks) are skipped.       */
+void orc_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int dtype,
+                     int num_blocks, int Hkv, int bs, int D, const int32_t* pairs, int n) {
+  size_t eb = orc_elem_bytes(dtype);
+  size_t blk = (size_t)Hkv * bs * D * eb;
+  for (int i = 0; i < n; ++i) {
+    int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
+    memmove((char*)k_cache + (size_t)dst * blk, (const char*)k_cache + (size_t)src * blk, blk);
+    memmove((char*)v_cache + (size_t)dst * blk, (const char*)v_cache + (size_t)src * blk, blk);
+    for (int g = 0; g < Hkv; ++g) {
+      if (k_scale) k_scale[(size_t)dst * Hkv + g] = k_scale[(size_t)src * Hkv + g];
+      if (v_scale) v_scale[(size_t)dst * Hkv + g] = v_scale[(size_t)src * Hkv + g];
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Gather: copy each sequence's K and V into logical order, giving the
  * contiguous layout the paging replaces ([KVC] "预分配的困境").  Output rows
  * are [cu_seqlens[s] + t][g][:].                                            */

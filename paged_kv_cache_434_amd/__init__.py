@@ -69,6 +69,7 @@ def _load():
                                                ctypes.c_size_t, P, I32, P]),
             "pkv_quantize": (ctypes.c_int, [C, C, P, I32, P]),
             "pkv_gather": (ctypes.c_int, [C, P, I32, P, P, I32, P, P, P]),
+            "pkv_copy_blocks": (ctypes.c_int, [C, P, I32, P]),
             "pkv_validate_tables": (ctypes.c_int, [P, I32, P, I32, I32,
                                                    ctypes.POINTER(I32), P]),
         }
@@ -88,7 +89,7 @@ def lib():
 EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_mapping",
                     "pkv_cache_write", "pkv_decode_workspace_bytes",
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
-                    "pkv_quantize",
+                    "pkv_quantize", "pkv_copy_blocks",
                     "pkv_gather", "pkv_validate_tables")
 
 
@@ -344,6 +345,17 @@ def quantize(src: PagedCache, dst: PagedCache, block_ids=None, stream=None):
     _check("pkv_quantize",
            _load().pkv_quantize(ctypes.byref(src.desc), ctypes.byref(dst.desc), _ptr(block_ids),
                                 n, _stream(stream)))
+
+
+def copy_blocks(cache: PagedCache, pairs, stream=None):
+    """Copy-on-write block copies: pairs is int32 [n][2] of (src, dst) block ids."""
+    torch = _torch()
+    _need(pairs, "pairs", torch.int32, 2)
+    if pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    _check("pkv_copy_blocks",
+           _load().pkv_copy_blocks(ctypes.byref(cache.desc), _ptr(pairs), pairs.shape[0],
+                                   _stream(stream)))
 
 
 def gather(cache: PagedCache, block_tables, context_lens, cu_seqlens, total_tokens: int,

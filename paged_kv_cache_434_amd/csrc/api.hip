@@ -186,6 +186,17 @@ int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* 
   return launch_quantize(*src, *dst, block_ids, n_ids, static_cast<hipStream_t>(stream));
 }
 
+int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t n, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  if (n < 0 || n > 65535 * 1024) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!pairs) return PKV_ERR_NULL;
+  if (block_elems(*cache) * (int64_t)elem_bytes(cache->kv_dtype) / 16 > (int64_t)INT_MAX)
+    return PKV_ERR_SHAPE;
+  return launch_copy_blocks(*cache, pairs, n, static_cast<hipStream_t>(stream));
+}
+
 int pkv_gather(const pkv_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                const int32_t* context_lens, const int32_t* cu_seqlens, int32_t num_seqs,
                void* k_out, void* v_out, void* stream) {

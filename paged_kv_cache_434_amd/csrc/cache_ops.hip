@@ -78,7 +78,37 @@ __global__ void gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __r
   }
 }
 
+// Copy-on-write block copy: one workgroup per (pair, K or V); the block's
+// every-head region (blk_bytes) is moved in 16-byte pieces, consecutive
+// threads on consecutive addresses; the K workgroup also copies the K scales
+// and the V workgroup the V scales of 8-bit pools.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
+    float* __restrict__ vs, const int32_t* __restrict__ pairs, int num_blocks, int hkv,
+    size_t stride_bytes, int blk_chunks) {
+  const int i = blockIdx.x;
+  const bool is_v = blockIdx.y != 0;
+  const int src = pairs[2 * i], dst = pairs[2 * i + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint8_t* base = is_v ? vc : kc;
+  const uint4* from = reinterpret_cast<const uint4*>(base + (size_t)src * stride_bytes);
+  uint4* to = reinterpret_cast<uint4*>(base + (size_t)dst * stride_bytes);
+  for (int c = threadIdx.x; c < blk_chunks; c += blockDim.x) to[c] = from[c];
+  float* sc = is_v ? vs : ks;
+  if (sc != nullptr && (int)threadIdx.x < hkv)
+    sc[(size_t)dst * hkv + threadIdx.x] = sc[(size_t)src * hkv + threadIdx.x];
+}
+
 }  // namespace
+
+int launch_copy_blocks(const pkv_cache_t& c, const int32_t* pairs, int n, hipStream_t st) {
+  const bool q8 = c.kv_dtype == PKV_I8 || c.kv_dtype == PKV_FP8_E4M3;
+  const int chunks = (int)(block_elems(c) * (int64_t)elem_bytes(c.kv_dtype) / 16);
+  dim3 grid((unsigned)n, 2), block(256);
+  return launch(copy_blocks_kernel, grid, block, st, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache,
+                q8 ? c.k_scale : nullptr, q8 ? c.v_scale : nullptr, pairs, c.num_blocks,
+                c.num_kv_heads, block_stride_bytes(c), chunks);
+}
 
 int launch_slot_mapping(const int32_t* tables, int max_blocks, const int32_t* lens, int n,
                         int32_t* slots, hipStream_t st) {

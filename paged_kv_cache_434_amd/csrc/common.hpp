@@ -84,6 +84,7 @@ int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const
 int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
                   const int32_t* lens, const int32_t* cu, int num_seqs, void* ko, void* vo,
                   hipStream_t st);
+int launch_copy_blocks(const pkv_cache_t& c, const int32_t* pairs, int n, hipStream_t st);
 int launch_quantize(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n_ids,
                     hipStream_t st);
 

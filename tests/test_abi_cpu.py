@@ -154,3 +154,22 @@ def test_gather_and_slots_reject_bad_arguments():
     assert lib.pkv_validate_tables(FAKE, 4, FAKE, 0, 8, ctypes.byref(bad), None) == 0
     assert bad.value == -1
     assert lib.pkv_validate_tables(None, 4, FAKE, 2, 8, ctypes.byref(bad), None) == 1
+
+
+def test_copy_blocks_rejects_bad_arguments():
+    lib = pkv.lib()
+    c = _cache()
+    assert lib.pkv_copy_blocks(ctypes.byref(c), None, 0, None) == 0     # nothing to do
+    assert lib.pkv_copy_blocks(ctypes.byref(c), None, 3, None) == 1     # NULL pairs
+    assert lib.pkv_copy_blocks(ctypes.byref(c), FAKE, -1, None) == 2
+    assert lib.pkv_copy_blocks(None, FAKE, 3, None) == 1
+    bad = _cache(kv_dtype=2)                                          # 8-bit without scales
+    assert lib.pkv_copy_blocks(ctypes.byref(bad), FAKE, 3, None) == 1
+
+
+def test_block_stride_validation():
+    lib = pkv.lib()
+    small = _cache(block_stride=2 * 16 * 128 - 8)      # smaller than one block of every head
+    assert lib.pkv_copy_blocks(ctypes.byref(small), FAKE, 1, None) == 2
+    odd = _cache(block_stride=2 * 2 * 16 * 128 + 3)    # not a multiple of 16 bytes
+    assert lib.pkv_copy_blocks(ctypes.byref(odd), FAKE, 1, None) == 6

@@ -532,3 +532,103 @@ def test_blocks_layout_decode_step_full_size(cfg, part):
     ref, _ = _oracle_step(wl)
     err = _cmp(_out_np(out), ref, TOL[wl.kv_dtype], "bf16", wl.name)
     _say(f"  max abs err {err:.3e}")
+
+
+# ------------------------------------------------------------- copy on write
+
+
+def _cow_pairs(rng, NB, n):
+    ids = rng.permutation(NB)
+    return np.stack([ids[:n], ids[n:2 * n]], axis=1).astype(np.int32)   # dst never a src
+
+
+@pytest.mark.parametrize("layout", ["split", "blocks"])
+@pytest.mark.parametrize("cfg,over", [(1, {}), (2, dict(B=8, lo=1, hi=600, pool=300))])
+def test_copy_blocks_bit_exact(cfg, over, layout):
+    wl = W.make(cfg, **over)
+    _say(f"copy blocks: {wl.name} layout={layout}")
+    d = W.to_device(wl, layout=layout)
+    rng = np.random.default_rng(11)
+    pairs = _cow_pairs(rng, wl.num_blocks, min(40, wl.num_blocks // 2))
+    pairs[3] = [wl.num_blocks + 5, pairs[3, 1]]          # out of range: skipped
+    pkv.copy_blocks(_dev_cache(d, wl), torch.from_numpy(pairs).cuda())
+    k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    oracle.copy_blocks(k, v, wl.kv_dtype, pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.from_device(d["k_pool"]), k)
+    assert np.array_equal(W.from_device(d["v_pool"]), v)
+
+
+@pytest.mark.parametrize("quant", ["i8", "fp8"])
+def test_copy_blocks_quantized_with_scales(quant):
+    wl = W.make(5, B=6, prefix=64, suffix_hi=40)
+    d = W.to_device(wl, layout="blocks")
+    NB = wl.num_blocks
+    qt = torch.int8 if quant == "i8" else torch.uint8
+    ks = torch.empty((NB, wl.Hkv), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    kv = torch.empty((NB, 2, wl.Hkv, 16, wl.D), dtype=qt, device="cuda")
+    qc = pkv.PagedCache.from_blocks(kv, quant, ks, vs)
+    pkv.quantize(_dev_cache(d, wl), qc)
+    kc, kss = oracle.quantize(wl.k_pool, "bf16", quant)
+    vc, vss = oracle.quantize(wl.v_pool, "bf16", quant)
+    pairs = _cow_pairs(np.random.default_rng(12), NB, NB // 3)
+    pkv.copy_blocks(qc, torch.from_numpy(pairs).cuda())
+    oracle.copy_blocks(kc, vc, quant, pairs, kss, vss)
+    torch.cuda.synchronize()
+    got = kv.cpu().numpy()
+    assert np.array_equal(got[:, 0], kc) and np.array_equal(got[:, 1], vc)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), kss.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vss.view(np.uint32))
+
+
+@pytest.mark.parametrize("part", [0, -1])
+def test_copy_on_write_branch_append(part):
+    """Beam branches share all blocks; half of them append a token: their
+    shared last block is copied first, their tables re-pointed, then the fused
+    decode step writes the token and attends.  Branches that did not append
+    keep their exact earlier output; every output matches the oracle."""
+    rng = np.random.default_rng(13)
+    base = W.make(2, B=1, lens=[700], hi=800, pool=200)
+    nb = -(-700 // 16)
+    nbr = 8                                               # branches
+    tables = np.repeat(base.tables[:1], nbr, axis=0)
+    lens = np.full(nbr, 700, dtype=np.int32)
+    free = np.setdiff1d(np.arange(base.num_blocks), base.tables[0, :nb])
+    app = np.arange(0, nbr, 2)                            # branches that append
+    pairs = np.stack([np.full(len(app), base.tables[0, nb - 1]), free[:len(app)]], 1)
+    pairs = pairs.astype(np.int32)
+    q = W.to_bf16_bits(rng.standard_normal((nbr, base.Hq, base.D)).astype(np.float32))
+    wl = W.Workload(**{**base.__dict__, "B": nbr, "tables": tables.copy(), "lens": lens.copy(),
+                       "q": q, "k_new": None, "v_new": None})
+    d = W.to_device(wl, layout="blocks")
+    cache = _dev_cache(d, wl)
+    before = pkv.attention_decode(cache, d["q"], d["tables"], d["lens"], float(wl.scale),
+                                  partition_tokens=part, out_dtype=torch.float32).clone()
+    # copy on write, re-point, then one fused step for the appending branches
+    pkv.copy_blocks(cache, torch.from_numpy(pairs).cuda())
+    t2, l2 = tables.copy(), lens.copy()
+    t2[app, nb - 1] = pairs[:, 1]
+    l2[app] += 1                                          # 701: still inside block nb-1
+    kn = W.to_bf16_bits(rng.standard_normal((len(app), wl.Hkv, wl.D)).astype(np.float32))
+    vn = W.to_bf16_bits(rng.standard_normal((len(app), wl.Hkv, wl.D)).astype(np.float32))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    out_app = pkv.decode_step(cache, d["q"][app], dev(kn), dev(vn),
+                              torch.from_numpy(t2[app]).cuda(), torch.from_numpy(l2[app]).cuda(),
+                              float(wl.scale), partition_tokens=part, out_dtype=torch.float32)
+    after = pkv.attention_decode(cache, d["q"], torch.from_numpy(t2).cuda(),
+                                 torch.from_numpy(l2).cuda(), float(wl.scale),
+                                 partition_tokens=part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    keep = np.setdiff1d(np.arange(nbr), app)
+    assert torch.equal(after[keep], before[keep])
+    if part == 0:   # no split: a row's result does not depend on the rest of the batch
+        assert torch.equal(after[app], out_app)
+    # oracle: the same sequence of operations on the host
+    k, v = wl.k_pool.copy(), wl.v_pool.copy()
+    oracle.copy_blocks(k, v, "bf16", pairs)
+    oracle.cache_write(k, v, "bf16", kn, vn, oracle.slot_mapping(t2[app], l2[app]))
+    ref = oracle.decode(q, "bf16", k, v, "bf16", t2, l2, wl.scale)
+    _cmp(_out_np(after), ref, TOL["bf16"], "f32", "copy-on-write branches")
+    _cmp(_out_np(out_app), ref[app], TOL["bf16"], "f32", "copy-on-write fused step")
