@@ -71,6 +71,10 @@ def _load():
         lib.orc_decode.argtypes = [P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, F, P]
         lib.orc_decode_rows.restype = I
         lib.orc_decode_rows.argtypes = [P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, F, P, I, P]
+        lib.orc_decode_multi.restype = I
+        lib.orc_decode_multi.argtypes = [P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, I, F, P]
+        lib.orc_slot_mapping_tokens.restype = None
+        lib.orc_slot_mapping_tokens.argtypes = [P, I, P, I, I, I, P]
         lib.orc_decode_partials.restype = I
         lib.orc_decode_partials.argtypes = [P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, F, I, I,
                                             P, P, P]
@@ -198,6 +202,38 @@ def decode(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens, s
                             bs, float(np.float32(scale)), _ptr(out))
     if rc != 0:
         raise MemoryError("oracle decode: allocation failed")
+    return out
+
+
+def decode_multi(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens, scale,
+                 k_scale=None, v_scale=None) -> np.ndarray:
+    """Several query tokens per sequence, each attending to the context up to
+    and including its own position (vLLM deep-dive page, "投机解码"); q is
+    [B][ntok][Hq][D]; float64 output of the same shape."""
+    qa = _c(q, NP_STORAGE[q_dtype])
+    B, ntok, Hq, D = qa.shape
+    _, kc, vc, ks, vs, bt, lens = _decode_args(qa.reshape(B * ntok, Hq, D), q_dtype, k_cache,
+                                               v_cache, kv_dtype, k_scale, v_scale, block_tables,
+                                               context_lens)
+    NB, Hkv, bs, D2 = kc.shape
+    assert D == D2 and Hq % Hkv == 0 and lens.shape[0] == B
+    out = np.zeros((B, ntok, Hq, D), dtype=np.float64)
+    rc = _load().orc_decode_multi(_ptr(qa), DTYPES[q_dtype], _ptr(kc), _ptr(vc), DTYPES[kv_dtype],
+                                  _ptr(ks), _ptr(vs), _ptr(bt), bt.shape[1], _ptr(lens), B, ntok,
+                                  Hq, Hkv, D, bs, float(np.float32(scale)), _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle decode_multi: allocation failed")
+    return out
+
+
+def slot_mapping_tokens(block_tables, context_lens, ntok, block_size=16) -> np.ndarray:
+    """Slots of the last ntok positions of every sequence ([B][ntok], -1 for
+    negative positions)."""
+    bt = _c(block_tables, np.int32)
+    lens = _c(context_lens, np.int32)
+    out = np.empty((lens.shape[0], ntok), dtype=np.int32)
+    _load().orc_slot_mapping_tokens(_ptr(bt), bt.shape[1], _ptr(lens), lens.shape[0], ntok,
+                                    block_size, _ptr(out))
     return out
 
 

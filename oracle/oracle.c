@@ -259,13 +259,13 @@ static void orc_attend_range(const void* q, int q_dtype, const void* k_cache,
                              const void* v_cache, int kv_dtype, const float* k_scale,
                              const float* v_scale, const int32_t* block_tables, int max_blocks,
                              int s, int h, int Hq, int Hkv, int D, int bs, double scale, int t0,
-                             int t1, double* logits, double* m_out, double* l_out,
+                             int t1, size_t qrow, double* logits, double* m_out, double* l_out,
                              double* o_out) {
   /* [KVC] "MQA 与 GQA": Hq/Hkv query heads share one KV head; head h reads
-   * KV head h / (Hq/Hkv) (contiguous groups).                               */
+   * KV head h / (Hq/Hkv) (contiguous groups).  qrow: element offset of the
+   * query row in q.                                                          */
   int G = Hq / Hkv;
   int g = h / G;
-  const size_t qrow = ((size_t)s * Hq + h) * (size_t)D;
   double m = -INFINITY, l = 0.0;
   for (int d = 0; d < D; ++d) o_out[d] = 0.0;
   if (t1 <= t0) {
@@ -327,7 +327,7 @@ int orc_decode(const void* q, int q_dtype, const void* k_cache, const void* v_ca
         double m, l;
         orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
                          max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, context_lens[s],
-                         logits, &m, &l, out + (size_t)r * D);
+                         ((size_t)s * Hq + h) * (size_t)D, logits, &m, &l, out + (size_t)r * D);
       }
       free(logits);
     }
@@ -356,12 +356,63 @@ int orc_decode_rows(const void* q, int q_dtype, const void* k_cache, const void*
         double m, l;
         orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
                          max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, context_lens[s],
-                         logits, &m, &l, out + (size_t)i * D);
+                         ((size_t)s * Hq + h) * (size_t)D, logits, &m, &l, out + (size_t)i * D);
       }
       free(logits);
     }
   }
   return fail ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Several query tokens per sequence ([KVC] "投机解码": the large model checks
+ * k drafted tokens in one forward pass; "Continuous Batching": long prompts
+ * are fed in chunks).  Sequence s has L = context_lens[s] tokens, the last
+ * ntok of which are its query tokens: query token i (0 <= i < ntok) sits at
+ * position p = L - ntok + i and attends to the tokens t <= p, so each query
+ * sees the context before it and itself, never a later token.  q and out are
+ * [num_seqs][ntok][Hq][D]; a query token with p < 0 gets a zero row.         */
+int orc_decode_multi(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                     int kv_dtype, const float* k_scale, const float* v_scale,
+                     const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                     int num_seqs, int ntok, int Hq, int Hkv, int D, int bs, float scale,
+                     double* out) {
+  int max_len = 0, fail = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (context_lens[s] > max_len) max_len = context_lens[s];
+#pragma omp parallel reduction(| : fail)
+  {
+    double* logits = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!logits) {
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long r = 0; r < (long)num_seqs * ntok * Hq; ++r) {
+        int s = (int)(r / ((long)ntok * Hq));
+        int i = (int)((r / Hq) % ntok), h = (int)(r % Hq);
+        int p = context_lens[s] - ntok + i;
+        double m, l;
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+                         max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, p + 1 > 0 ? p + 1 : 0,
+                         (size_t)r * D, logits, &m, &l, out + (size_t)r * D);
+      }
+      free(logits);
+    }
+  }
+  return fail ? -1 : 0;
+}
+
+/* Slots of the last ntok positions of every sequence: slots[s][i] is the slot
+ * of position L - ntok + i ([MGMT] 二, append_slot), or -1 when that position
+ * is negative.                                                               */
+void orc_slot_mapping_tokens(const int32_t* block_tables, int max_blocks,
+                             const int32_t* context_lens, int num_seqs, int ntok, int bs,
+                             int32_t* slots) {
+  for (int s = 0; s < num_seqs; ++s)
+    for (int i = 0; i < ntok; ++i) {
+      int p = context_lens[s] - ntok + i;
+      slots[(size_t)s * ntok + i] = p >= 0 ? orc_slot_of(block_tables, max_blocks, s, p, bs) : -1;
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -392,7 +443,8 @@ int orc_decode_partials(const void* q, int q_dtype, const void* k_cache, const v
           size_t i = (size_t)r * n_parts + p;
           orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                            block_tables, max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, t0,
-                           t1, logits, &m_out[i], &l_out[i], o_out + i * D);
+                           t1, ((size_t)s * Hq + h) * (size_t)D, logits, &m_out[i], &l_out[i],
+                           o_out + i * D);
         }
       }
       free(logits);
