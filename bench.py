@@ -48,7 +48,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("paged_kv_cache_434_amd/csrc/decode.hip", "paged_kv_cache_434_amd/csrc/common.hpp")
 
 
-def algorithmic_bytes(wl):
+def algorithmic_bytes(wl, ntok=1):
     """Bytes the method must move for one step: K/V of every context token,
     the used block-table entries, 8-bit scales, q in and out, lengths, and for
     workloads with a new token its K/V row read and written plus its slot."""
@@ -61,10 +61,10 @@ def algorithmic_bytes(wl):
     kv = int(L.sum()) * wl.Hkv * wl.D * 2 * e_kv
     tables = int(nblk.sum()) * 4
     scales = int(nblk.sum()) * wl.Hkv * 2 * 4 if wl.quant else 0
-    q_out = wl.B * wl.Hq * wl.D * 2 * e_q
+    q_out = wl.B * ntok * wl.Hq * wl.D * 2 * e_q
     lens = wl.B * 4
     attention = kv + tables + scales + q_out + lens
-    write = (wl.B * wl.Hkv * wl.D * 2 * e_kv * 2) if wl.write else 0
+    write = (wl.B * wl.Hkv * wl.D * 2 * e_kv * 2) if wl.write and ntok == 1 else 0
     return dict(attention=attention, kv=kv, write=write, step=attention + write)
 
 
@@ -93,7 +93,8 @@ class Replica:
     """One independent copy of the workload's device inputs plus a prepared
     step call."""
 
-    def __init__(self, wl, part, layout):
+    def __init__(self, wl, part, layout, ntok=1):
+        import numpy as np
         import torch
         import paged_kv_cache_434_amd as pkv
         from paged_kv_cache_434_amd import workloads as W
@@ -118,7 +119,19 @@ class Replica:
             cache = qcache
         out_dtype = torch.float32 if wl.q_dtype == "f32" else torch.bfloat16
         ws = pkv.alloc_workspace(wl.B, wl.Hq, wl.D, wl.max_blocks, part)
-        if wl.write:
+        if ntok > 1:
+            # several query tokens per sequence (their K/V already in the pool)
+            rng = np.random.default_rng(1)
+            q = torch.from_numpy(W.to_bf16_bits(rng.standard_normal(
+                (wl.B, ntok, wl.Hq, wl.D)).astype(np.float32)).view(np.int16)).view(
+                torch.bfloat16).cuda()
+            ws = pkv.alloc_workspace(wl.B * ntok, wl.Hq, wl.D, wl.max_blocks, part)
+            tables, lens, scale = d["tables"], d["lens"], float(wl.scale)
+            self.out = torch.empty((wl.B, ntok, wl.Hq, wl.D), dtype=out_dtype, device="cuda")
+            self.call = lambda: pkv.attention_multi(cache, q, tables, lens, scale,
+                                                    partition_tokens=part, workspace=ws,
+                                                    out=self.out)
+        elif wl.write:
             self.call, self.out = pkv.prepare_decode_step(
                 cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"], float(wl.scale),
                 partition_tokens=part, workspace=ws, out_dtype=out_dtype)
@@ -256,6 +269,9 @@ def main():
                          "[NB][Hkv][16][D] pools (split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="query tokens per sequence (>1: multi-token attention, e.g. verifying "
+                         "drafted tokens; their K/V are taken as already written)")
     ap.add_argument("--op", choices=("step", "quantize", "copy_blocks"), default="step",
                     help="what to time: the decode step (default) or another operation")
     args = ap.parse_args()
@@ -282,7 +298,7 @@ def main():
     e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[wl.quant or wl.kv_dtype]
     pool_bytes = wl.num_blocks * wl.Hkv * 16 * wl.D * 2 * e_kv
     n_rep = args.replicas or max(2, min(8, math.ceil(1.3e9 / pool_bytes) + 1))
-    reps = [Replica(wl, part, args.layout) for _ in range(n_rep)]
+    reps = [Replica(wl, part, args.layout, args.tokens) for _ in range(n_rep)]
     print(f"# workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
           f"sum(L)={int(wl.lens.sum())} pool={wl.num_blocks} quant={wl.quant} "
           f"partition={part} layout={args.layout} replicas={len(reps)}",
@@ -312,10 +328,11 @@ def main():
     torch.cuda.synchronize()
     kern_s = statistics.mean(a.elapsed_time(b) for a, b in evs) / 1e3
 
-    ab = algorithmic_bytes(wl)
+    ab = algorithmic_bytes(wl, args.tokens)
     value = ab["step"] / step_s / 1e9
     achieved = ab["step"] / kern_s / 1e9
-    key = f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/{part}"
+    key = (f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/{part}"
+           + (f"/tokens{args.tokens}" if args.tokens > 1 else ""))
     traffic = recorded_traffic(key)
     e_q = {"f32": "f32", "bf16": "bf16"}[wl.q_dtype]
     line = {
@@ -337,7 +354,10 @@ def main():
                    "pool_blocks": wl.num_blocks, "partition_tokens": part,
                    "split": "balanced" if part == pkv.SPLIT_BALANCED else "fixed",
                    "layout": args.layout, "replicas": len(reps),
-                   "step": ("decode step: slot of position L-1 + cache write + paged attention "
+                   "query_tokens_per_seq": args.tokens,
+                   "step": (f"paged attention of {args.tokens} query tokens per sequence + "
+                            "partition combine") if args.tokens > 1 else
+                           ("decode step: slot of position L-1 + cache write + paged attention "
                             "(one launch) + partition combine") if wl.write else
                            "paged attention over a quantized pool + partition combine"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -350,7 +370,7 @@ def main():
                      "kernel": "the step's kernels (decode attention, then the combine)",
                      "bytes_per_launch": ab["step"]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.tokens == 1:
         med, runs, threads = cpu_baseline(wl)
         line["cpu_baseline"] = {
             "value": round(ab["step"] / med / 1e9, 3), "unit": "GB/s", "cores": threads,

@@ -125,6 +125,15 @@ int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, int32_t num_seqs, int32_t* slot_mapping,
                      void* stream);
 
+/* Slot mapping for several new tokens per sequence: slot_mapping[s][i] is
+ * the slot of position t = context_lens[s] - tokens_per_seq + i (i <
+ * tokens_per_seq), or -1 when t < 0 or the length is past the table.  With
+ * tokens_per_seq = 1 this is pkv_slot_mapping.
+ *   slot_mapping: device int32 [num_seqs][tokens_per_seq], written. */
+int pkv_slot_mapping_tokens(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t tokens_per_seq,
+                            int32_t* slot_mapping, void* stream);
+
 /* Cache write ([KVC] "KV Cache 的本质": each decode step appends the new
  * token's K and V): for i < n with slot = slot_mapping[i] >= 0, copies the
  * bytes of k[i][g][:] and v[i][g][:] into row slot % 16 of block slot / 16,
@@ -200,6 +209,30 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                     float scale, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
+
+/* Paged attention for several query tokens per sequence ([KVC] "投机解码":
+ * the large model checks k drafted tokens in one forward pass; "Continuous
+ * Batching": a long prompt is fed in chunks).  The last k = tokens_per_seq of
+ * the L = context_lens[s] cached tokens are the queries: query token i sits at
+ * position L - k + i and attends to the tokens t <= L - k + i (causal within
+ * the chunk; tokens before it and itself):
+ *   out[s][i][h] = sum_{t <= L-k+i} softmax_t(scale * q[s][i][h] . k_t) v_t;
+ * a query token with L - k + i < 0 gets a zero row.  Their K/V must already be
+ * in the pool (pkv_slot_mapping_tokens + pkv_cache_write).
+ *   q, out: device [num_seqs][tokens_per_seq][num_q_heads][head_dim]
+ *   workspace: at least pkv_decode_workspace_bytes(num_seqs * tokens_per_seq,
+ *     num_q_heads, head_dim, max_blocks_per_seq, partition_tokens) bytes when
+ *     that is nonzero.
+ * A wavefront covers 16 / G query tokens of one KV head's group at a time
+ * (the K/V of a block is read once per such pass); other arguments, splits
+ * and dtypes as for pkv_attention_decode, except that fp32 pools are
+ * PKV_ERR_UNSUPPORTED here. */
+int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                        int32_t tokens_per_seq, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, float scale, int32_t partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                        void* stream);
 
 /* KV quantization ([MGMT] section 四, with one symmetric binary32 scale per
  * (block, KV head) tile): for each listed block b and KV head g, with

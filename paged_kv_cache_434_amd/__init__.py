@@ -60,6 +60,7 @@ def _load():
             "pkv_version": (ctypes.c_int, []),
             "pkv_pool_bytes": (ctypes.c_uint64, [I32, I32, I32, I32, I32]),
             "pkv_slot_mapping": (ctypes.c_int, [P, I32, P, I32, P, P]),
+            "pkv_slot_mapping_tokens": (ctypes.c_int, [P, I32, P, I32, I32, P, P]),
             "pkv_cache_write": (ctypes.c_int, [C, P, P, P, I32, P]),
             "pkv_decode_workspace_bytes": (ctypes.c_size_t, [I32, I32, I32, I32, I32]),
             "pkv_decode_default_partition": (I32, [I32, I32, I32]),
@@ -67,6 +68,8 @@ def _load():
                                                     ctypes.c_size_t, P, I32, P]),
             "pkv_decode_step": (ctypes.c_int, [C, P, I32, P, P, P, I32, P, I32, I32, F, I32, P,
                                                ctypes.c_size_t, P, I32, P]),
+            "pkv_attention_multi": (ctypes.c_int, [C, P, I32, I32, P, I32, P, I32, I32, F, I32, P,
+                                                   ctypes.c_size_t, P, I32, P]),
             "pkv_quantize": (ctypes.c_int, [C, C, P, I32, P]),
             "pkv_gather": (ctypes.c_int, [C, P, I32, P, P, I32, P, P, P]),
             "pkv_copy_blocks": (ctypes.c_int, [C, P, I32, P]),
@@ -87,6 +90,7 @@ def lib():
 
 
 EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_mapping",
+                    "pkv_slot_mapping_tokens", "pkv_attention_multi",
                     "pkv_cache_write", "pkv_decode_workspace_bytes",
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
                     "pkv_quantize", "pkv_copy_blocks",
@@ -200,6 +204,22 @@ def slot_mapping(block_tables, context_lens, out=None, stream=None):
     return out
 
 
+def slot_mapping_tokens(block_tables, context_lens, tokens_per_seq: int, out=None, stream=None):
+    """Slots of the last tokens_per_seq positions of every sequence, [B][k]."""
+    torch = _torch()
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    if out is None:
+        out = torch.empty((B, tokens_per_seq), dtype=torch.int32, device=context_lens.device)
+    _need(out, "slot_mapping", torch.int32, 2)
+    _check("pkv_slot_mapping_tokens",
+           _load().pkv_slot_mapping_tokens(_ptr(block_tables), block_tables.shape[1],
+                                           _ptr(context_lens), B, tokens_per_seq, _ptr(out),
+                                           _stream(stream)))
+    return out
+
+
 def cache_write(cache: PagedCache, k, v, slot_mapping, stream=None):
     torch = _torch()
     sd = _storage_dtype(cache.kv_dtype)
@@ -296,6 +316,38 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, 
                                           partition_tokens, workspace, out, out_dtype, stream,
                                           (k_new, v_new))
     _check(name, fn(*args))
+    return out
+
+
+def attention_multi(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                    partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
+                    stream=None):
+    """Several query tokens per sequence (q [B][k][Hq][D]); query token i of a
+    sequence of length L attends to the tokens up to position L - k + i."""
+    torch = _torch()
+    qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if qd is None:
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", None, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, k, Hq, D = q.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("q, block_tables and context_lens disagree on the batch size")
+    od = out_dtype or (out.dtype if out is not None else q.dtype)
+    if out is None:
+        out = torch.empty((B, k, Hq, D), dtype=od, device=q.device)
+    _need(out, "out", od, 4)
+    odn = {torch.float32: "f32", torch.bfloat16: "bf16"}[od]
+    maxb = block_tables.shape[1]
+    if decode_workspace_bytes(B * k, Hq, D, maxb, partition_tokens) and workspace is None:
+        workspace = alloc_workspace(B * k, Hq, D, maxb, partition_tokens, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attention_multi",
+           _load().pkv_attention_multi(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd], k,
+                                       _ptr(block_tables), maxb, _ptr(context_lens), B, Hq,
+                                       ctypes.c_float(scale), partition_tokens, _ptr(workspace),
+                                       ws_bytes, _ptr(out), DTYPE_CODES[odn], _stream(stream)))
     return out
 
 

@@ -69,8 +69,20 @@ int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
     return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!block_tables || !context_lens || !slot_mapping) return PKV_ERR_NULL;
-  return launch_slot_mapping(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return launch_slot_mapping(block_tables, max_blocks_per_seq, context_lens, num_seqs, 1,
                              slot_mapping, static_cast<hipStream_t>(stream));
+}
+
+int pkv_slot_mapping_tokens(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t tokens_per_seq,
+                            int32_t* slot_mapping, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE ||
+      tokens_per_seq <= 0 || (int64_t)num_seqs * tokens_per_seq > (int64_t)INT_MAX)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !slot_mapping) return PKV_ERR_NULL;
+  return launch_slot_mapping(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                             tokens_per_seq, slot_mapping, static_cast<hipStream_t>(stream));
 }
 
 int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
@@ -108,7 +120,8 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                          int32_t num_seqs, int32_t num_q_heads, float scale,
                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                         void* out, int32_t out_dtype, void* stream, bool append) {
+                         void* out, int32_t out_dtype, void* stream, bool append,
+                         int32_t ntok = 1) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   if (elem_bytes(q_dtype) == 0 || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
@@ -123,6 +136,9 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
     return PKV_ERR_SHAPE;
   if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
+  if (ntok <= 0 || ntok > 1024) return PKV_ERR_SHAPE;
+  if (ntok > 1 && kv == PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * ntok * num_q_heads > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (append) {
     if (cache->kv_dtype != PKV_F32 && cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
@@ -136,15 +152,15 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   // balanced split: flat block positions (and a range past the last) fit in int
   if ((int64_t)num_seqs * max_blocks_per_seq > (int64_t)(INT_MAX / 2)) return PKV_ERR_SHAPE;
   if (np > 1) {
-    size_t need = decode_workspace_layout((int64_t)num_seqs * num_q_heads, np, cache->head_dim,
-                                          num_seqs, nullptr, nullptr, nullptr);
+    size_t need = decode_workspace_layout((int64_t)num_seqs * ntok * num_q_heads, np,
+                                          cache->head_dim, num_seqs, nullptr, nullptr, nullptr);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
   }
   DecodeArgs a{cache,     q,          q_dtype,   block_tables,     max_blocks_per_seq,
                context_lens, num_seqs, num_q_heads, scale,          partition_tokens,
                workspace, out,        out_dtype, append ? k_new : nullptr,
-               append ? v_new : nullptr};
+               append ? v_new : nullptr, ntok};
   return launch_decode(a, static_cast<hipStream_t>(stream));
 }
 
@@ -166,6 +182,17 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
   return decode_common(cache, q, q_dtype, k, v, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, partition_tokens, workspace, workspace_bytes,
                        out, out_dtype, stream, true);
+}
+
+int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                        int32_t tokens_per_seq, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, float scale, int32_t partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                        void* stream) {
+  return decode_common(cache, q, q_dtype, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, partition_tokens, workspace,
+                       workspace_bytes, out, out_dtype, stream, false, tokens_per_seq);
 }
 
 int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,

@@ -11,18 +11,21 @@ namespace pkv {
 
 namespace {
 
+// slots[s][i] for the last ntok positions L - ntok + i of every sequence
+// (-1 for a negative position or a length past the table).
 __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int max_blocks,
-                                    const int32_t* __restrict__ lens, int n,
+                                    const int32_t* __restrict__ lens, int n, int ntok,
                                     int32_t* __restrict__ slots) {
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= n) return;
-  int L = lens[s];
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n * ntok) return;
+  const int s = (int)(idx / ntok), i = (int)(idx % ntok);
+  const int L = lens[s];
   int32_t slot = -1;
   if (L > 0 && L <= max_blocks * kBlock) {
-    int t = L - 1;
-    slot = tables[(size_t)s * max_blocks + t / kBlock] * kBlock + t % kBlock;
+    const int t = L - ntok + i;
+    if (t >= 0) slot = tables[(size_t)s * max_blocks + t / kBlock] * kBlock + t % kBlock;
   }
-  slots[s] = slot;
+  slots[idx] = slot;
 }
 
 // One thread per 16-byte chunk of one (token, KV head) row; rows of K and V
@@ -111,9 +114,9 @@ int launch_copy_blocks(const pkv_cache_t& c, const int32_t* pairs, int n, hipStr
 }
 
 int launch_slot_mapping(const int32_t* tables, int max_blocks, const int32_t* lens, int n,
-                        int32_t* slots, hipStream_t st) {
-  dim3 grid((n + 255) / 256), block(256);
-  return launch(slot_mapping_kernel, grid, block, st, tables, max_blocks, lens, n, slots);
+                        int ntok, int32_t* slots, hipStream_t st) {
+  dim3 grid((unsigned)(((int64_t)n * ntok + 255) / 256)), block(256);
+  return launch(slot_mapping_kernel, grid, block, st, tables, max_blocks, lens, n, ntok, slots);
 }
 
 int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,

@@ -78,7 +78,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---- launchers (defined in the .hip sources) --------------------------------
 
 int launch_slot_mapping(const int32_t* tables, int max_blocks, const int32_t* lens, int n,
-                        int32_t* slots, hipStream_t st);
+                        int ntok, int32_t* slots, hipStream_t st);
 int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,
                        int n, hipStream_t st);
 int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
@@ -104,6 +104,7 @@ struct DecodeArgs {
   int out_dtype;
   const void* k_new;   // fused append of position L-1 (decode step), or nullptr
   const void* v_new;
+  int ntok;            // query tokens per sequence (1: decode)
 };
 int launch_decode(const DecodeArgs& a, hipStream_t st);
 

@@ -156,6 +156,8 @@ struct MfmaArgs {
   int kstride;        // partial slots per (sequence, query head)
   int part_blocks;    // fixed split: blocks per partition
   int min_blocks;     // balanced split: fewest blocks one wavefront takes
+  int ntok;           // query tokens per sequence (1: decode)
+  int tok_per_pass;   // query tokens one wavefront takes (ntok * G columns split in passes)
   void* out;
   const uint8_t* kn;  // fused append (decode step): new K/V rows, or null
   const uint8_t* vn;
@@ -186,13 +188,15 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 __device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 
-// Zero output rows of the query heads of KV head g for an empty sequence s.
+// Zero output rows of the query heads of KV head g of an empty sequence s
+// (every query token of this wavefront's pass).
 template <int D, int OUT>
-__device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g) {
+__device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g, int tok0) {
   const int lane = threadIdx.x;
   const int j = lane >> 4, n = lane & 15;
-  if (n >= a.G) return;
-  const size_t row = (size_t)s * a.hq + g * a.G + n;
+  const int ti = tok0 + n / a.G;
+  if (n >= a.G * a.tok_per_pass || ti >= a.ntok) return;
+  const size_t row = ((size_t)s * a.ntok + ti) * a.hq + g * a.G + n % a.G;
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     store_out4<D, OUT>(a.out, row * D + 16 * t + 4 * j, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -202,10 +206,10 @@ __device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g) {
 // its logical blocks [b0, b1).  `whole`: the range is the whole context, so the
 // normalised rows go to `out`; otherwise the partial (max, sum, output) goes
 // to partial slot `slot` of each row.
-template <int D, int KV, int OUT, int NST>
+template <int D, int KV, int OUT, int NST, bool MQ>
 __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, int L, int b0,
-                                             int b1, int slot, bool whole, uint8_t* lds_k,
-                                             uint8_t* lds_v) {
+                                             int b1, int slot, bool whole, int tok0,
+                                             uint8_t* lds_k, uint8_t* lds_v) {
   constexpr int kEsz = (KV == KV_BF16) ? 2 : 1;
   constexpr int kTile = kBlock * D * kEsz;  // bytes of one (block, head) tile in HBM
   constexpr int kLoads = kTile / 1024;      // 16-byte loads per lane per tile
@@ -215,8 +219,14 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   const int j = lane >> 4;   // token quad (rows 4j..4j+3 of S) / k-slice
   const int n = lane & 15;   // head column
   const int G = a.G, hq = a.hq, hkv = a.hkv, num_blocks = a.num_blocks;
-  const int h = g * G + n;
-  const bool has_head = n < G;
+  // column n of S, P and O: query token ti (several per sequence only with
+  // MQ) and head h of the group
+  const int ti = MQ ? tok0 + n / G : 0;
+  const int h = g * G + (MQ ? n % G : n);
+  const bool has_head = MQ ? (n < G * a.tok_per_pass && ti < a.ntok) : n < G;
+  const size_t out_row = MQ ? ((size_t)s * a.ntok + ti) * hq + h : (size_t)s * hq + h;
+  // last key position + 1 this column may see (causal within the chunk)
+  const int lim = MQ ? L - a.ntok + ti + 1 : L;
 
   f32x4 acc[kNT];
 #pragma unroll
@@ -226,7 +236,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // q[h][32 kk + 8 j .. + 8] for each kk
   bf16x8 qop[kNKK];
   {
-    const uint16_t* qrow = a.q + ((size_t)s * hq + (has_head ? h : g * G)) * D;
+    const uint16_t* qrow = a.q + (has_head ? out_row : (size_t)s * a.ntok * hq) * D;
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * j);
@@ -361,9 +371,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const float cb = a.scale_log2 * kscale;
       float x[4];
       float mx = -INFINITY;
+      const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = (4 * j + i < valid) ? sv[i] * cb : -INFINITY;
+        x[i] = (4 * j + i < vcol) ? sv[i] * cb : -INFINITY;
         mx = fmaxf(mx, x[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -417,14 +428,16 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
   float lt = lsum + __shfl_xor(lsum, 16, kWave);
   lt += __shfl_xor(lt, 32, kWave);
+  // a column that saw no key (a query token before the start, or a piece
+  // past its causal limit) has lt == 0: zero output, zero weight
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (!has_head) return;
-  const float inv = 1.0f / lt;
   if (whole) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
-      store_out4<D, OUT>(a.out, ((size_t)s * hq + h) * D + 16 * t + 4 * j, acc[t] * inv);
+      store_out4<D, OUT>(a.out, out_row * D + 16 * t + 4 * j, acc[t] * inv);
   } else {
-    const size_t row = ((size_t)s * hq + h) * a.kstride + slot;
+    const size_t row = out_row * a.kstride + slot;
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
       *reinterpret_cast<f32x4*>(a.ws_o + row * D + 16 * t + 4 * j) = acc[t] * inv;
@@ -437,7 +450,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
 // Fixed split: one wavefront per (sequence, KV head, partition of
 // part_blocks blocks); the launch index is decoded KV-head-fastest.
-template <int D, int KV, int OUT>
+template <int D, int KV, int OUT, bool MQ>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
@@ -450,11 +463,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
   const int parts_s = (nblk + a.part_blocks - 1) / a.part_blocks;
   const int b0 = p * a.part_blocks;
   const int b1 = min(b0 + a.part_blocks, nblk);
+  const int tok0 = blockIdx.y * a.tok_per_pass;
   if (b0 >= b1) {
-    if (p == 0) zero_rows<D, OUT>(a, s, g);   // empty sequence
+    if (p == 0) zero_rows<D, OUT>(a, s, g, tok0);   // empty sequence
     return;
   }
-  mfma_segment<D, KV, OUT, 2>(a, s, g, L, b0, b1, p, parts_s == 1, lds_k, lds_v);
+  mfma_segment<D, KV, OUT, 2, MQ>(a, s, g, L, b0, b1, p, parts_s == 1, tok0, lds_k, lds_v);
 }
 
 // Balanced split: a persistent grid of V wavefronts per KV head, one
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 #define PKV_BAL_STAGES 2
 #define PKV_BAL_WAVES 2
 #endif
-template <int D, int KV, int OUT>
+template <int D, int KV, int OUT, bool MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_BAL_WAVES))) void
 decode_mfma_balanced_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
@@ -483,6 +497,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   const int v = blockIdx.x / a.hkv;
   const int V = gridDim.x / a.hkv;
   const int B = a.num_seqs;
+  const int tok0 = blockIdx.y * a.tok_per_pass;
 
   // The lengths of the first kLenChunks * 64 sequences are loaded once, all
   // at the same time, and kept in registers for both passes and the walk.
@@ -518,7 +533,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
       while (empty) {
         const int e = __ffsll((unsigned long long)empty) - 1;
         empty &= empty - 1;
-        zero_rows<D, OUT>(a, base + e, g);
+        zero_rows<D, OUT>(a, base + e, g, tok0);
       }
     }
   }
@@ -557,9 +572,9 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int vf = R0 / per;
     const int K = (R1 - 1) / per - vf + 1;
     const int slot = v - vf;
-    if (g == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
-    mfma_segment<D, KV, OUT, PKV_BAL_STAGES>(a, s, g, L, x - R0, e - R0, slot, K == 1, lds_k,
-                                             lds_v);
+    if (g == 0 && blockIdx.y == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
+    mfma_segment<D, KV, OUT, PKV_BAL_STAGES, MQ>(a, s, g, L, x - R0, e - R0, slot, K == 1, tok0,
+                                                 lds_k, lds_v);
     if (e >= x1) break;
     x = e;
     R0 = R1;
@@ -725,12 +740,13 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
                                                     const float* __restrict__ ws_o,
                                                     const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ lens,
-                                                    int max_blocks, int hq, int part_blocks,
-                                                    int kstride, void* __restrict__ out) {
+                                                    int max_blocks, int rows_per_seq,
+                                                    int part_blocks, int kstride,
+                                                    void* __restrict__ out) {
   constexpr int kCols = D / 4;             // lanes per partial row (16-byte pieces)
   constexpr int kRowsPerLoad = kWave / kCols;
   const int row = blockIdx.x;
-  const int s = row / hq;
+  const int s = row / rows_per_seq;
   const int lane = threadIdx.x;
   const float* mrow = ws_m + (size_t)row * kstride;
   const float* lrow = ws_l + (size_t)row * kstride;
@@ -799,7 +815,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   for (int o = kCols; o < kWave; o <<= 1)
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], o, kWave);
-  if (sub == 0) store_out4<D, OUT>(out, (size_t)row * D + col * 4, a * (1.0f / den));
+  // den == 0: no piece saw a key (query tokens before the start)
+  if (sub == 0) store_out4<D, OUT>(out, (size_t)row * D + col * 4, a * (den > 0.f ? 1.0f / den : 0.f));
 }
 
 // One-wavefront workgroups of `kernel` that fit on a compute unit at once
@@ -824,6 +841,8 @@ struct Plan {
   int n_parts;        // fixed split: partitions per sequence
   int kstride;        // partial slots per row in the workspace
   int cus;            // balanced split: compute units of the device
+  int tok_per_pass;   // query tokens per wavefront (tok_per_pass * G <= 16 columns)
+  int passes;         // wavefronts per work unit: ceil(ntok / tok_per_pass)
   float *ws_m, *ws_l, *ws_o;
   int32_t* ws_count;
 };
@@ -868,6 +887,8 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
     m.kstride = pl.kstride;
     m.part_blocks = pl.part_blocks;
     m.min_blocks = kBalancedMinBlocks;
+    m.ntok = a.ntok;
+    m.tok_per_pass = pl.tok_per_pass;
     m.out = a.out;
     m.kn = q8 ? nullptr : (const uint8_t*)a.k_new;
     m.vn = q8 ? nullptr : (const uint8_t*)a.v_new;
@@ -879,30 +900,40 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(balanced_kernel));
         if (per_cu <= 0) return (int)PKV_ERR_HIP;
         const int64_t waves = (int64_t)pl.cus * per_cu;
-        dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv));
+        dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv), (unsigned)pl.passes);
         return launch(balanced_kernel, grid, block, st, m);
       }
-      dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts));
+      dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts), (unsigned)pl.passes);
       return launch(fixed_kernel, grid, block, st, m, pl.n_parts);
     };
+    const bool mq = a.ntok > 1;
     switch (c.kv_dtype) {
       case PKV_BF16:
-        rc = go(decode_mfma_kernel<D, KV_BF16, OUT>, decode_mfma_balanced_kernel<D, KV_BF16, OUT>);
+        rc = mq ? go(decode_mfma_kernel<D, KV_BF16, OUT, true>,
+                     decode_mfma_balanced_kernel<D, KV_BF16, OUT, true>)
+                : go(decode_mfma_kernel<D, KV_BF16, OUT, false>,
+                     decode_mfma_balanced_kernel<D, KV_BF16, OUT, false>);
         break;
       case PKV_I8:
-        rc = go(decode_mfma_kernel<D, KV_I8, OUT>, decode_mfma_balanced_kernel<D, KV_I8, OUT>);
+        rc = mq ? go(decode_mfma_kernel<D, KV_I8, OUT, true>,
+                     decode_mfma_balanced_kernel<D, KV_I8, OUT, true>)
+                : go(decode_mfma_kernel<D, KV_I8, OUT, false>,
+                     decode_mfma_balanced_kernel<D, KV_I8, OUT, false>);
         break;
       default:
-        rc = go(decode_mfma_kernel<D, KV_FP8, OUT>, decode_mfma_balanced_kernel<D, KV_FP8, OUT>);
+        rc = mq ? go(decode_mfma_kernel<D, KV_FP8, OUT, true>,
+                     decode_mfma_balanced_kernel<D, KV_FP8, OUT, true>)
+                : go(decode_mfma_kernel<D, KV_FP8, OUT, false>,
+                     decode_mfma_balanced_kernel<D, KV_FP8, OUT, false>);
         break;
     }
   }
   if (rc != PKV_OK || pl.kstride <= 1) return rc;
-  dim3 rgrid((unsigned)((int64_t)a.num_seqs * hq));
+  dim3 rgrid((unsigned)((int64_t)a.num_seqs * a.ntok * hq));
   return launch(reduce_kernel<D, OUT>, rgrid, block, st, (const float*)pl.ws_m,
                 (const float*)pl.ws_l, (const float*)pl.ws_o,
-                (const int32_t*)(pl.balanced ? pl.ws_count : nullptr), a.lens, a.max_blocks, hq,
-                pl.part_blocks, pl.kstride, a.out);
+                (const int32_t*)(pl.balanced ? pl.ws_count : nullptr), a.lens, a.max_blocks,
+                a.ntok * hq, pl.part_blocks, pl.kstride, a.out);
 }
 
 }  // namespace
@@ -962,12 +993,15 @@ int launch_decode(const DecodeArgs& a, hipStream_t st) {
     pl.cus = device_cu_count();
     if (pl.cus <= 0) return PKV_ERR_HIP;
   }
+  const int G = a.num_q_heads / c.num_kv_heads;
+  pl.tok_per_pass = a.ntok > 1 ? max(1, 16 / G) : 1;
+  pl.passes = (a.ntok + pl.tok_per_pass - 1) / pl.tok_per_pass;
   pl.ws_m = pl.ws_l = pl.ws_o = nullptr;
   pl.ws_count = nullptr;
   if (pl.kstride > 1) {
     size_t om, ol, oc;
-    decode_workspace_layout((int64_t)a.num_seqs * a.num_q_heads, pl.kstride, c.head_dim,
-                            a.num_seqs, &om, &ol, &oc);
+    decode_workspace_layout((int64_t)a.num_seqs * a.ntok * a.num_q_heads, pl.kstride,
+                            c.head_dim, a.num_seqs, &om, &ol, &oc);
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     pl.ws_o = reinterpret_cast<float*>(ws);
     pl.ws_m = reinterpret_cast<float*>(ws + om);

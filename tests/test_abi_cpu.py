@@ -173,3 +173,20 @@ def test_block_stride_validation():
     assert lib.pkv_copy_blocks(ctypes.byref(small), FAKE, 1, None) == 2
     odd = _cache(block_stride=2 * 2 * 16 * 128 + 3)    # not a multiple of 16 bytes
     assert lib.pkv_copy_blocks(ctypes.byref(odd), FAKE, 1, None) == 6
+
+
+def test_multi_token_entry_points_reject_bad_arguments():
+    lib = pkv.lib()
+    c = _cache()
+    f = ctypes.c_float(0.1)
+    # tokens_per_seq must be positive; fp32 pools are not supported for several tokens
+    assert lib.pkv_attention_multi(ctypes.byref(c), FAKE, 1, 0, FAKE, 4, FAKE, 2, 4, f, 0, None, 0,
+                                   FAKE, 1, None) == 2
+    c32 = _cache(kv_dtype=0)
+    assert lib.pkv_attention_multi(ctypes.byref(c32), FAKE, 0, 2, FAKE, 4, FAKE, 2, 4, f, 0, None,
+                                   0, FAKE, 0, None) == 6
+    assert lib.pkv_attention_multi(ctypes.byref(c), FAKE, 1, 2, FAKE, 64, FAKE, 2, 4, f, 256,
+                                   None, 0, FAKE, 1, None) == 5        # split needs a workspace
+    assert lib.pkv_slot_mapping_tokens(FAKE, 4, FAKE, 2, 0, FAKE, None) == 2
+    assert lib.pkv_slot_mapping_tokens(None, 4, FAKE, 2, 3, FAKE, None) == 1
+    assert lib.pkv_slot_mapping_tokens(FAKE, 4, FAKE, 0, 3, FAKE, None) == 0

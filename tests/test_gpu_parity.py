@@ -632,3 +632,101 @@ def test_copy_on_write_branch_append(part):
     ref = oracle.decode(q, "bf16", k, v, "bf16", t2, l2, wl.scale)
     _cmp(_out_np(after), ref, TOL["bf16"], "f32", "copy-on-write branches")
     _cmp(_out_np(out_app), ref[app], TOL["bf16"], "f32", "copy-on-write fused step")
+
+
+# ------------------------------------------------- several query tokens per sequence
+
+
+def _mq_q(rng, B, k, Hq, D):
+    return W.to_bf16_bits(rng.standard_normal((B, k, Hq, D)).astype(np.float32))
+
+
+def _dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+MQ_CASES = [
+    # (workload, overrides, tokens per sequence, split, layout, quant)
+    (2, dict(B=6, lo=1, hi=600, pool=300), 1, 0, "split", None),
+    (2, dict(B=6, lo=1, hi=600, pool=300), 2, 0, "split", None),
+    (2, dict(B=6, lo=1, hi=600, pool=300), 4, 256, "split", None),
+    (2, dict(B=6, lo=1, hi=600, pool=300), 4, -1, "blocks", None),
+    (2, dict(B=6, lo=1, hi=600, pool=300), 7, -1, "split", None),      # 2 passes of 4 tokens
+    (2, dict(B=5, lens=[1, 3, 16, 17, 300], hi=300, pool=100), 4, -1, "blocks", None),
+    (3, dict(B=12, median=200, lo=1, hi=700), 2, -1, "blocks", None),  # G = 8
+    (3, dict(B=12, median=200, lo=1, hi=700), 3, 128, "split", None),  # G = 8, 2 passes
+    (2, dict(B=4, lo=1, hi=300, pool=200, Hq=8, Hkv=8), 16, -1, "split", None),   # G = 1
+    (2, dict(B=4, lo=1, hi=300, pool=200, Hq=8, Hkv=8), 20, 0, "blocks", None),   # 2 passes
+    (2, dict(B=4, lo=1, hi=400, pool=200, D=64), 4, -1, "split", None),           # D = 64
+    (5, dict(B=8, prefix=128, suffix_hi=200), 4, -1, "blocks", "i8"),
+    (5, dict(B=8, prefix=128, suffix_hi=200), 3, 256, "split", "fp8"),
+]
+
+
+@pytest.mark.parametrize("cfg,over,k,part,layout,quant", MQ_CASES)
+def test_attention_multi(cfg, over, k, part, layout, quant):
+    wl = W.make(cfg, quant=quant, **over)
+    _say(f"attention multi: {wl.name} {over} k={k} part={part} {layout} quant={quant}")
+    rng = np.random.default_rng(100 + k)
+    q = _mq_q(rng, wl.B, k, wl.Hq, wl.D)
+    d = W.to_device(wl, layout=layout)
+    cache = _dev_cache(d, wl)
+    kc, vc, ks, vs, kvd = wl.k_pool, wl.v_pool, None, None, wl.kv_dtype
+    if quant:
+        NB = wl.num_blocks
+        qt = torch.int8 if quant == "i8" else torch.uint8
+        kss = torch.empty((NB, wl.Hkv), dtype=torch.float32, device="cuda")
+        vss = torch.empty_like(kss)
+        qc = pkv.PagedCache.from_blocks(torch.empty((NB, 2, wl.Hkv, 16, wl.D), dtype=qt,
+                                                    device="cuda"), quant, kss, vss)
+        pkv.quantize(cache, qc)
+        cache = qc
+        kc, ks = oracle.quantize(wl.k_pool, "bf16", quant)
+        vc, vs = oracle.quantize(wl.v_pool, "bf16", quant)
+        kvd = quant
+    out = pkv.attention_multi(cache, _dev_bf16(q), d["tables"], d["lens"], float(wl.scale),
+                              partition_tokens=part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.decode_multi(q, "bf16", kc, vc, kvd, wl.tables, wl.lens, wl.scale,
+                              k_scale=ks, v_scale=vs)
+    _cmp(_out_np(out), ref, TOL[quant or "bf16"], "f32", f"multi k={k}")
+    if k == 1:   # the single-token call runs the decode kernel itself
+        dec = pkv.attention_decode(cache, _dev_bf16(q[:, 0]), d["tables"], d["lens"],
+                                   float(wl.scale), partition_tokens=part,
+                                   out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, 0], dec)
+
+
+def test_slot_mapping_tokens_bit_exact():
+    wl = W.make(2, B=9, lens=[0, 1, 3, 15, 16, 17, 40, 100, 599], hi=600, pool=200)
+    d = W.to_device(wl)
+    for k in (1, 3, 5):
+        got = pkv.slot_mapping_tokens(d["tables"], d["lens"], k)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), oracle.slot_mapping_tokens(wl.tables, wl.lens, k))
+
+
+@pytest.mark.parametrize("part", [0, -1])
+def test_speculative_verify_flow(part):
+    """k drafted tokens per sequence: slots of the last k positions, one cache
+    write of all B*k rows, then one multi-token attention call."""
+    k = 4
+    wl = W.make(2, B=8, lo=k, hi=900, pool=600)
+    rng = np.random.default_rng(77)
+    kn = W.to_bf16_bits(rng.standard_normal((wl.B * k, wl.Hkv, wl.D)).astype(np.float32))
+    vn = W.to_bf16_bits(rng.standard_normal((wl.B * k, wl.Hkv, wl.D)).astype(np.float32))
+    q = _mq_q(rng, wl.B, k, wl.Hq, wl.D)
+    d = W.to_device(wl, layout="blocks")
+    cache = _dev_cache(d, wl)
+    slots = pkv.slot_mapping_tokens(d["tables"], d["lens"], k)
+    pkv.cache_write(cache, _dev_bf16(kn), _dev_bf16(vn), slots.reshape(-1))
+    out = pkv.attention_multi(cache, _dev_bf16(q), d["tables"], d["lens"], float(wl.scale),
+                              partition_tokens=part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    kh, vh = wl.k_pool.copy(), wl.v_pool.copy()
+    oracle.cache_write(kh, vh, "bf16", kn, vn,
+                       oracle.slot_mapping_tokens(wl.tables, wl.lens, k).reshape(-1))
+    assert np.array_equal(W.from_device(d["k_pool"]), kh)
+    ref = oracle.decode_multi(q, "bf16", kh, vh, "bf16", wl.tables, wl.lens, wl.scale)
+    _cmp(_out_np(out), ref, TOL["bf16"], "bf16", "speculative verify")
