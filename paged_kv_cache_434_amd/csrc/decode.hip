@@ -90,12 +90,13 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * (D * 2) + ((chunk ^ (row & (kChunks - 1))) << 4);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16_of_int(float lo, float hi) {
-  // lo and hi are small integers: their binary32 upper halves are exact bf16
-  return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
-}
-
 // 16 8-bit codes -> 16 bf16 values (two 16-byte chunks), exact.
+// E4M3: the gfx950 conversion instruction, two codes at a time.
+// INT8: the sign bit is flipped, so code c becomes u = c + 128 in [1, 255];
+// an unsigned byte converts to binary32 in one instruction and u < 256 has at
+// most 8 significant bits, so its binary32 upper half is u in bf16 exactly.
+// The kernel subtracts the offset afterwards: 128 * sum(q) from each logit
+// and 128 * sum(p) from each output column.
 template <int KV>
 __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
   const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
@@ -103,12 +104,14 @@ __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (KV == KV_I8) {
-      const float f0 = (float)(int8_t)(w[i] & 0xFF);
-      const float f1 = (float)(int8_t)((w[i] >> 8) & 0xFF);
-      const float f2 = (float)(int8_t)((w[i] >> 16) & 0xFF);
-      const float f3 = (float)(int8_t)(w[i] >> 24);
-      o[2 * i] = pack_bf16_of_int(f0, f1);
-      o[2 * i + 1] = pack_bf16_of_int(f2, f3);
+      const uint32_t u = w[i] ^ 0x80808080u;
+      const float f0 = (float)(u & 0xFFu);
+      const float f1 = (float)((u >> 8) & 0xFFu);
+      const float f2 = (float)((u >> 16) & 0xFFu);
+      const float f3 = (float)(u >> 24);
+      // bytes 2,3 of the low value, then bytes 2,3 of the high value
+      o[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+      o[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
     } else {
       bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
       bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
@@ -243,6 +246,18 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       qop[kk] = has_head ? v : bf16x8{};
     }
   }
+  // INT8 codes enter the MFMA as c + 128 (see widen16): each logit then holds
+  // 128 * sum_d q[h][d] too, which is taken off again before the softmax
+  float qoff = 0.f;
+  if constexpr (KV == KV_I8) {
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qoff += static_cast<float>(qop[kk][e]);
+    qoff += __shfl_xor(qoff, 16, kWave);
+    qoff += __shfl_xor(qoff, 32, kWave);
+    qoff *= 128.f;
+  }
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = a.blk_stride;
@@ -272,6 +287,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
   float m = kNoMax;   // running reference maximum (log2 units)
   float lsum = 0.f;   // this lane's share of the softmax denominator
+  float psum = 0.f;   // INT8: this lane's share of sum(P), rescaled like the accumulator
 
   // The range is walked in chunks of up to 64 blocks.  Per chunk, lane i
   // loads block-table entry i (and, for 8-bit KV, that block's two scales);
@@ -374,7 +390,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = (4 * j + i < vcol) ? sv[i] * cb : -INFINITY;
+        const float raw = (KV == KV_I8) ? sv[i] - qoff : sv[i];
+        x[i] = (4 * j + i < vcol) ? raw * cb : -INFINITY;
         mx = fmaxf(mx, x[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -384,6 +401,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         const float mnew = bump ? mx : m;
         const float alpha = exp2f(m - mnew);
         lsum *= alpha;
+        if constexpr (KV == KV_I8) psum *= alpha;
 #pragma unroll
         for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
         m = mnew;
@@ -394,6 +412,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         const float pe = exp2f(x[i] - m);
         lsum += pe;
         pop[i] = static_cast<__bf16>(pe * vscale);
+        if constexpr (KV == KV_I8) psum += static_cast<float>(pop[i]);
       }
 
       // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n]
@@ -428,6 +447,14 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
   float lt = lsum + __shfl_xor(lsum, 16, kWave);
   lt += __shfl_xor(lt, 32, kWave);
+  if constexpr (KV == KV_I8) {
+    // the V codes entered as c + 128: take 128 * sum(P) off every output row
+    float pt = psum + __shfl_xor(psum, 16, kWave);
+    pt += __shfl_xor(pt, 32, kWave);
+    const float voff = 128.f * pt;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) acc[t] -= voff;
+  }
   // a column that saw no key (a query token before the start, or a piece
   // past its causal limit) has lt == 0: zero output, zero weight
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -675,30 +702,78 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
     const int phys = trow[b];
     if (phys < 0 || phys >= num_blocks) continue;
     const int valid = min(kBlock, L - b * kBlock);
-    for (int o = 0; o < valid; ++o) {
-      const size_t base = (size_t)phys * bstride + ((size_t)g * kBlock + o) * D + lane * kPer;
-      const bool is_new = app && b * kBlock + o == L - 1;
-      float kv[kPer], vv[kPer];
+    // the block's 16 K and V rows are loaded together (one memory latency per
+    // block, not per token); rows past L are loaded but never used
+    const size_t base0 = (size_t)phys * bstride + (size_t)g * kBlock * D + lane * kPer;
+    float kt[kBlock][kPer], vt[kBlock][kPer];
+#pragma unroll
+    for (int o = 0; o < kBlock; ++o)
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
-        kv[e] = is_new ? kx[e] : kc[base + e];
-        vv[e] = is_new ? vx[e] : vc[base + e];
+        kt[o][e] = kc[base0 + (size_t)o * D + e];
+        vt[o][e] = vc[base0 + (size_t)o * D + e];
+      }
+    if (app && (L - 1) / kBlock == b) {   // the appended token's row
+      const int o = (L - 1) % kBlock;
+#pragma unroll
+      for (int oo = 0; oo < kBlock; ++oo)
+        if (oo == o)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            kt[oo][e] = kx[e];
+            vt[oo][e] = vx[e];
+          }
+    }
+    // after the reduce-scatter below lane l holds the dot product of token l / 4
+    const int tok = (lane >> 2) & (kBlock - 1);
+#pragma unroll
+    for (int hh = 0; hh < MAXG; ++hh) {
+      if (hh >= G) break;
+      // 16 partial dot products per lane, then a butterfly reduce-scatter:
+      // after it, every lane holds the full dot product of token lane / 4
+      float x[kBlock];
+#pragma unroll
+      for (int o = 0; o < kBlock; ++o) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) d += qv[hh][e] * kt[o][e];
+        x[o] = d;
       }
 #pragma unroll
-      for (int hh = 0; hh < MAXG; ++hh) {
-        if (hh >= G) break;
-        float dot = 0.f;
+      for (int step = 0, half = kBlock / 2; half >= 1; ++step, half >>= 1) {
+        const int bit = 32 >> step;                 // lane bits 5, 4, 3, 2
+        const bool upper = (lane & bit) != 0;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) dot += qv[hh][e] * kv[e];
-        const float xl = wave_sum(dot) * scale_log2;
-        const float mn = fmaxf(m[hh], xl);
-        const float alpha = exp2f(m[hh] - mn);
-        const float pe = exp2f(xl - mn);
-        l[hh] = l[hh] * alpha + pe;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) acc[hh][e] = acc[hh][e] * alpha + pe * vv[e];
-        m[hh] = mn;
+        for (int i = 0; i < half; ++i) {
+          const float mine = upper ? x[i + half] : x[i];
+          const float other = upper ? x[i] : x[i + half];
+          x[i] = mine + __shfl_xor(other, bit, kWave);
+        }
       }
+      float dot = x[0];
+      dot += __shfl_xor(dot, 1, kWave);
+      dot += __shfl_xor(dot, 2, kWave);
+      const float xl = tok < valid ? dot * scale_log2 : -INFINITY;
+      float mx = xl;
+#pragma unroll
+      for (int o = 4; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+      const float mn = fmaxf(m[hh], mx);
+      const float alpha = exp2f(m[hh] - mn);
+      const float pe = exp2f(xl - mn);               // 0 for masked tokens
+      float ps = pe;
+#pragma unroll
+      for (int o = 4; o < kWave; o <<= 1) ps += __shfl_xor(ps, o, kWave);
+      l[hh] = l[hh] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[hh][e] *= alpha;
+#pragma unroll
+      for (int o = 0; o < kBlock; ++o) {
+        // lanes 4 o .. 4 o + 3 hold token o's weight
+        const float po = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), 4 * o));
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[hh][e] += po * vt[o][e];
+      }
+      m[hh] = mn;
     }
   }
 #pragma unroll
@@ -928,7 +1003,8 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         break;
     }
   }
-  if (rc != PKV_OK || pl.kstride <= 1) return rc;
+  // no combine when nothing can be split: a fixed split with one partition
+  if (rc != PKV_OK || pl.kstride <= 1 || (!pl.balanced && pl.n_parts <= 1)) return rc;
   dim3 rgrid((unsigned)((int64_t)a.num_seqs * a.ntok * hq));
   return launch(reduce_kernel<D, OUT>, rgrid, block, st, (const float*)pl.ws_m,
                 (const float*)pl.ws_l, (const float*)pl.ws_o,
