@@ -27,7 +27,10 @@
  * uses KV head h / (Hq/Hkv); context_len counts the newly written token;
  * context_len 0 gives a zero output row; symmetric per-(block, head) scales
  * with fp32 arithmetic; FP8 is OCP E4M3 ("fn": no infinities, 0x7F/0xFF NaN,
- * max finite 448), round-to-nearest-even with saturation.
+ * max finite 448), round-to-nearest-even with saturation.  The asymmetric
+ * per-row format (uint8 code, binary32 scale, uint8 zero point per (block,
+ * head, row)) follows [MGMT] section 四's KVQuantizationCache in binary32,
+ * with a zero-width row stored as scale 0, zero point 0, codes 0.
  *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
@@ -40,7 +43,7 @@
 #endif
 
 /* Element type codes understood by the oracle (its own numbering). */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_U8Z = 4 };
 
 /* Number of threads the parallel loops below use (1 without OpenMP).       */
 int orc_max_threads(void) {
@@ -57,6 +60,7 @@ static size_t orc_elem_bytes(int dtype) {
     case ORC_BF16: return 2;
     case ORC_I8: return 1;
     case ORC_FP8: return 1;
+    case ORC_U8Z: return 1;
   }
   return 0;
 }
@@ -139,15 +143,34 @@ uint8_t orc_e4m3_from_float(float x) {
 /* Widen one stored KV element to double.  Quantized codes are multiplied by
  * their (block, head) scale, as in [MGMT] section 四 (dequantize: code times
  * scale); the product of an 8-bit code and a binary32 scale is exact in
- * double.                                                                   */
-static double orc_load_elem(const void* base, size_t idx, int dtype, double scale) {
+ * double.  Asymmetric codes first lose their row's zero point ([MGMT] 四,
+ * dequantize_key: (code - zero_point) * scale); the difference is an integer
+ * in [-255, 255], so that product is exact in double too.                   */
+static double orc_load_elem(const void* base, size_t idx, int dtype, double scale, double zero) {
   switch (dtype) {
     case ORC_F32: return (double)((const float*)base)[idx];
     case ORC_BF16: return orc_bf16_to_double(((const uint16_t*)base)[idx]);
     case ORC_I8: return (double)((const int8_t*)base)[idx] * scale;
     case ORC_FP8: return orc_e4m3_to_double(((const uint8_t*)base)[idx]) * scale;
+    case ORC_U8Z: return ((double)((const uint8_t*)base)[idx] - zero) * scale;
   }
   return NAN;
+}
+
+/* Scale and zero point of the stored row (block b, KV head g, row o): one
+ * pair per (block, head) for the symmetric formats, one per row for the
+ * asymmetric one, none (1, 0) for float pools.                              */
+static void orc_row_params(int dtype, const float* scale, const uint8_t* zero, size_t b,
+                           size_t g, size_t o, int Hkv, int bs, double* sc, double* zp) {
+  *sc = 1.0;
+  *zp = 0.0;
+  if (dtype == ORC_U8Z) {
+    size_t r = (b * (size_t)Hkv + g) * (size_t)bs + o;
+    *sc = (double)scale[r];
+    *zp = (double)zero[r];
+  } else if (scale) {
+    *sc = (double)scale[b * (size_t)Hkv + g];
+  }
 }
 
 static double orc_load_q(const void* q, size_t idx, int dtype) {
@@ -212,18 +235,24 @@ void orc_cache_write(void* k_cache, void* v_cache, int dtype, int num_blocks, in
  * element of physical block src = pairs[2i] (all KV heads, K and V) into
  * block dst = pairs[2i+1], and the per-(block, head) scales when given.
  * Pairs are applied in order; ids outside [0, num_blocks) are skipped.       */
-void orc_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int dtype,
-                     int num_blocks, int Hkv, int bs, int D, const int32_t* pairs, int n) {
+void orc_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                     uint8_t* k_zero, uint8_t* v_zero, int dtype, int num_blocks, int Hkv, int bs,
+                     int D, const int32_t* pairs, int n) {
   size_t eb = orc_elem_bytes(dtype);
   size_t blk = (size_t)Hkv * bs * D * eb;
+  /* parameters per block: one scale per head, or (asymmetric) one scale and
+   * one zero point per (head, row)                                           */
+  size_t np = dtype == ORC_U8Z ? (size_t)Hkv * bs : (size_t)Hkv;
   for (int i = 0; i < n; ++i) {
     int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
     memmove((char*)k_cache + (size_t)dst * blk, (const char*)k_cache + (size_t)src * blk, blk);
     memmove((char*)v_cache + (size_t)dst * blk, (const char*)v_cache + (size_t)src * blk, blk);
-    for (int g = 0; g < Hkv; ++g) {
-      if (k_scale) k_scale[(size_t)dst * Hkv + g] = k_scale[(size_t)src * Hkv + g];
-      if (v_scale) v_scale[(size_t)dst * Hkv + g] = v_scale[(size_t)src * Hkv + g];
+    for (size_t j = 0; j < np; ++j) {
+      if (k_scale) k_scale[(size_t)dst * np + j] = k_scale[(size_t)src * np + j];
+      if (v_scale) v_scale[(size_t)dst * np + j] = v_scale[(size_t)src * np + j];
+      if (k_zero) k_zero[(size_t)dst * np + j] = k_zero[(size_t)src * np + j];
+      if (v_zero) v_zero[(size_t)dst * np + j] = v_zero[(size_t)src * np + j];
     }
   }
 }
@@ -257,7 +286,8 @@ void orc_gather(const void* k_cache, const void* v_cache, int dtype, int Hkv, in
  * o = 0.  Tokens are visited in logical order through the block table.      */
 static void orc_attend_range(const void* q, int q_dtype, const void* k_cache,
                              const void* v_cache, int kv_dtype, const float* k_scale,
-                             const float* v_scale, const int32_t* block_tables, int max_blocks,
+                             const float* v_scale, const uint8_t* k_zero, const uint8_t* v_zero,
+                             const int32_t* block_tables, int max_blocks,
                              int s, int h, int Hq, int Hkv, int D, int bs, double scale, int t0,
                              int t1, size_t qrow, double* logits, double* m_out, double* l_out,
                              double* o_out) {
@@ -277,10 +307,12 @@ static void orc_attend_range(const void* q, int q_dtype, const void* k_cache,
   for (int t = t0; t < t1; ++t) {
     int32_t b = block_tables[(size_t)s * max_blocks + t / bs];
     size_t base = orc_pool_offset((size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs, D);
-    double ks = k_scale ? (double)k_scale[(size_t)b * Hkv + g] : 1.0;
-    double dot = 0.0;
+    double ks, kz, dot = 0.0;
+    orc_row_params(kv_dtype, k_scale, k_zero, (size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs,
+                   &ks, &kz);
     for (int d = 0; d < D; ++d)
-      dot += orc_load_q(q, qrow + d, q_dtype) * orc_load_elem(k_cache, base + d, kv_dtype, ks);
+      dot += orc_load_q(q, qrow + d, q_dtype) *
+             orc_load_elem(k_cache, base + d, kv_dtype, ks, kz);
     logits[t - t0] = scale * dot;
   }
   /* softmax with the maximum subtracted, then the weighted sum of V rows    */
@@ -289,10 +321,12 @@ static void orc_attend_range(const void* q, int q_dtype, const void* k_cache,
   for (int t = t0; t < t1; ++t) {
     int32_t b = block_tables[(size_t)s * max_blocks + t / bs];
     size_t base = orc_pool_offset((size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs, D);
-    double vs = v_scale ? (double)v_scale[(size_t)b * Hkv + g] : 1.0;
-    double w = exp(logits[t - t0] - m);
+    double vs, vz, w = exp(logits[t - t0] - m);
+    orc_row_params(kv_dtype, v_scale, v_zero, (size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs,
+                   &vs, &vz);
     l += w;
-    for (int d = 0; d < D; ++d) o_out[d] += w * orc_load_elem(v_cache, base + d, kv_dtype, vs);
+    for (int d = 0; d < D; ++d)
+      o_out[d] += w * orc_load_elem(v_cache, base + d, kv_dtype, vs, vz);
   }
   for (int d = 0; d < D; ++d) o_out[d] /= l;
   *m_out = m;
@@ -308,9 +342,10 @@ static void orc_attend_range(const void* q, int q_dtype, const void* k_cache,
  * out is double [num_seqs][Hq][D].  Rows (s, h) are independent; OpenMP
  * spreads them over threads without changing any row's arithmetic.         */
 int orc_decode(const void* q, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
-               const float* k_scale, const float* v_scale, const int32_t* block_tables,
-               int max_blocks, const int32_t* context_lens, int num_seqs, int Hq, int Hkv, int D,
-               int bs, float scale, double* out) {
+               const float* k_scale, const float* v_scale, const uint8_t* k_zero,
+               const uint8_t* v_zero, const int32_t* block_tables, int max_blocks,
+               const int32_t* context_lens, int num_seqs, int Hq, int Hkv, int D, int bs,
+               float scale, double* out) {
   int max_len = 0;
   int fail = 0;
   for (int s = 0; s < num_seqs; ++s)
@@ -325,7 +360,8 @@ int orc_decode(const void* q, int q_dtype, const void* k_cache, const void* v_ca
       for (long r = 0; r < (long)num_seqs * Hq; ++r) {
         int s = (int)(r / Hq), h = (int)(r % Hq);
         double m, l;
-        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, k_zero,
+                         v_zero, block_tables,
                          max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, context_lens[s],
                          ((size_t)s * Hq + h) * (size_t)D, logits, &m, &l, out + (size_t)r * D);
       }
@@ -338,9 +374,9 @@ int orc_decode(const void* q, int q_dtype, const void* k_cache, const void* v_ca
 /* Decode for a subset of rows: rows[i] = s * Hq + h.  out is [n_rows][D].   */
 int orc_decode_rows(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
                     int kv_dtype, const float* k_scale, const float* v_scale,
-                    const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
-                    int num_seqs, int Hq, int Hkv, int D, int bs, float scale, const int64_t* rows,
-                    int n_rows, double* out) {
+                    const uint8_t* k_zero, const uint8_t* v_zero, const int32_t* block_tables,
+                    int max_blocks, const int32_t* context_lens, int num_seqs, int Hq, int Hkv,
+                    int D, int bs, float scale, const int64_t* rows, int n_rows, double* out) {
   int max_len = 0, fail = 0;
   for (int s = 0; s < num_seqs; ++s)
     if (context_lens[s] > max_len) max_len = context_lens[s];
@@ -354,7 +390,8 @@ int orc_decode_rows(const void* q, int q_dtype, const void* k_cache, const void*
       for (int i = 0; i < n_rows; ++i) {
         int s = (int)(rows[i] / Hq), h = (int)(rows[i] % Hq);
         double m, l;
-        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, k_zero,
+                         v_zero, block_tables,
                          max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, context_lens[s],
                          ((size_t)s * Hq + h) * (size_t)D, logits, &m, &l, out + (size_t)i * D);
       }
@@ -374,9 +411,9 @@ int orc_decode_rows(const void* q, int q_dtype, const void* k_cache, const void*
  * [num_seqs][ntok][Hq][D]; a query token with p < 0 gets a zero row.         */
 int orc_decode_multi(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
                      int kv_dtype, const float* k_scale, const float* v_scale,
-                     const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
-                     int num_seqs, int ntok, int Hq, int Hkv, int D, int bs, float scale,
-                     double* out) {
+                     const uint8_t* k_zero, const uint8_t* v_zero, const int32_t* block_tables,
+                     int max_blocks, const int32_t* context_lens, int num_seqs, int ntok, int Hq,
+                     int Hkv, int D, int bs, float scale, double* out) {
   int max_len = 0, fail = 0;
   for (int s = 0; s < num_seqs; ++s)
     if (context_lens[s] > max_len) max_len = context_lens[s];
@@ -392,7 +429,8 @@ int orc_decode_multi(const void* q, int q_dtype, const void* k_cache, const void
         int i = (int)((r / Hq) % ntok), h = (int)(r % Hq);
         int p = context_lens[s] - ntok + i;
         double m, l;
-        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_tables,
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, k_zero,
+                         v_zero, block_tables,
                          max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, 0, p + 1 > 0 ? p + 1 : 0,
                          (size_t)r * D, logits, &m, &l, out + (size_t)r * D);
       }
@@ -423,6 +461,7 @@ void orc_slot_mapping_tokens(const int32_t* block_tables, int max_blocks,
  * [num_seqs][Hq][P][D] with P = n_parts.                                    */
 int orc_decode_partials(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
                         int kv_dtype, const float* k_scale, const float* v_scale,
+                        const uint8_t* k_zero, const uint8_t* v_zero,
                         const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
                         int num_seqs, int Hq, int Hkv, int D, int bs, float scale, int part,
                         int n_parts, double* m_out, double* l_out, double* o_out) {
@@ -442,7 +481,7 @@ int orc_decode_partials(const void* q, int q_dtype, const void* k_cache, const v
           int t1 = (p + 1) * part < L ? (p + 1) * part : L;
           size_t i = (size_t)r * n_parts + p;
           orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
-                           block_tables, max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, t0,
+                           k_zero, v_zero, block_tables, max_blocks, s, h, Hq, Hkv, D, bs, (double)scale, t0,
                            t1, ((size_t)s * Hq + h) * (size_t)D, logits, &m_out[i], &l_out[i],
                            o_out + i * D);
         }
@@ -500,14 +539,14 @@ int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, flo
     size_t cnt = (size_t)bs * D;
     float a = 0.0f, sc;
     for (size_t i = 0; i < cnt; ++i) {
-      float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0);
+      float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0, 0.0);
       float ax = fabsf(x);
       if (ax > a) a = ax;
     }
     sc = (dst_dtype == ORC_I8) ? a / 127.0f : a / 448.0f;
     scales[(size_t)b * Hkv + g] = sc;
     for (size_t i = 0; i < cnt; ++i) {
-      float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0);
+      float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0, 0.0);
       if (dst_dtype == ORC_I8) {
         float r = (a == 0.0f) ? 0.0f : rintf(x / sc);
         if (r > 127.0f) r = 127.0f;
@@ -518,5 +557,113 @@ int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, flo
       }
     }
   }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Asymmetric uint8 quantization of one row of n values, [MGMT] section 四,
+ * KVQuantizationCache.quantize_key with per_channel on: the minimum and the
+ * maximum are taken along the last (head_dim) axis, so every (head, token)
+ * row gets its own parameters:
+ *   scale      = (max - min) / 255
+ *   zero_point = clamp(round(-min / scale), 0, 255)
+ *   code       = clamp(round((x - min) / scale), 0, 255)
+ * and dequantize_key restores (code - zero_point) * scale.  The page computes
+ * in the tensor's own 16-bit type; here every step is a binary32 operation
+ * (the stored scale's type), and round is to nearest, ties to even, as
+ * torch.round does.  A row whose values are all equal has scale 0, where the
+ * page's divisions are undefined: it is stored as scale 0, zero point 0 and
+ * codes 0.  Note the page's clamp of the zero point: a row with no negative
+ * value gets zero point 0 and restores as about x - min.                    */
+void orc_quantize_row_asym(const float* x, int n, uint8_t* codes, float* scale_out,
+                           uint8_t* zero_out) {
+  float mn = x[0], mx = x[0], sc;
+  for (int i = 1; i < n; ++i) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  sc = (mx - mn) / 255.0f;
+  if (sc == 0.0f) {
+    *scale_out = 0.0f;
+    *zero_out = 0;
+    for (int i = 0; i < n; ++i) codes[i] = 0;
+    return;
+  }
+  {
+    float z = rintf(-mn / sc);
+    if (z < 0.0f) z = 0.0f;
+    if (z > 255.0f) z = 255.0f;
+    *scale_out = sc;
+    *zero_out = (uint8_t)z;
+  }
+  for (int i = 0; i < n; ++i) {
+    float c = rintf((x[i] - mn) / sc);
+    if (c < 0.0f) c = 0.0f;
+    if (c > 255.0f) c = 255.0f;
+    codes[i] = (uint8_t)c;
+  }
+}
+
+/* Per-row asymmetric quantization of a pool (F32 or BF16 source) into codes
+ * [num_blocks][Hkv][bs][D] and parameters scales, zeros [num_blocks][Hkv][bs].
+ * block_ids == NULL means every block.                                      */
+int orc_quantize_asym(const void* src, int src_dtype, uint8_t* codes, float* scales,
+                      uint8_t* zeros, int num_blocks, int Hkv, int bs, int D,
+                      const int32_t* block_ids, int n_ids) {
+  int n = block_ids ? n_ids : num_blocks;
+  int fail = 0;
+  if (src_dtype != ORC_F32 && src_dtype != ORC_BF16) return -1;
+#pragma omp parallel reduction(| : fail)
+  {
+    float* row = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!row) {
+      fail = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (long it = 0; it < (long)n * Hkv * bs; ++it) {
+        int b = block_ids ? block_ids[it / ((long)Hkv * bs)] : (int)(it / ((long)Hkv * bs));
+        int g = (int)((it / bs) % Hkv), o = (int)(it % bs);
+        size_t base = orc_pool_offset((size_t)b, (size_t)g, (size_t)o, Hkv, bs, D);
+        size_t r = ((size_t)b * Hkv + g) * (size_t)bs + (size_t)o;
+        for (int d = 0; d < D; ++d) row[d] = (float)orc_load_elem(src, base + d, src_dtype, 1.0, 0.0);
+        orc_quantize_row_asym(row, D, codes + base, scales + r, zeros + r);
+      }
+      free(row);
+    }
+  }
+  return fail ? -1 : 0;
+}
+
+/* Quantized append: the cache write of [KVC] "KV Cache 的本质" into an
+ * asymmetric per-row pool.  Token i's K and V rows of head g (F32 or BF16
+ * values in k_new, v_new [n][Hkv][D]) are quantized row by row as above and
+ * stored at slot slot_mapping[i] (negative = skip) with their parameters;
+ * because every row has its own scale and zero point, no other row of the
+ * block changes.                                                            */
+int orc_cache_write_quant(uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
+                          uint8_t* k_zero, uint8_t* v_zero, int Hkv, int bs, int D,
+                          const void* k_new, const void* v_new, int src_dtype,
+                          const int32_t* slot_mapping, int n) {
+  float* row = (float*)malloc(sizeof(float) * (size_t)D);
+  if (!row) return -1;
+  if (src_dtype != ORC_F32 && src_dtype != ORC_BF16) {
+    free(row);
+    return -1;
+  }
+  for (int i = 0; i < n; ++i) {
+    int32_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    for (int g = 0; g < Hkv; ++g) {
+      size_t b = (size_t)(slot / bs), o = (size_t)(slot % bs);
+      size_t dst = orc_pool_offset(b, (size_t)g, o, Hkv, bs, D);
+      size_t r = (b * Hkv + g) * (size_t)bs + o;
+      size_t src = ((size_t)i * Hkv + g) * (size_t)D;
+      for (int d = 0; d < D; ++d) row[d] = (float)orc_load_elem(k_new, src + d, src_dtype, 1.0, 0.0);
+      orc_quantize_row_asym(row, D, k_cache + dst, k_scale + r, k_zero + r);
+      for (int d = 0; d < D; ++d) row[d] = (float)orc_load_elem(v_new, src + d, src_dtype, 1.0, 0.0);
+      orc_quantize_row_asym(row, D, v_cache + dst, v_scale + r, v_zero + r);
+    }
+  }
+  free(row);
   return 0;
 }
