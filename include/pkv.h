@@ -29,7 +29,8 @@
  *          二 (KVCacheBlock stores [heads][block_size][head_dim]; append_slot
  *          takes logical block token_idx // block_size; allocation failure is
  *          a return value), section 四 (KV stored as 8-bit codes, restored as
- *          code * scale).
+ *          code * scale; KVQuantizationCache: asymmetric uint8 codes with a
+ *          scale and a zero point per (head, token) row).
  */
 #ifndef PKV_H
 #define PKV_H
@@ -59,7 +60,9 @@ enum {
   PKV_F32 = 0,      /* IEEE binary32                                            */
   PKV_BF16 = 1,     /* bfloat16 (upper half of binary32)                        */
   PKV_I8 = 2,       /* int8 code, value = code * scale                          */
-  PKV_FP8_E4M3 = 3  /* OCP E4M3 "fn" code (bias 7, max 448, no inf), value = decoded * scale */
+  PKV_FP8_E4M3 = 3, /* OCP E4M3 "fn" code (bias 7, max 448, no inf), value = decoded * scale */
+  PKV_U8_ZP = 4     /* uint8 code with a binary32 scale and a uint8 zero point per
+                       (block, KV head, row): value = (code - zero) * scale */
 };
 
 #define PKV_BLOCK_SIZE 16
@@ -87,7 +90,11 @@ enum {
  *     block_size * head_dim, with block_stride * element size a multiple of
  *     16 bytes; the K and V regions of all blocks must not overlap.
  *   k_scale, v_scale: [num_blocks][num_kv_heads] binary32 scales, required for
- *     PKV_I8 / PKV_FP8_E4M3 and ignored otherwise.
+ *     PKV_I8 / PKV_FP8_E4M3; for PKV_U8_ZP [num_blocks][num_kv_heads][block_size]
+ *     (one per row); ignored for float pools.
+ *   k_zero, v_zero: [num_blocks][num_kv_heads][block_size] uint8 zero points,
+ *     required for PKV_U8_ZP and ignored otherwise.  Scales and zero points are
+ *     dense arrays whatever block_stride is.
  * block_size must be 16 ([KVC] "PagedAttention"); head_dim must be 64 or 128. */
 typedef struct pkv_cache_t {
   int32_t num_blocks;
@@ -100,6 +107,8 @@ typedef struct pkv_cache_t {
   float* k_scale;
   float* v_scale;
   int64_t block_stride;
+  uint8_t* k_zero;
+  uint8_t* v_zero;
 } pkv_cache_t;
 
 /* Human-readable text for a status code (static storage). */
@@ -140,10 +149,30 @@ int pkv_slot_mapping_tokens(const int32_t* block_tables, int32_t max_blocks_per_
  * KV head g, for every g.  Bit-exact copy.
  *   k, v: device [n][num_kv_heads][head_dim] of cache->kv_dtype
  *   slot_mapping: device int32 [n]; negative = skip; slots must be distinct.
- * kv_dtype must be PKV_F32 or PKV_BF16 (appending into an 8-bit cache is
- * PKV_ERR_UNSUPPORTED: quantize whole blocks with pkv_quantize instead). */
+ * kv_dtype must be PKV_F32 or PKV_BF16 (for PKV_U8_ZP use
+ * pkv_cache_write_quant; appending into a PKV_I8 / PKV_FP8_E4M3 pool is
+ * PKV_ERR_UNSUPPORTED, since one new row would change its block's scale:
+ * quantize whole blocks with pkv_quantize instead). */
 int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
                     const int32_t* slot_mapping, int32_t n, void* stream);
+
+/* Quantized append ([KVC] "KV Cache 的本质": each step appends the new token's
+ * K and V; [MGMT] section 四, KVQuantizationCache.quantize_key with per-channel
+ * parameters): for i < n with slot = slot_mapping[i] in range, each KV head's
+ * row k[i][g][:] (and v[i][g][:]) is quantized on its own,
+ *   scale = (max - min) / 255, zero = clamp(rint(-min / scale), 0, 255),
+ *   code  = clamp(rint((x - min) / scale), 0, 255),
+ * every step a binary32 operation rounding to nearest even; a row whose values
+ * are all equal is stored as scale 0, zero 0, codes 0.  The codes go to row
+ * slot % 16 of block slot / 16 and the scale and zero point to the same row
+ * of k_scale / k_zero (v_scale / v_zero); no other row changes.  Bit-exact
+ * with pkv_quantize of the same values.
+ *   cache: kv_dtype PKV_U8_ZP
+ *   k, v: device [n][num_kv_heads][head_dim] of src_dtype (PKV_F32 or PKV_BF16)
+ *   slot_mapping: device int32 [n]; negative = skip; slots must be distinct. */
+int pkv_cache_write_quant(const pkv_cache_t* cache, const void* k, const void* v,
+                          int32_t src_dtype, const int32_t* slot_mapping, int32_t n,
+                          void* stream);
 
 /* Workspace bytes pkv_attention_decode / pkv_decode_step need for the given
  * split: per (sequence, query head) and partial slot a running maximum, a sum
@@ -186,7 +215,10 @@ int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
  *     that is nonzero (contents need not be initialised), else may be NULL
  *   out: device [num_seqs][num_q_heads][head_dim] of out_dtype.
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8),
- * (BF16, FP8_E4M3); out_dtype F32 or BF16 (bf16 rounded to nearest even). */
+ * (BF16, FP8_E4M3), (BF16, U8_ZP); out_dtype F32 or BF16 (bf16 rounded to
+ * nearest even).  8-bit pools are restored as code * scale (I8, FP8_E4M3) or
+ * (code - zero) * scale (U8_ZP) on the fly; rows past L are never used, so
+ * their codes and parameters may hold anything. */
 int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -201,7 +233,9 @@ int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
  * pkv_attention_decode, and leaves the pool in the same state.
  *   k, v: device [num_seqs][num_kv_heads][head_dim] of cache->kv_dtype (the
  *     new token of each sequence; ignored for sequences with length 0)
- * kv_dtype must be PKV_F32 or PKV_BF16; other arguments as for
+ * kv_dtype must be PKV_F32, PKV_BF16 or PKV_U8_ZP; for PKV_U8_ZP, k and v are
+ * of q_dtype and are quantized as pkv_cache_write_quant does, by a launch of
+ * its own before the attention.  Other arguments as for
  * pkv_attention_decode.  Tables must not map the new token's slot of two
  * sequences to the same physical row. */
 int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, const void* k,
@@ -240,10 +274,15 @@ int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype
  *   PKV_I8:       scale = a / 127, code = clamp(rint(x / scale), -127, 127)
  *   PKV_FP8_E4M3: scale = a / 448, code = nearest E4M3 (ties to even), values
  *                 beyond 448 in magnitude saturate to +-448
- * a == 0 gives scale 0 and zero codes.  Divisions and rounding are binary32,
- * round-to-nearest-even.  Quantizes src->k_cache into dst->k_cache (scales to
- * dst->k_scale) and src->v_cache into dst->v_cache (dst->v_scale).
- *   src: kv_dtype F32 or BF16; dst: kv_dtype I8 or FP8_E4M3, same geometry
+ * a == 0 gives scale 0 and zero codes.  With dst PKV_U8_ZP ([MGMT] section 四,
+ * KVQuantizationCache with per-channel parameters) every (block, head, row) of
+ * head_dim values is quantized on its own, as pkv_cache_write_quant states,
+ * and its scale and zero point go to that row of the parameter arrays.
+ * Divisions and rounding are binary32, round-to-nearest-even.  Quantizes
+ * src->k_cache into dst->k_cache (scales to dst->k_scale, zero points to
+ * dst->k_zero) and src->v_cache into dst->v_cache (dst->v_scale, v_zero).
+ *   src: kv_dtype F32 or BF16; dst: kv_dtype I8, FP8_E4M3 or U8_ZP, same
+ *   geometry
  *   block_ids: device int32 [n_ids], or NULL for every block (n_ids ignored). */
 int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,
                  int32_t n_ids, void* stream);
@@ -254,7 +293,7 @@ int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* 
  * sharing": shared blocks are reference-counted and copied on write).  For
  * each i < n with (src, dst) = (pairs[2i], pairs[2i+1]): every KV head's K and
  * V tile of block dst becomes a bit-exact copy of block src's, and for 8-bit
- * pools k_scale / v_scale rows too.
+ * pools the block's scales (and zero points) too.
  *   pairs: device int32 [n][2]; a pair with an id outside [0, num_blocks) is
  *     skipped.  Destinations must be distinct and no destination may also be
  *     a source (the result would depend on the order of the copies).

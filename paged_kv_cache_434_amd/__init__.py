@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 SPLIT_BALANCED = -1     # partition_tokens value: balanced split (PKV_SPLIT_BALANCED)
-DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3}
+DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "u8z": 4}
 BLOCK_SIZE = 16
 
 _lib = None
@@ -43,6 +43,8 @@ class CacheDesc(ctypes.Structure):
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
         ("block_stride", ctypes.c_int64),
+        ("k_zero", ctypes.c_void_p),
+        ("v_zero", ctypes.c_void_p),
     ]
 
 
@@ -62,6 +64,7 @@ def _load():
             "pkv_slot_mapping": (ctypes.c_int, [P, I32, P, I32, P, P]),
             "pkv_slot_mapping_tokens": (ctypes.c_int, [P, I32, P, I32, I32, P, P]),
             "pkv_cache_write": (ctypes.c_int, [C, P, P, P, I32, P]),
+            "pkv_cache_write_quant": (ctypes.c_int, [C, P, P, I32, P, I32, P]),
             "pkv_decode_workspace_bytes": (ctypes.c_size_t, [I32, I32, I32, I32, I32]),
             "pkv_decode_default_partition": (I32, [I32, I32, I32]),
             "pkv_attention_decode": (ctypes.c_int, [C, P, I32, P, I32, P, I32, I32, F, I32, P,
@@ -91,7 +94,7 @@ def lib():
 
 EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_mapping",
                     "pkv_slot_mapping_tokens", "pkv_attention_multi",
-                    "pkv_cache_write", "pkv_decode_workspace_bytes",
+                    "pkv_cache_write", "pkv_cache_write_quant", "pkv_decode_workspace_bytes",
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
                     "pkv_quantize", "pkv_copy_blocks",
                     "pkv_gather", "pkv_validate_tables")
@@ -110,7 +113,7 @@ def _torch():
 def _storage_dtype(name: str):
     torch = _torch()
     return {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8,
-            "fp8": torch.uint8}[name]
+            "fp8": torch.uint8, "u8z": torch.uint8}[name]
 
 
 def _ptr(t) -> Optional[int]:
@@ -136,14 +139,17 @@ def _need(t, name, dtype=None, ndim=None):
 
 
 class PagedCache:
-    """One layer's K and V pools and, for 8-bit pools, their [num_blocks][Hkv]
-    binary32 scales.  ``k_cache`` / ``v_cache`` are [num_blocks][Hkv][16][D]
-    tensors whose last three dimensions are dense; the block dimension may be
-    strided, so both separate dense pools and the two halves of one
-    [num_blocks][2][Hkv][16][D] allocation (see ``from_blocks``) are accepted.
-    Holds references so the tensors outlive the descriptor."""
+    """One layer's K and V pools and, for 8-bit pools, their binary32 scales:
+    [num_blocks][Hkv] for ``i8`` / ``fp8``, [num_blocks][Hkv][16] plus uint8
+    zero points of the same shape for ``u8z`` (the asymmetric per-row format).
+    ``k_cache`` / ``v_cache`` are [num_blocks][Hkv][16][D] tensors whose last
+    three dimensions are dense; the block dimension may be strided, so both
+    separate dense pools and the two halves of one [num_blocks][2][Hkv][16][D]
+    allocation (see ``from_blocks``) are accepted.  Holds references so the
+    tensors outlive the descriptor."""
 
-    def __init__(self, k_cache, v_cache, kv_dtype: str, k_scale=None, v_scale=None):
+    def __init__(self, k_cache, v_cache, kv_dtype: str, k_scale=None, v_scale=None,
+                 k_zero=None, v_zero=None):
         torch = _torch()
         sd = _storage_dtype(kv_dtype)
         if kv_dtype == "fp8" and k_cache.dtype == torch.float8_e4m3fn:
@@ -160,20 +166,34 @@ class PagedCache:
                 raise ValueError(f"{name}: the last three dimensions must be dense")
         if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
             raise ValueError("k_cache and v_cache shapes or strides differ")
+        NB, Hkv, bs, D = k_cache.shape
         if kv_dtype in ("i8", "fp8"):
             _need(k_scale, "k_scale", torch.float32, 2)
             _need(v_scale, "v_scale", torch.float32, 2)
-        NB, Hkv, bs, D = k_cache.shape
+            if tuple(k_scale.shape) != (NB, Hkv) or k_scale.shape != v_scale.shape:
+                raise ValueError("k_scale/v_scale must be [num_blocks][num_kv_heads]")
+        if kv_dtype == "u8z":
+            for name, t, dt in (("k_scale", k_scale, torch.float32),
+                                ("v_scale", v_scale, torch.float32),
+                                ("k_zero", k_zero, torch.uint8), ("v_zero", v_zero, torch.uint8)):
+                _need(t, name, dt, 3)
+                if tuple(t.shape) != (NB, Hkv, bs):
+                    raise ValueError(f"{name} must be [num_blocks][num_kv_heads][block_size]")
+        else:
+            k_zero = v_zero = None
         stride = int(k_cache.stride(0))
         self.block_stride = 0 if stride == Hkv * bs * D else stride
         self.k_cache, self.v_cache, self.k_scale, self.v_scale = k_cache, v_cache, k_scale, v_scale
+        self.k_zero, self.v_zero = k_zero, v_zero
         self.kv_dtype = kv_dtype
         self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = NB, Hkv, bs, D
         self.desc = CacheDesc(NB, Hkv, bs, D, DTYPE_CODES[kv_dtype], k_cache.data_ptr(),
-                              v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), self.block_stride)
+                              v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), self.block_stride,
+                              _ptr(k_zero), _ptr(v_zero))
 
     @classmethod
-    def from_blocks(cls, kv, kv_dtype: str, k_scale=None, v_scale=None):
+    def from_blocks(cls, kv, kv_dtype: str, k_scale=None, v_scale=None, k_zero=None,
+                    v_zero=None):
         """A pool held as one [num_blocks][2][Hkv][16][D] tensor: each block
         holds every head's K, then every head's V."""
         torch = _torch()
@@ -182,7 +202,7 @@ class PagedCache:
         _need(kv, "kv", _storage_dtype(kv_dtype), 5)
         if kv.shape[1] != 2:
             raise ValueError("kv must be [num_blocks][2][num_kv_heads][block_size][head_dim]")
-        return cls(kv[:, 0], kv[:, 1], kv_dtype, k_scale, v_scale)
+        return cls(kv[:, 0], kv[:, 1], kv_dtype, k_scale, v_scale, k_zero, v_zero)
 
 
 def pool_bytes(num_blocks, num_kv_heads, head_dim, dtype, block_size=BLOCK_SIZE) -> int:
@@ -234,6 +254,26 @@ def cache_write(cache: PagedCache, k, v, slot_mapping, stream=None):
                                    _ptr(slot_mapping), n, _stream(stream)))
 
 
+def cache_write_quant(cache: PagedCache, k, v, slot_mapping, stream=None):
+    """Quantized append into a ``u8z`` pool: every new (token, head) row of k
+    and v (float32 or bfloat16 [n][Hkv][D]) is quantized on its own and stored
+    with its scale and zero point at its slot."""
+    torch = _torch()
+    sd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(k.dtype)
+    if sd is None:
+        raise TypeError("k must be float32 or bfloat16")
+    _need(k, "k", k.dtype, 3)
+    _need(v, "v", k.dtype, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    n = slot_mapping.shape[0]
+    if tuple(k.shape) != (n, cache.num_kv_heads, cache.head_dim) or k.shape != v.shape:
+        raise ValueError("k/v must be [n][num_kv_heads][head_dim]")
+    _check("pkv_cache_write_quant",
+           _load().pkv_cache_write_quant(ctypes.byref(cache.desc), _ptr(k), _ptr(v),
+                                         DTYPE_CODES[sd], _ptr(slot_mapping), n,
+                                         _stream(stream)))
+
+
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                            partition_tokens) -> int:
     return int(_load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
@@ -267,7 +307,8 @@ def _decode_call(cache: PagedCache, q, block_tables, context_lens, scale: float,
     if context_lens.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("q, block_tables and context_lens disagree on the batch size")
     if append is not None:
-        sd = _storage_dtype(cache.kv_dtype)
+        # new rows for a u8z pool come in q's dtype and are quantized on append
+        sd = q.dtype if cache.kv_dtype == "u8z" else _storage_dtype(cache.kv_dtype)
         k_new, v_new = append
         _need(k_new, "k_new", sd, 3)
         _need(v_new, "v_new", sd, 3)

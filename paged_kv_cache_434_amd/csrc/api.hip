@@ -20,8 +20,13 @@ int check_cache(const pkv_cache_t* c) {
     return PKV_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!c->k_cache || !c->v_cache) return PKV_ERR_NULL;
-  if ((c->kv_dtype == PKV_I8 || c->kv_dtype == PKV_FP8_E4M3) && (!c->k_scale || !c->v_scale))
-    return PKV_ERR_NULL;
+  if (is_q8(c->kv_dtype) && (!c->k_scale || !c->v_scale)) return PKV_ERR_NULL;
+  if (c->kv_dtype == PKV_U8_ZP) {
+    if (!c->k_zero || !c->v_zero) return PKV_ERR_NULL;
+    // zero points are read four rows per 32-bit load
+    if ((reinterpret_cast<uintptr_t>(c->k_zero) & 3u) || (reinterpret_cast<uintptr_t>(c->v_zero) & 3u))
+      return PKV_ERR_UNSUPPORTED;
+  }
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_UNSUPPORTED;
   if (c->block_stride != 0) {
     if (c->block_stride < block_elems(*c)) return PKV_ERR_SHAPE;
@@ -98,6 +103,22 @@ int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
   return launch_cache_write(*cache, k, v, slot_mapping, n, static_cast<hipStream_t>(stream));
 }
 
+int pkv_cache_write_quant(const pkv_cache_t* cache, const void* k, const void* v,
+                          int32_t src_dtype, const int32_t* slot_mapping, int32_t n,
+                          void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  if (cache->kv_dtype != PKV_U8_ZP || (src_dtype != PKV_F32 && src_dtype != PKV_BF16))
+    return PKV_ERR_DTYPE;
+  if (n < 0) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)n * cache->num_kv_heads > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
+  return launch_cache_write_quant(*cache, k, v, src_dtype, slot_mapping, nullptr, 0, nullptr, n,
+                                  static_cast<hipStream_t>(stream));
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_tokens) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
@@ -128,8 +149,7 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
     return PKV_ERR_DTYPE;
   const int kv = cache->kv_dtype;
   const bool pair_ok = (q_dtype == PKV_F32 && kv == PKV_F32) ||
-                       (q_dtype == PKV_BF16 &&
-                        (kv == PKV_BF16 || kv == PKV_I8 || kv == PKV_FP8_E4M3));
+                       (q_dtype == PKV_BF16 && (kv == PKV_BF16 || is_q8(kv)));
   if (!pair_ok) return PKV_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || !split_ok(partition_tokens) ||
       max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
@@ -141,7 +161,7 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   if ((int64_t)num_seqs * ntok * num_q_heads > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (append) {
-    if (cache->kv_dtype != PKV_F32 && cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (kv != PKV_F32 && kv != PKV_BF16 && kv != PKV_U8_ZP) return PKV_ERR_UNSUPPORTED;
     if (!k_new || !v_new) return PKV_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_UNSUPPORTED;
   }
@@ -157,11 +177,20 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
   }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // asymmetric per-row pools: the new rows are quantized and stored by a
+  // launch of their own, then the attention reads them from the pool
+  const bool fused = append && kv != PKV_U8_ZP;
+  if (append && !fused) {
+    rc = launch_cache_write_quant(*cache, k_new, v_new, q_dtype, nullptr, block_tables,
+                                  max_blocks_per_seq, context_lens, num_seqs, st);
+    if (rc != PKV_OK) return rc;
+  }
   DecodeArgs a{cache,     q,          q_dtype,   block_tables,     max_blocks_per_seq,
                context_lens, num_seqs, num_q_heads, scale,          partition_tokens,
-               workspace, out,        out_dtype, append ? k_new : nullptr,
-               append ? v_new : nullptr, ntok};
-  return launch_decode(a, static_cast<hipStream_t>(stream));
+               workspace, out,        out_dtype, fused ? k_new : nullptr,
+               fused ? v_new : nullptr, ntok};
+  return launch_decode(a, st);
 }
 
 int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
@@ -201,8 +230,7 @@ int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* 
   if (rc != PKV_OK) return rc;
   rc = check_cache(dst);
   if (rc != PKV_OK) return rc;
-  if ((src->kv_dtype != PKV_F32 && src->kv_dtype != PKV_BF16) ||
-      (dst->kv_dtype != PKV_I8 && dst->kv_dtype != PKV_FP8_E4M3))
+  if ((src->kv_dtype != PKV_F32 && src->kv_dtype != PKV_BF16) || !is_q8(dst->kv_dtype))
     return PKV_ERR_DTYPE;
   if (src->num_blocks != dst->num_blocks || src->num_kv_heads != dst->num_kv_heads ||
       src->head_dim != dst->head_dim)

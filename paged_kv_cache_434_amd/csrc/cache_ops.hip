@@ -83,12 +83,14 @@ __global__ void gather_kernel(const uint8_t* __restrict__ kc, const uint8_t* __r
 
 // Copy-on-write block copy: one workgroup per (pair, K or V); the block's
 // every-head region (blk_bytes) is moved in 16-byte pieces, consecutive
-// threads on consecutive addresses; the K workgroup also copies the K scales
-// and the V workgroup the V scales of 8-bit pools.
+// threads on consecutive addresses; the K workgroup also copies the block's
+// K parameters and the V workgroup its V parameters: n_par scales (and zero
+// points) per block, one per head or one per (head, row).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
-    float* __restrict__ vs, const int32_t* __restrict__ pairs, int num_blocks, int hkv,
-    size_t stride_bytes, int blk_chunks) {
+    float* __restrict__ vs, uint8_t* __restrict__ kz, uint8_t* __restrict__ vz,
+    const int32_t* __restrict__ pairs, int num_blocks, int n_par, size_t stride_bytes,
+    int blk_chunks) {
   const int i = blockIdx.x;
   const bool is_v = blockIdx.y != 0;
   const int src = pairs[2 * i], dst = pairs[2 * i + 1];
@@ -98,19 +100,24 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   uint4* to = reinterpret_cast<uint4*>(base + (size_t)dst * stride_bytes);
   for (int c = threadIdx.x; c < blk_chunks; c += blockDim.x) to[c] = from[c];
   float* sc = is_v ? vs : ks;
-  if (sc != nullptr && (int)threadIdx.x < hkv)
-    sc[(size_t)dst * hkv + threadIdx.x] = sc[(size_t)src * hkv + threadIdx.x];
+  uint8_t* zp = is_v ? vz : kz;
+  for (int j = threadIdx.x; sc != nullptr && j < n_par; j += blockDim.x) {
+    sc[(size_t)dst * n_par + j] = sc[(size_t)src * n_par + j];
+    if (zp != nullptr) zp[(size_t)dst * n_par + j] = zp[(size_t)src * n_par + j];
+  }
 }
 
 }  // namespace
 
 int launch_copy_blocks(const pkv_cache_t& c, const int32_t* pairs, int n, hipStream_t st) {
-  const bool q8 = c.kv_dtype == PKV_I8 || c.kv_dtype == PKV_FP8_E4M3;
+  const bool q8 = is_q8(c.kv_dtype);
+  const bool rows = c.kv_dtype == PKV_U8_ZP;
   const int chunks = (int)(block_elems(c) * (int64_t)elem_bytes(c.kv_dtype) / 16);
   dim3 grid((unsigned)n, 2), block(256);
   return launch(copy_blocks_kernel, grid, block, st, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache,
-                q8 ? c.k_scale : nullptr, q8 ? c.v_scale : nullptr, pairs, c.num_blocks,
-                c.num_kv_heads, block_stride_bytes(c), chunks);
+                q8 ? c.k_scale : nullptr, q8 ? c.v_scale : nullptr, rows ? c.k_zero : nullptr,
+                rows ? c.v_zero : nullptr, pairs, c.num_blocks,
+                rows ? c.num_kv_heads * kBlock : c.num_kv_heads, block_stride_bytes(c), chunks);
 }
 
 int launch_slot_mapping(const int32_t* tables, int max_blocks, const int32_t* lens, int n,

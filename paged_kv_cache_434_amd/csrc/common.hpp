@@ -20,6 +20,7 @@ inline size_t elem_bytes(int dtype) {
     case PKV_BF16: return 2;
     case PKV_I8: return 1;
     case PKV_FP8_E4M3: return 1;
+    case PKV_U8_ZP: return 1;
     default: return 0;
   }
 }
@@ -27,6 +28,10 @@ inline size_t elem_bytes(int dtype) {
 // Elements of one block of one pool (every KV head's tile).
 inline int64_t block_elems(const pkv_cache_t& c) {
   return (int64_t)c.num_kv_heads * c.block_size * c.head_dim;
+}
+
+inline bool is_q8(int dtype) {
+  return dtype == PKV_I8 || dtype == PKV_FP8_E4M3 || dtype == PKV_U8_ZP;
 }
 
 // Bytes from one block to the next in k_cache / v_cache.
@@ -87,6 +92,11 @@ int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
 int launch_copy_blocks(const pkv_cache_t& c, const int32_t* pairs, int n, hipStream_t st);
 int launch_quantize(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n_ids,
                     hipStream_t st);
+// Quantized append into a PKV_U8_ZP pool: row i goes to slots[i], or (slots
+// null) to position lens[i] - 1 of sequence i through its table.
+int launch_cache_write_quant(const pkv_cache_t& c, const void* k, const void* v, int src_dtype,
+                             const int32_t* slots, const int32_t* tables, int max_blocks,
+                             const int32_t* lens, int n, hipStream_t st);
 
 struct DecodeArgs {
   const pkv_cache_t* cache;

@@ -34,6 +34,11 @@
 //      read transposed from LDS and B = P, which the QK^T result already holds
 //      in the B-operand layout (4 consecutive tokens per lane, head = lane % 16);
 //      for 8-bit KV, P is multiplied by the block's V scale first.
+// Asymmetric per-row pools (value = (code - zero) * scale for each row) run
+// the matrix cores on the raw codes: row t's logit is
+// scale_t * (q . code_t - zero_t * sum(q)) and the output is
+// sum_t p_t scale_t code_t - sum_t p_t scale_t zero_t, so P is multiplied by
+// each row's V scale and the second sum is kept beside the accumulator.
 // The head index of a lane is lane % 16 in S, P and O alike, so the running
 // maximum and sum stay lane-local.
 //
@@ -67,7 +72,7 @@ constexpr int kMaxDevices = 64;
 constexpr float kNoMax = -3.0e38f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 
-enum { KV_BF16 = 0, KV_I8 = 1, KV_FP8 = 2 };
+enum { KV_BF16 = 0, KV_I8 = 1, KV_FP8 = 2, KV_U8Z = 3 };
 enum { OUT_F32 = 0, OUT_BF16 = 1 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -96,15 +101,16 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // an unsigned byte converts to binary32 in one instruction and u < 256 has at
 // most 8 significant bits, so its binary32 upper half is u in bf16 exactly.
 // The kernel subtracts the offset afterwards: 128 * sum(q) from each logit
-// and 128 * sum(p) from each output column.
+// and 128 * sum(p) from each output column.  Asymmetric uint8 codes are
+// widened the same way without the flip.
 template <int KV>
 __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
   const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (KV == KV_I8) {
-      const uint32_t u = w[i] ^ 0x80808080u;
+    if constexpr (KV == KV_I8 || KV == KV_U8Z) {
+      const uint32_t u = KV == KV_I8 ? w[i] ^ 0x80808080u : w[i];
       const float f0 = (float)(u & 0xFFu);
       const float f1 = (float)((u >> 8) & 0xFFu);
       const float f2 = (float)((u >> 16) & 0xFFu);
@@ -143,8 +149,10 @@ struct MfmaArgs {
   const uint16_t* q;
   const uint8_t* kc;
   const uint8_t* vc;
-  const float* ksc;
+  const float* ksc;   // 8-bit pools: scales per (block, head), or per row
   const float* vsc;
+  const uint8_t* kz;  // asymmetric per-row pools: zero points per row
+  const uint8_t* vz;
   const int32_t* tables;
   const int32_t* lens;
   int max_blocks;
@@ -212,7 +220,7 @@ __device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g, int t
 template <int D, int KV, int OUT, int NST, bool MQ>
 __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, int L, int b0,
                                              int b1, int slot, bool whole, int tok0,
-                                             uint8_t* lds_k, uint8_t* lds_v) {
+                                             uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_p) {
   constexpr int kEsz = (KV == KV_BF16) ? 2 : 1;
   constexpr int kTile = kBlock * D * kEsz;  // bytes of one (block, head) tile in HBM
   constexpr int kLoads = kTile / 1024;      // 16-byte loads per lane per tile
@@ -247,17 +255,18 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     }
   }
   // INT8 codes enter the MFMA as c + 128 (see widen16): each logit then holds
-  // 128 * sum_d q[h][d] too, which is taken off again before the softmax
-  float qoff = 0.f;
-  if constexpr (KV == KV_I8) {
+  // 128 * sum_d q[h][d] too, which is taken off again before the softmax;
+  // asymmetric rows take off zero_t * sum_d q[h][d]
+  float qsum = 0.f;
+  if constexpr (KV == KV_I8 || KV == KV_U8Z) {
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qoff += static_cast<float>(qop[kk][e]);
-    qoff += __shfl_xor(qoff, 16, kWave);
-    qoff += __shfl_xor(qoff, 32, kWave);
-    qoff *= 128.f;
+      for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qop[kk][e]);
+    qsum += __shfl_xor(qsum, 16, kWave);
+    qsum += __shfl_xor(qsum, 32, kWave);
   }
+  const float qoff = 128.f * qsum;
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = a.blk_stride;
@@ -287,7 +296,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
   float m = kNoMax;   // running reference maximum (log2 units)
   float lsum = 0.f;   // this lane's share of the softmax denominator
-  float psum = 0.f;   // INT8: this lane's share of sum(P), rescaled like the accumulator
+  float psum = 0.f;   // INT8: this lane's share of sum(P), rescaled like the accumulator;
+                      // asymmetric rows: of sum_t P_t zero_t, likewise
 
   // The range is walked in chunks of up to 64 blocks.  Per chunk, lane i
   // loads block-table entry i (and, for 8-bit KV, that block's two scales);
@@ -301,7 +311,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     const int c1 = min(c0 + 64, b1);
     const int tab = (c0 + lane < c1) ? trow[c0 + lane] : -1;
     float ks_l = 1.f, vs_l = 1.f;
-    if constexpr (KV != KV_BF16) {
+    if constexpr (KV == KV_I8 || KV == KV_FP8) {
       if (tab >= 0 && tab < num_blocks) {
         ks_l = a.ksc[(size_t)tab * hkv + g];
         vs_l = a.vsc[(size_t)tab * hkv + g];
@@ -310,7 +320,11 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     auto phys_of = [&](int b) -> int {
       return b < c1 ? __builtin_amdgcn_readlane(tab, b - c0) : -1;
     };
-    auto load_tile = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], int ph) {
+    // Asymmetric rows: the block's 16 K scales land in lanes 0-15, its 16 V
+    // scales in lanes 16-31, its K zero points (4 per dword) in lanes 32-35
+    // and its V zero points in lanes 36-39; every other lane's offset lies
+    // outside the descriptor's range and reads zero.
+    auto load_tile = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], u32x4& pr, int ph) {
       const bool in = ph >= 0 && ph < num_blocks;
       const size_t off = in ? (size_t)ph * blk_stride : 0;
       const rsrc_t rk = make_rsrc(kbase + off, in ? kTile : 0);
@@ -320,11 +334,22 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         kr[i] = buffer_load16(rk, i * 1024 + lane * 16);
         vr[i] = buffer_load16(rv, i * 1024 + lane * 16);
       }
+      if constexpr (KV == KV_U8Z) {
+        const size_t row0 = in ? ((size_t)ph * hkv + g) * kBlock : 0;
+        const rsrc_t rks = make_rsrc(a.ksc + row0, in ? kBlock * 4 : 0);
+        const rsrc_t rvs = make_rsrc(a.vsc + row0, in ? kBlock * 4 : 0);
+        const rsrc_t rkz = make_rsrc(a.kz + row0, in ? kBlock : 0);
+        const rsrc_t rvz = make_rsrc(a.vz + row0, in ? kBlock : 0);
+        pr[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, lane * 4, 0, 0);
+        pr[1] = __builtin_amdgcn_raw_buffer_load_b32(rvs, (lane - 16) * 4, 0, 0);
+        pr[2] = __builtin_amdgcn_raw_buffer_load_b32(rkz, (lane - 32) * 4, 0, 0);
+        pr[3] = __builtin_amdgcn_raw_buffer_load_b32(rvz, (lane - 36) * 4, 0, 0);
+      }
     };
 
     // Stage block b from (kr, vr) into LDS, refill the buffer with block
     // b+2, then run QK^T, the softmax update and PV for block b.
-    auto process = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], int& ph, int b) {
+    auto process = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], u32x4& pr, int& ph, int b) {
       const int cur = ph;
       const bool cur_ok = cur >= 0 && cur < num_blocks;
       const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
@@ -364,16 +389,28 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         }
       }
       float kscale = 1.f, vscale = 1.f;
-      if constexpr (KV != KV_BF16) {
+      if constexpr (KV == KV_I8 || KV == KV_FP8) {
         if (b < c1) {
           kscale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ks_l), b - c0));
           vscale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs_l), b - c0));
         }
       }
+      // asymmetric rows: lane (j, n) takes the scales and zero points of its
+      // rows 4j..4j+3 through LDS
+      f32x4 ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
+      uint32_t kzw = 0u, vzw = 0u;
+      if constexpr (KV == KV_U8Z) {
+        const uint32_t pw = pr[0] | pr[1] | pr[2] | pr[3];
+        if (lane < 40) *reinterpret_cast<uint32_t*>(lds_p + 4 * lane) = pw;
+        ks4 = *reinterpret_cast<const f32x4*>(lds_p + 16 * j);
+        vs4 = *reinterpret_cast<const f32x4*>(lds_p + 64 + 16 * j);
+        kzw = *reinterpret_cast<const uint32_t*>(lds_p + 128 + 4 * j);
+        vzw = *reinterpret_cast<const uint32_t*>(lds_p + 144 + 4 * j);
+      }
 
       // ---- refill this buffer with block b+NST (zero-length if absent)
       ph = phys_of(b + NST);
-      load_tile(kr, vr, ph);
+      load_tile(kr, vr, pr, ph);
 
       // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
       f32x4 sv = {0.f, 0.f, 0.f, 0.f};
@@ -390,8 +427,12 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float raw = (KV == KV_I8) ? sv[i] - qoff : sv[i];
-        x[i] = (4 * j + i < vcol) ? raw * cb : -INFINITY;
+        float y;
+        if constexpr (KV == KV_U8Z)
+          y = (sv[i] - (float)((kzw >> (8 * i)) & 0xFFu) * qsum) * (cb * ks4[i]);
+        else
+          y = ((KV == KV_I8) ? sv[i] - qoff : sv[i]) * cb;
+        x[i] = (4 * j + i < vcol) ? y : -INFINITY;
         mx = fmaxf(mx, x[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -401,7 +442,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         const float mnew = bump ? mx : m;
         const float alpha = exp2f(m - mnew);
         lsum *= alpha;
-        if constexpr (KV == KV_I8) psum *= alpha;
+        if constexpr (KV == KV_I8 || KV == KV_U8Z) psum *= alpha;
 #pragma unroll
         for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
         m = mnew;
@@ -411,8 +452,14 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       for (int i = 0; i < 4; ++i) {
         const float pe = exp2f(x[i] - m);
         lsum += pe;
-        pop[i] = static_cast<__bf16>(pe * vscale);
-        if constexpr (KV == KV_I8) psum += static_cast<float>(pop[i]);
+        if constexpr (KV == KV_U8Z) {
+          // rows past the end have p = 0 but may hold any scale
+          pop[i] = static_cast<__bf16>(4 * j + i < vcol ? pe * vs4[i] : 0.f);
+          psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
+        } else {
+          pop[i] = static_cast<__bf16>(pe * vscale);
+          if constexpr (KV == KV_I8) psum += static_cast<float>(pop[i]);
+        }
       }
 
       // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n]
@@ -430,28 +477,29 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     };
 
     // NST register buffers in a ring: buffer i holds block b with b % NST == i
-    u32x4 kr[NST][kLoads], vr[NST][kLoads];
+    u32x4 kr[NST][kLoads], vr[NST][kLoads], pr[NST];
     int ph[NST];
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       ph[i] = phys_of(c0 + i);
-      load_tile(kr[i], vr[i], ph[i]);
+      load_tile(kr[i], vr[i], pr[i], ph[i]);
     }
     for (int b = c0; b < c1; b += NST) {
 #pragma unroll
       for (int i = 0; i < NST; ++i)
-        process(kr[i], vr[i], ph[i], b + i);   // past c1: masked, no memory traffic
+        process(kr[i], vr[i], pr[i], ph[i], b + i);   // past c1: masked, no memory traffic
     }
   }
 
   // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
   float lt = lsum + __shfl_xor(lsum, 16, kWave);
   lt += __shfl_xor(lt, 32, kWave);
-  if constexpr (KV == KV_I8) {
-    // the V codes entered as c + 128: take 128 * sum(P) off every output row
+  if constexpr (KV == KV_I8 || KV == KV_U8Z) {
+    // the V codes entered as c + 128: take 128 * sum(P) off every output row;
+    // asymmetric rows: take sum_t P_t zero_t off
     float pt = psum + __shfl_xor(psum, 16, kWave);
     pt += __shfl_xor(pt, 32, kWave);
-    const float voff = 128.f * pt;
+    const float voff = KV == KV_I8 ? 128.f * pt : pt;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[t] -= voff;
   }
@@ -481,6 +529,7 @@ template <int D, int KV, int OUT, bool MQ>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[KV == KV_U8Z ? 160 : 16];
   const int g = blockIdx.x % a.hkv;
   const int r = blockIdx.x / a.hkv;
   const int p = r % n_parts;
@@ -495,7 +544,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
     if (p == 0) zero_rows<D, OUT>(a, s, g, tok0);   // empty sequence
     return;
   }
-  mfma_segment<D, KV, OUT, 2, MQ>(a, s, g, L, b0, b1, p, parts_s == 1, tok0, lds_k, lds_v);
+  mfma_segment<D, KV, OUT, 2, MQ>(a, s, g, L, b0, b1, p, parts_s == 1, tok0, lds_k, lds_v,
+                                  lds_p);
 }
 
 // Balanced split: a persistent grid of V wavefronts per KV head, one
@@ -519,6 +569,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_BAL_WAVE
 decode_mfma_balanced_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[KV == KV_U8Z ? 160 : 16];
   const int lane = threadIdx.x;
   const int g = blockIdx.x % a.hkv;
   const int v = blockIdx.x / a.hkv;
@@ -601,7 +652,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int slot = v - vf;
     if (g == 0 && blockIdx.y == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
     mfma_segment<D, KV, OUT, PKV_BAL_STAGES, MQ>(a, s, g, L, x - R0, e - R0, slot, K == 1, tok0,
-                                                 lds_k, lds_v);
+                                                 lds_k, lds_v, lds_p);
     if (e >= x1) break;
     x = e;
     R0 = R1;
@@ -945,6 +996,8 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
     const bool q8 = c.kv_dtype != PKV_BF16;
     m.ksc = q8 ? c.k_scale : nullptr;
     m.vsc = q8 ? c.v_scale : nullptr;
+    m.kz = c.kv_dtype == PKV_U8_ZP ? c.k_zero : nullptr;
+    m.vz = c.kv_dtype == PKV_U8_ZP ? c.v_zero : nullptr;
     m.tables = a.tables;
     m.lens = a.lens;
     m.max_blocks = a.max_blocks;
@@ -994,6 +1047,12 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
                      decode_mfma_balanced_kernel<D, KV_I8, OUT, true>)
                 : go(decode_mfma_kernel<D, KV_I8, OUT, false>,
                      decode_mfma_balanced_kernel<D, KV_I8, OUT, false>);
+        break;
+      case PKV_U8_ZP:
+        rc = mq ? go(decode_mfma_kernel<D, KV_U8Z, OUT, true>,
+                     decode_mfma_balanced_kernel<D, KV_U8Z, OUT, true>)
+                : go(decode_mfma_kernel<D, KV_U8Z, OUT, false>,
+                     decode_mfma_balanced_kernel<D, KV_U8Z, OUT, false>);
         break;
       default:
         rc = mq ? go(decode_mfma_kernel<D, KV_FP8, OUT, true>,

@@ -1,6 +1,9 @@
 // KV quantization: symmetric 8-bit codes with one binary32 scale per
 // (block, KV head) tile (page "大模型推理的KV Cache管理…", section 四: cached
-// K/V stored as 8-bit codes and restored as code * scale).
+// K/V stored as 8-bit codes and restored as code * scale), and the same
+// section's asymmetric scheme (KVQuantizationCache with per-channel
+// parameters): uint8 codes with a scale and a zero point per (head, token)
+// row of head_dim values, which also makes a one-token append local to its row.
 //
 // One wavefront per (block, KV head, K-or-V) tile of 16 x head_dim values:
 // coalesced 16-byte loads into registers, a wave-wide max of |x|, then
@@ -127,9 +130,185 @@ int launch_q(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids,
                 (int64_t)(block_stride_bytes(src) / sizeof(SrcT)), (int64_t)block_stride_bytes(dst));
 }
 
+// Asymmetric row parameters and codes (binary32 steps, ties to even):
+// scale = (max - min) / 255, zero = clamp(rint(-min / scale), 0, 255),
+// code = clamp(rint((x - min) / scale), 0, 255); a zero-width row (scale 0)
+// gets zero 0 and codes 0.
+struct AsymRow {
+  float mn, sc;
+  uint8_t zero;
+  __device__ __forceinline__ AsymRow(float lo, float hi) : mn(lo) {
+    sc = (hi - lo) / 255.0f;
+    zero = 0;
+    if (sc != 0.0f) zero = (uint8_t)fminf(fmaxf(rintf(-lo / sc), 0.0f), 255.0f);
+  }
+  __device__ __forceinline__ uint32_t code(float x) const {
+    if (sc == 0.0f) return 0u;
+    return (uint32_t)fminf(fmaxf(rintf((x - mn) / sc), 0.0f), 255.0f);
+  }
+};
+
+// Per-row asymmetric quantization of a pool: one wavefront per (block, KV
+// head, K-or-V) tile, loaded as in quantize_kernel; the kVec values a lane
+// holds per load lie in one row, whose D / kVec lanes are consecutive, so the
+// row minimum and maximum are shuffle reductions over that lane group.
+template <typename SrcT, int D>
+__global__ __launch_bounds__(64) void quantize_rows_kernel(
+    const SrcT* __restrict__ ksrc, const SrcT* __restrict__ vsrc, uint8_t* __restrict__ kdst,
+    uint8_t* __restrict__ vdst, float* __restrict__ kscale, float* __restrict__ vscale,
+    uint8_t* __restrict__ kzero, uint8_t* __restrict__ vzero, const int32_t* __restrict__ ids,
+    int hkv, int num_blocks, int64_t src_stride, int64_t dst_stride) {
+  constexpr int kElems = kBlock * D;
+  constexpr int kVec = 16 / sizeof(SrcT);        // values per 16-byte load
+  constexpr int kLoads = kElems / kWave / kVec;
+  constexpr int kLpr = D / kVec;                 // lanes per row
+  constexpr int kRowsPerLoad = kWave / kLpr;
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % hkv;
+  const int idx = blockIdx.x / hkv;
+  const int b = ids ? ids[idx] : idx;
+  if (b < 0 || b >= num_blocks) return;
+  const bool is_v = blockIdx.y != 0;
+  const SrcT* src = (is_v ? vsrc : ksrc) + (size_t)b * src_stride + (size_t)g * kElems;
+  uint8_t* dst = (is_v ? vdst : kdst) + (size_t)b * dst_stride + (size_t)g * kElems;
+  float* scale = (is_v ? vscale : kscale) + ((size_t)b * hkv + g) * kBlock;
+  uint8_t* zero = (is_v ? vzero : kzero) + ((size_t)b * hkv + g) * kBlock;
+
+#pragma unroll
+  for (int ld = 0; ld < kLoads; ++ld) {
+    float x[kVec];
+    uint4 raw = *reinterpret_cast<const uint4*>(src + (size_t)ld * kWave * kVec + lane * kVec);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (sizeof(SrcT) == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu);
+        x[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+      }
+    }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < kVec; ++e) {
+      mn = fminf(mn, x[e]);
+      mx = fmaxf(mx, x[e]);
+    }
+#pragma unroll
+    for (int o = 1; o < kLpr; o <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    }
+    const AsymRow q(mn, mx);
+    const int row = ld * kRowsPerLoad + lane / kLpr;
+    if (lane % kLpr == 0) {
+      scale[row] = q.sc;
+      zero[row] = q.zero;
+    }
+    uint8_t* p = dst + (size_t)ld * kWave * kVec + lane * kVec;
+    if constexpr (kVec == 4) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c |= q.code(x[e]) << (8 * e);
+      *reinterpret_cast<uint32_t*>(p) = c;
+    } else {
+      uint2 c = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c.x |= q.code(x[e]) << (8 * e);
+        c.y |= q.code(x[4 + e]) << (8 * e);
+      }
+      *reinterpret_cast<uint2*>(p) = c;
+    }
+  }
+}
+
+// Quantized append: one wavefront per (token, KV head) row pair (K in
+// blockIdx.y 0, V in 1); lane l holds values [l * kPer, l * kPer + kPer) of
+// the row.  Row i goes to slots[i], or with slots null to position
+// lens[i] - 1 of sequence i through its block table.
+template <typename SrcT, int D>
+__global__ __launch_bounds__(64) void cache_write_quant_kernel(
+    const SrcT* __restrict__ kn, const SrcT* __restrict__ vn, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, float* __restrict__ kscale, float* __restrict__ vscale,
+    uint8_t* __restrict__ kzero, uint8_t* __restrict__ vzero, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens, int hkv,
+    int num_blocks, size_t blk_bytes) {
+  constexpr int kPer = D / kWave;   // 1 or 2 values per lane
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  int64_t slot = -1;
+  if (slots != nullptr) {
+    slot = slots[i];
+  } else {
+    const int L = lens[i];
+    if (L > 0 && L <= max_blocks * kBlock)
+      slot = (int64_t)tables[(size_t)i * max_blocks + (L - 1) / kBlock] * kBlock + (L - 1) % kBlock;
+  }
+  if (slot < 0 || slot >= (int64_t)num_blocks * kBlock) return;
+  const bool is_v = blockIdx.y != 0;
+  const SrcT* src = (is_v ? vn : kn) + ((size_t)i * hkv + g) * D + lane * kPer;
+  float x[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if constexpr (sizeof(SrcT) == 4)
+      x[e] = src[e];
+    else
+      x[e] = bf16_bits_to_f32(src[e]);
+  }
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < kPer; ++e) {
+    mn = fminf(mn, x[e]);
+    mx = fmaxf(mx, x[e]);
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  }
+  const AsymRow q(mn, mx);
+  const int64_t blk = slot / kBlock, o = slot % kBlock;
+  uint8_t* dst = (is_v ? vc : kc) + (size_t)blk * blk_bytes + ((size_t)g * kBlock + o) * D +
+                 lane * kPer;
+  if constexpr (kPer == 2)
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(q.code(x[0]) | (q.code(x[1]) << 8));
+  else
+    *dst = (uint8_t)q.code(x[0]);
+  if (lane == 0) {
+    const size_t r = ((size_t)blk * hkv + g) * kBlock + o;
+    (is_v ? vscale : kscale)[r] = q.sc;
+    (is_v ? vzero : kzero)[r] = q.zero;
+  }
+}
+
+template <typename SrcT, int D>
+int launch_qrows(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n,
+                 hipStream_t st) {
+  dim3 grid((unsigned)(n * src.num_kv_heads), 2), block(kWave);
+  return launch(quantize_rows_kernel<SrcT, D>, grid, block, st, (const SrcT*)src.k_cache,
+                (const SrcT*)src.v_cache, (uint8_t*)dst.k_cache, (uint8_t*)dst.v_cache,
+                dst.k_scale, dst.v_scale, dst.k_zero, dst.v_zero, ids, src.num_kv_heads,
+                src.num_blocks, (int64_t)(block_stride_bytes(src) / sizeof(SrcT)),
+                (int64_t)block_stride_bytes(dst));
+}
+
+template <typename SrcT, int D>
+int launch_cwq(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,
+               const int32_t* tables, int max_blocks, const int32_t* lens, int n,
+               hipStream_t st) {
+  dim3 grid((unsigned)((int64_t)n * c.num_kv_heads), 2), block(kWave);
+  return launch(cache_write_quant_kernel<SrcT, D>, grid, block, st, (const SrcT*)k,
+                (const SrcT*)v, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache, c.k_scale, c.v_scale,
+                c.k_zero, c.v_zero, slots, tables, max_blocks, lens, c.num_kv_heads,
+                c.num_blocks, block_stride_bytes(c));
+}
+
 template <typename SrcT, int D>
 int launch_qd(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n,
               hipStream_t st) {
+  if (dst.kv_dtype == PKV_U8_ZP) return launch_qrows<SrcT, D>(src, dst, ids, n, st);
   return dst.kv_dtype == PKV_FP8_E4M3 ? launch_q<SrcT, D, true>(src, dst, ids, n, st)
                                       : launch_q<SrcT, D, false>(src, dst, ids, n, st);
 }
@@ -146,6 +325,18 @@ int launch_quantize(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_
                : launch_qd<uint16_t, 128>(src, dst, ids, n, st);
   return f32 ? launch_qd<float, 64>(src, dst, ids, n, st)
              : launch_qd<uint16_t, 64>(src, dst, ids, n, st);
+}
+
+int launch_cache_write_quant(const pkv_cache_t& c, const void* k, const void* v, int src_dtype,
+                             const int32_t* slots, const int32_t* tables, int max_blocks,
+                             const int32_t* lens, int n, hipStream_t st) {
+  if (n == 0) return PKV_OK;
+  const bool f32 = src_dtype == PKV_F32;
+  if (c.head_dim == 128)
+    return f32 ? launch_cwq<float, 128>(c, k, v, slots, tables, max_blocks, lens, n, st)
+               : launch_cwq<uint16_t, 128>(c, k, v, slots, tables, max_blocks, lens, n, st);
+  return f32 ? launch_cwq<float, 64>(c, k, v, slots, tables, max_blocks, lens, n, st)
+             : launch_cwq<uint16_t, 64>(c, k, v, slots, tables, max_blocks, lens, n, st);
 }
 
 }  // namespace pkv

@@ -190,3 +190,34 @@ def test_multi_token_entry_points_reject_bad_arguments():
     assert lib.pkv_slot_mapping_tokens(FAKE, 4, FAKE, 2, 0, FAKE, None) == 2
     assert lib.pkv_slot_mapping_tokens(None, 4, FAKE, 2, 3, FAKE, None) == 1
     assert lib.pkv_slot_mapping_tokens(FAKE, 4, FAKE, 0, 3, FAKE, None) == 0
+
+
+def _u8z(**kw):
+    d = dict(kv_dtype=4, k_scale=FAKE, v_scale=FAKE, k_zero=FAKE + 8192, v_zero=FAKE + 12288)
+    d.update(kw)
+    return _cache(**d)
+
+
+def test_asymmetric_pool_validation():
+    lib = pkv.lib()
+    assert _decode(_u8z(k_zero=None)) == 1              # zero points required
+    assert _decode(_u8z(v_scale=None)) == 1             # scales required
+    assert _decode(_u8z(v_zero=FAKE + 8194)) == 6       # zero points read 4 bytes at a time
+    assert _decode(_u8z(), q_dtype=0) == 3              # 8-bit pools take bf16 queries
+    assert _decode(_u8z(), B=0) == 0
+    # byte copies cannot append into it: the quantizing append is its own call
+    assert lib.pkv_cache_write(ctypes.byref(_u8z()), FAKE, FAKE, FAKE, 3, None) == 6
+    wq = lambda cc, k=FAKE, v=FAKE, sd=1, s=FAKE, n=3: lib.pkv_cache_write_quant(
+        ctypes.byref(cc), k, v, sd, s, n, None)
+    assert wq(_cache()) == 3                            # not a u8z pool
+    assert wq(_u8z(), sd=2) == 3                        # source must be f32 or bf16
+    assert wq(_u8z(), n=-1) == 2
+    assert wq(_u8z(), n=0) == 0
+    assert wq(_u8z(), k=None) == 1
+    assert wq(_u8z(), s=None) == 1
+    assert wq(_u8z(), v=FAKE + 2) == 6
+    # quantizing into it from a float pool is accepted up to the launch;
+    # from another 8-bit pool it is not
+    q = lambda a, b: lib.pkv_quantize(ctypes.byref(a), ctypes.byref(b), None, 0, None)
+    assert q(_u8z(), _u8z()) == 3
+    assert q(_cache(), _u8z(num_blocks=9)) == 2
