@@ -78,6 +78,9 @@ def _load():
         lib.orc_decode_multi.restype = I
         lib.orc_decode_multi.argtypes = [P, I, P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, I, F,
                                          P]
+        lib.orc_decode_window.restype = I
+        lib.orc_decode_window.argtypes = [P, I, P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, I,
+                                          I, F, P]
         lib.orc_slot_mapping_tokens.restype = None
         lib.orc_slot_mapping_tokens.argtypes = [P, I, P, I, I, I, P]
         lib.orc_decode_partials.restype = I
@@ -247,6 +250,30 @@ def decode_multi(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_l
                                   Hq, Hkv, D, bs, float(np.float32(scale)), _ptr(out))
     if rc != 0:
         raise MemoryError("oracle decode_multi: allocation failed")
+    return out
+
+
+def decode_window(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens, scale,
+                  window, k_scale=None, v_scale=None, k_zero=None, v_zero=None) -> np.ndarray:
+    """Sliding-window attention (page on KV cache and PagedAttention, "三个直接推论"):
+    q [B][ntok][Hq][D]; query token i at position p = L - ntok + i attends to
+    the window most recent positions up to p; window <= 0: no window.
+    float64 output of q's shape."""
+    qa = _c(q, NP_STORAGE[q_dtype])
+    B, ntok, Hq, D = qa.shape
+    _, kc, vc, ks, vs, kz, vz, bt, lens = _decode_args(qa.reshape(B * ntok, Hq, D), q_dtype,
+                                                       k_cache, v_cache, kv_dtype, k_scale,
+                                                       v_scale, block_tables, context_lens,
+                                                       k_zero, v_zero)
+    NB, Hkv, bs, D2 = kc.shape
+    assert D == D2 and Hq % Hkv == 0 and lens.shape[0] == B
+    out = np.zeros((B, ntok, Hq, D), dtype=np.float64)
+    rc = _load().orc_decode_window(_ptr(qa), DTYPES[q_dtype], _ptr(kc), _ptr(vc),
+                                   DTYPES[kv_dtype], _ptr(ks), _ptr(vs), _ptr(kz), _ptr(vz),
+                                   _ptr(bt), bt.shape[1], _ptr(lens), B, ntok, int(window), Hq,
+                                   Hkv, D, bs, float(np.float32(scale)), _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle decode_window: allocation failed")
     return out
 
 

@@ -667,3 +667,45 @@ int orc_cache_write_quant(uint8_t* k_cache, uint8_t* v_cache, float* k_scale, fl
   free(row);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sliding-window attention ([WIKI] "三个直接推论": keeping only a window of
+ * the most recent tokens is one of the ways to cut KV bytes).  As in
+ * orc_decode_multi, query token i of sequence s sits at position
+ * p = L - ntok + i, but it attends only to the `window` most recent tokens up
+ * to itself: max(0, p - window + 1) <= t <= p.  window <= 0 means no window
+ * (the whole prefix, orc_decode_multi).  Tokens before every query's window
+ * are never read.  q and out are [num_seqs][ntok][Hq][D].                   */
+int orc_decode_window(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                      int kv_dtype, const float* k_scale, const float* v_scale,
+                      const uint8_t* k_zero, const uint8_t* v_zero, const int32_t* block_tables,
+                      int max_blocks, const int32_t* context_lens, int num_seqs, int ntok,
+                      int window, int Hq, int Hkv, int D, int bs, float scale, double* out) {
+  int max_len = 0, fail = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (context_lens[s] > max_len) max_len = context_lens[s];
+#pragma omp parallel reduction(| : fail)
+  {
+    double* logits = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!logits) {
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long r = 0; r < (long)num_seqs * ntok * Hq; ++r) {
+        int s = (int)(r / ((long)ntok * Hq));
+        int i = (int)((r / Hq) % ntok), h = (int)(r % Hq);
+        int p = context_lens[s] - ntok + i;
+        int t1 = p + 1 > 0 ? p + 1 : 0;
+        int t0 = (window > 0 && p - window + 1 > 0) ? p - window + 1 : 0;
+        double m, l;
+        orc_attend_range(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, k_zero,
+                         v_zero, block_tables, max_blocks, s, h, Hq, Hkv, D, bs, (double)scale,
+                         t0 < t1 ? t0 : t1, t1, (size_t)r * D, logits, &m, &l,
+                         out + (size_t)r * D);
+      }
+      free(logits);
+    }
+  }
+  return fail ? -1 : 0;
+}
+

@@ -564,6 +564,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 #define PKV_BAL_STAGES 2
 #define PKV_BAL_WAVES 2
 #endif
+#ifndef PKV_BAL_STAGES_Q8
+#define PKV_BAL_STAGES_Q8 2
+#endif
 template <int D, int KV, int OUT, bool MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_BAL_WAVES))) void
 decode_mfma_balanced_kernel(MfmaArgs a) {
@@ -651,8 +654,10 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int K = (R1 - 1) / per - vf + 1;
     const int slot = v - vf;
     if (g == 0 && blockIdx.y == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
-    mfma_segment<D, KV, OUT, PKV_BAL_STAGES, MQ>(a, s, g, L, x - R0, e - R0, slot, K == 1, tok0,
-                                                 lds_k, lds_v, lds_p);
+    // 8-bit tiles are half the bytes of bf16 ones: they may keep more blocks in flight
+    constexpr int kStages = KV == KV_BF16 ? PKV_BAL_STAGES : PKV_BAL_STAGES_Q8;
+    mfma_segment<D, KV, OUT, kStages, MQ>(a, s, g, L, x - R0, e - R0, slot, K == 1, tok0, lds_k,
+                                          lds_v, lds_p);
     if (e >= x1) break;
     x = e;
     R0 = R1;
