@@ -25,6 +25,12 @@
  *          heads share KV heads), "PagedAttention：vLLM 的显存碎片治理"
  *          (16-token blocks; block table maps logical to physical blocks;
  *          shared blocks for common prefixes).
+ *   [CSDN] the ascendai.csdn.net article on PagedAttention and KV quantization
+ *          (its text carries no title): section 二 "核心突破：PagedAttention与
+ *          虚拟内存" (copy-on-write of shared blocks), section 三 "进阶优化：KV
+ *          Cache量化与压缩" (INT8, FP8 and FP4 KV).
+ *   [WIKI] "KV Cache 与 PagedAttention": "三个直接推论" (GQA, KV quantization,
+ *          sliding windows and paging as the ways to save KV bytes).
  *   [MGMT] "大模型推理的KV Cache管理从内存碎片到前缀缓存的优化实战": section
  *          二 (KVCacheBlock stores [heads][block_size][head_dim]; append_slot
  *          takes logical block token_idx // block_size; allocation failure is
@@ -267,6 +273,28 @@ int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype
                         int32_t num_q_heads, float scale, int32_t partition_tokens,
                         void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
                         void* stream);
+
+/* Sliding-window paged attention ([WIKI] "三个直接推论": attending to, and
+ * keeping, only a window of the most recent tokens is one of the ways to cut
+ * KV bytes).  As pkv_attention_multi, except that query token i at position
+ * p = L - k + i (k = tokens_per_seq) attends only to max(0, p - window + 1)
+ * <= t <= p:
+ *   out[s][i][h] = sum_{p-window < t <= p} softmax_t(scale q[s][i][h] . k_t) v_t.
+ * window == 0 means no window (then the call equals pkv_attention_multi);
+ * negative is PKV_ERR_SHAPE.  Table entries before block
+ * (L - k + 1 - window) / 16 (when that is positive) are never read, so a
+ * caller may recycle the blocks that left every window; K/V rows outside
+ * every query's window may hold anything (NaN included).
+ *   q, out: device [num_seqs][tokens_per_seq][num_q_heads][head_dim]
+ *   workspace: as for pkv_attention_multi.
+ * Splits and dtypes as for pkv_attention_multi (fp32 pools are
+ * PKV_ERR_UNSUPPORTED). */
+int pkv_attention_window(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         int32_t tokens_per_seq, int32_t window, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, float scale,
+                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                         void* out, int32_t out_dtype, void* stream);
 
 /* KV quantization ([MGMT] section 四, with one symmetric binary32 scale per
  * (block, KV head) tile): for each listed block b and KV head g, with

@@ -18,8 +18,13 @@
  *          二 (classes KVCacheBlock: one block holds [heads][block_size][dim];
  *          PagedKVCache.append_slot: logical block = token_idx // block_size),
  *          section 四 (INT8 quantization of cached K/V, dequantize = code*scale).
+ *   [CSDN] the ascendai.csdn.net article on PagedAttention and KV quantization
+ *          (its text carries no title): section 二 "核心突破：PagedAttention与
+ *          虚拟内存" (copy-on-write of shared blocks), section 三 "进阶优化：KV
+ *          Cache量化与压缩" (INT8, FP8 and FP4 KV).
  *   [WIKI] "KV Cache 与 PagedAttention" -- "KV cache 有多大" (per-token size),
- *          "三个直接推论" (GQA and KV quantization as byte savers).
+ *          "三个直接推论" (GQA, KV quantization and sliding windows as byte
+ *          savers).
  *
  * Readings where the pages leave a step open (each is listed in the design
  * notes): pool layout [num_blocks][num_kv_heads][block_size][head_dim]; slot =

@@ -73,6 +73,8 @@ def _load():
                                                ctypes.c_size_t, P, I32, P]),
             "pkv_attention_multi": (ctypes.c_int, [C, P, I32, I32, P, I32, P, I32, I32, F, I32, P,
                                                    ctypes.c_size_t, P, I32, P]),
+            "pkv_attention_window": (ctypes.c_int, [C, P, I32, I32, I32, P, I32, P, I32, I32, F,
+                                                    I32, P, ctypes.c_size_t, P, I32, P]),
             "pkv_quantize": (ctypes.c_int, [C, C, P, I32, P]),
             "pkv_gather": (ctypes.c_int, [C, P, I32, P, P, I32, P, P, P]),
             "pkv_copy_blocks": (ctypes.c_int, [C, P, I32, P]),
@@ -93,7 +95,7 @@ def lib():
 
 
 EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_mapping",
-                    "pkv_slot_mapping_tokens", "pkv_attention_multi",
+                    "pkv_slot_mapping_tokens", "pkv_attention_multi", "pkv_attention_window",
                     "pkv_cache_write", "pkv_cache_write_quant", "pkv_decode_workspace_bytes",
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
                     "pkv_quantize", "pkv_copy_blocks",
@@ -362,9 +364,10 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, 
 
 def attention_multi(cache: PagedCache, q, block_tables, context_lens, scale: float,
                     partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
-                    stream=None):
+                    stream=None, window: Optional[int] = None):
     """Several query tokens per sequence (q [B][k][Hq][D]); query token i of a
-    sequence of length L attends to the tokens up to position L - k + i."""
+    sequence of length L attends to the tokens up to position L - k + i (with
+    ``window``, only to the window most recent of them)."""
     torch = _torch()
     qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
     if qd is None:
@@ -384,12 +387,28 @@ def attention_multi(cache: PagedCache, q, block_tables, context_lens, scale: flo
     if decode_workspace_bytes(B * k, Hq, D, maxb, partition_tokens) and workspace is None:
         workspace = alloc_workspace(B * k, Hq, D, maxb, partition_tokens, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("pkv_attention_multi",
-           _load().pkv_attention_multi(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd], k,
-                                       _ptr(block_tables), maxb, _ptr(context_lens), B, Hq,
-                                       ctypes.c_float(scale), partition_tokens, _ptr(workspace),
-                                       ws_bytes, _ptr(out), DTYPE_CODES[odn], _stream(stream)))
+    rest = (_ptr(block_tables), maxb, _ptr(context_lens), B, Hq, ctypes.c_float(scale),
+            partition_tokens, _ptr(workspace), ws_bytes, _ptr(out), DTYPE_CODES[odn],
+            _stream(stream))
+    if window is None:
+        _check("pkv_attention_multi",
+               _load().pkv_attention_multi(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd], k,
+                                           *rest))
+    else:
+        _check("pkv_attention_window",
+               _load().pkv_attention_window(ctypes.byref(cache.desc), _ptr(q), DTYPE_CODES[qd], k,
+                                            int(window), *rest))
     return out
+
+
+def attention_window(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                     window: int, partition_tokens: int = 0, workspace=None, out=None,
+                     out_dtype=None, stream=None):
+    """Sliding-window attention: q [B][k][Hq][D] (k = 1 for decode); query
+    token i at position p = L - k + i sees positions p - window < t <= p;
+    window 0: no window."""
+    return attention_multi(cache, q, block_tables, context_lens, scale, partition_tokens,
+                           workspace, out, out_dtype, stream, window=window)
 
 
 class PreparedCall:

@@ -142,7 +142,7 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                          int32_t num_seqs, int32_t num_q_heads, float scale,
                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                          void* out, int32_t out_dtype, void* stream, bool append,
-                         int32_t ntok = 1) {
+                         int32_t ntok = 1, int32_t window = 0) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   if (elem_bytes(q_dtype) == 0 || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
@@ -157,7 +157,8 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
   if (ntok <= 0 || ntok > 1024) return PKV_ERR_SHAPE;
-  if (ntok > 1 && kv == PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (window < 0) return PKV_ERR_SHAPE;
+  if ((ntok > 1 || window > 0) && kv == PKV_F32) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * ntok * num_q_heads > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (append) {
@@ -189,7 +190,7 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   DecodeArgs a{cache,     q,          q_dtype,   block_tables,     max_blocks_per_seq,
                context_lens, num_seqs, num_q_heads, scale,          partition_tokens,
                workspace, out,        out_dtype, fused ? k_new : nullptr,
-               fused ? v_new : nullptr, ntok};
+               fused ? v_new : nullptr, ntok, window};
   return launch_decode(a, st);
 }
 
@@ -222,6 +223,17 @@ int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype
   return decode_common(cache, q, q_dtype, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, partition_tokens, workspace,
                        workspace_bytes, out, out_dtype, stream, false, tokens_per_seq);
+}
+
+int pkv_attention_window(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         int32_t tokens_per_seq, int32_t window, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, float scale,
+                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                         void* out, int32_t out_dtype, void* stream) {
+  return decode_common(cache, q, q_dtype, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, partition_tokens, workspace,
+                       workspace_bytes, out, out_dtype, stream, false, tokens_per_seq, window);
 }
 
 int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,

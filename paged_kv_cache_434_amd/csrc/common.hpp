@@ -115,6 +115,7 @@ struct DecodeArgs {
   const void* k_new;   // fused append of position L-1 (decode step), or nullptr
   const void* v_new;
   int ntok;            // query tokens per sequence (1: decode)
+  int window;          // sliding window in tokens, 0 for none
 };
 int launch_decode(const DecodeArgs& a, hipStream_t st);
 

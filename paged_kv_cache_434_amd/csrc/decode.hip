@@ -42,6 +42,13 @@
 // The head index of a lane is lane % 16 in S, P and O alike, so the running
 // maximum and sum stay lane-local.
 //
+// Sliding window: with window W > 0 a query at position p sees only the
+// positions p - W < t <= p (page "KV Cache 与 PagedAttention", section
+// "三个直接推论": keeping a window of recent tokens saves KV bytes).  The
+// blocks before the earliest window of a sequence are left out of its block
+// range, so they are never read, and rows outside a column's window are
+// masked like rows past the end.
+//
 // Split context: with partition_tokens > 0 each wavefront writes its
 // partition's (max, sum, normalised output) to the workspace and a second
 // kernel combines them with the log-sum-exp rule; a sequence that fits in one
@@ -169,6 +176,7 @@ struct MfmaArgs {
   int min_blocks;     // balanced split: fewest blocks one wavefront takes
   int ntok;           // query tokens per sequence (1: decode)
   int tok_per_pass;   // query tokens one wavefront takes (ntok * G columns split in passes)
+  int window;         // sliding window in tokens, 0 for none
   void* out;
   const uint8_t* kn;  // fused append (decode step): new K/V rows, or null
   const uint8_t* vn;
@@ -178,6 +186,19 @@ struct MfmaArgs {
 
 __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
   return (L < 0 || L > max_blocks * kBlock) ? 0 : L;
+}
+
+// First logical block any query of a sequence of length L can see: with a
+// window W the earliest query (position L - ntok) starts at L - ntok + 1 - W.
+__device__ __forceinline__ int first_block(int L, int ntok, int window) {
+  if (window <= 0) return 0;
+  const int lo = L - ntok + 1 - window;
+  return lo > 0 ? lo / kBlock : 0;
+}
+
+// Blocks a sequence of length L contributes: [first_block, ceil(L / 16)).
+__device__ __forceinline__ int seq_blocks(int L, int ntok, int window) {
+  return L > 0 ? (L + kBlock - 1) / kBlock - first_block(L, ntok, window) : 0;
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -236,8 +257,13 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   const int h = g * G + (MQ ? n % G : n);
   const bool has_head = MQ ? (n < G * a.tok_per_pass && ti < a.ntok) : n < G;
   const size_t out_row = MQ ? ((size_t)s * a.ntok + ti) * hq + h : (size_t)s * hq + h;
-  // last key position + 1 this column may see (causal within the chunk)
+  // last key position + 1 this column may see (causal within the chunk), and
+  // with a window the first one (lo_col), and the lowest first position of
+  // all columns of this pass (lo_seg): V rows below it are zeroed in LDS
   const int lim = MQ ? L - a.ntok + ti + 1 : L;
+  constexpr int kNoLo = -(1 << 30);
+  const int lo_col = a.window > 0 ? lim - a.window : kNoLo;
+  const int lo_seg = a.window > 0 ? (MQ ? L - a.ntok + tok0 + 1 : L) - a.window : kNoLo;
 
   f32x4 acc[kNT];
 #pragma unroll
@@ -353,6 +379,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const int cur = ph;
       const bool cur_ok = cur >= 0 && cur < num_blocks;
       const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
+      const int vlo = lo_seg - b * kBlock;                          // rows below: outside
 
       // ---- stage into LDS as bf16 (V rows past L zeroed)
 #pragma unroll
@@ -362,17 +389,17 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           const int row = chunk / (D / 8), ch = chunk % (D / 8);
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) =
-              row < valid ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+              (row < valid && row >= vlo) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
         } else {
           const int byte = (i * 64 + lane) * 16;    // first code of this chunk
           const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
-          u32x4 klo, khi, vlo, vhi;
+          u32x4 klo, khi, vlo4, vhi;
           widen16<KV>(kr[i], klo, khi);
-          widen16<KV>(vr[i], vlo, vhi);
-          if (row >= valid) vlo = vhi = u32x4{0u, 0u, 0u, 0u};
+          widen16<KV>(vr[i], vlo4, vhi);
+          if (row >= valid || row < vlo) vlo4 = vhi = u32x4{0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
-          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo4;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
         }
       }
@@ -425,6 +452,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       float x[4];
       float mx = -INFINITY;
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
+      const int vmin = lo_col - b * kBlock;   // this column's first row in its window
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float y;
@@ -432,7 +460,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           y = (sv[i] - (float)((kzw >> (8 * i)) & 0xFFu) * qsum) * (cb * ks4[i]);
         else
           y = ((KV == KV_I8) ? sv[i] - qoff : sv[i]) * cb;
-        x[i] = (4 * j + i < vcol) ? y : -INFINITY;
+        x[i] = (4 * j + i < vcol && 4 * j + i >= vmin) ? y : -INFINITY;
         mx = fmaxf(mx, x[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -454,7 +482,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         lsum += pe;
         if constexpr (KV == KV_U8Z) {
           // rows past the end have p = 0 but may hold any scale
-          pop[i] = static_cast<__bf16>(4 * j + i < vcol ? pe * vs4[i] : 0.f);
+          pop[i] = static_cast<__bf16>(4 * j + i < vcol && 4 * j + i >= vmin ? pe * vs4[i] : 0.f);
           psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
         } else {
           pop[i] = static_cast<__bf16>(pe * vscale);
@@ -536,8 +564,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
   const int s = r / n_parts;
   const int L = clamp_len(a.lens[s], a.max_blocks);
   const int nblk = (L + kBlock - 1) / kBlock;
-  const int parts_s = (nblk + a.part_blocks - 1) / a.part_blocks;
-  const int b0 = p * a.part_blocks;
+  const int fb = first_block(L, a.ntok, a.window);
+  const int parts_s = (nblk - fb + a.part_blocks - 1) / a.part_blocks;
+  const int b0 = fb + p * a.part_blocks;
   const int b1 = min(b0 + a.part_blocks, nblk);
   const int tok0 = blockIdx.y * a.tok_per_pass;
   if (b0 >= b1) {
@@ -608,7 +637,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   for (int base = 0; base < B; base += kWave) {
     const int si = base + lane;
     const int Ll = len_chunk(base);
-    total += wave_sum_i((Ll + kBlock - 1) / kBlock);
+    total += wave_sum_i(seq_blocks(Ll, a.ntok, a.window));
     if (v == 0) {
       uint64_t empty = __ballot(si < B && Ll == 0);
       while (empty) {
@@ -632,7 +661,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   int base = 0, carry = 0, s = -1, R0 = 0, Lreg = 0, incl = 0;
   for (; base < B; base += kWave) {
     Lreg = len_chunk(base);
-    const int nb = (Lreg + kBlock - 1) / kBlock;
+    const int nb = seq_blocks(Lreg, a.ntok, a.window);
     incl = wave_incl_scan(nb) + carry;
     const uint64_t hit = __ballot(nb > 0 && incl - nb <= x0 && x0 < incl);
     if (hit) {
@@ -648,7 +677,8 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   int x = x0;
   while (true) {
     const int L = readlane_i(Lreg, s - base);
-    const int R1 = R0 + (L + kBlock - 1) / kBlock;
+    const int fb = first_block(L, a.ntok, a.window);
+    const int R1 = R0 + seq_blocks(L, a.ntok, a.window);
     const int e = min(x1, R1);
     const int vf = R0 / per;
     const int K = (R1 - 1) / per - vf + 1;
@@ -656,8 +686,8 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     if (g == 0 && blockIdx.y == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
     // 8-bit tiles are half the bytes of bf16 ones: they may keep more blocks in flight
     constexpr int kStages = KV == KV_BF16 ? PKV_BAL_STAGES : PKV_BAL_STAGES_Q8;
-    mfma_segment<D, KV, OUT, kStages, MQ>(a, s, g, L, x - R0, e - R0, slot, K == 1, tok0, lds_k,
-                                          lds_v, lds_p);
+    mfma_segment<D, KV, OUT, kStages, MQ>(a, s, g, L, fb + x - R0, fb + e - R0, slot, K == 1,
+                                          tok0, lds_k, lds_v, lds_p);
     if (e >= x1) break;
     x = e;
     R0 = R1;
@@ -669,7 +699,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
         carry = readlane_i(incl, kWave - 1);
         base += kWave;
         Lreg = len_chunk(base);
-        incl = wave_incl_scan((Lreg + kBlock - 1) / kBlock) + carry;
+        incl = wave_incl_scan(seq_blocks(Lreg, a.ntok, a.window)) + carry;
       }
       Lnext = readlane_i(Lreg, s - base);
     }
@@ -872,8 +902,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
                                                     const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ lens,
                                                     int max_blocks, int rows_per_seq,
-                                                    int part_blocks, int kstride,
-                                                    void* __restrict__ out) {
+                                                    int part_blocks, int kstride, int ntok,
+                                                    int window, void* __restrict__ out) {
   constexpr int kCols = D / 4;             // lanes per partial row (16-byte pieces)
   constexpr int kRowsPerLoad = kWave / kCols;
   const int row = blockIdx.x;
@@ -903,8 +933,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   if (counts != nullptr) {
     parts = min(cnt, kstride);
   } else {
-    const int nblk = (L + kBlock - 1) / kBlock;
-    parts = (nblk + part_blocks - 1) / part_blocks;
+    parts = (seq_blocks(L, ntok, window) + part_blocks - 1) / part_blocks;
   }
   if (parts <= 1) return;
   float M = lane < parts ? m0 : -INFINITY;
@@ -1022,6 +1051,7 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
     m.min_blocks = kBalancedMinBlocks;
     m.ntok = a.ntok;
     m.tok_per_pass = pl.tok_per_pass;
+    m.window = a.window;
     m.out = a.out;
     m.kn = q8 ? nullptr : (const uint8_t*)a.k_new;
     m.vn = q8 ? nullptr : (const uint8_t*)a.v_new;
@@ -1073,7 +1103,7 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
   return launch(reduce_kernel<D, OUT>, rgrid, block, st, (const float*)pl.ws_m,
                 (const float*)pl.ws_l, (const float*)pl.ws_o,
                 (const int32_t*)(pl.balanced ? pl.ws_count : nullptr), a.lens, a.max_blocks,
-                a.ntok * hq, pl.part_blocks, pl.kstride, a.out);
+                a.ntok * hq, pl.part_blocks, pl.kstride, a.ntok, a.window, a.out);
 }
 
 }  // namespace

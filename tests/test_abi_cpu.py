@@ -221,3 +221,15 @@ def test_asymmetric_pool_validation():
     q = lambda a, b: lib.pkv_quantize(ctypes.byref(a), ctypes.byref(b), None, 0, None)
     assert q(_u8z(), _u8z()) == 3
     assert q(_cache(), _u8z(num_blocks=9)) == 2
+
+
+def test_window_entry_point_rejects_bad_arguments():
+    lib = pkv.lib()
+    aw = lambda cc, k=2, w=64, qd=1, part=0: lib.pkv_attention_window(
+        ctypes.byref(cc), FAKE, qd, k, w, FAKE, 4, FAKE, 2, 4, ctypes.c_float(0.1), part, None,
+        0, FAKE, 1, None)
+    assert aw(_cache(), w=-1) == 2                       # negative window
+    assert aw(_cache(), k=0) == 2
+    assert aw(_cache(kv_dtype=0), qd=0) == 6             # fp32 pools: not on this path
+    assert aw(_cache(), part=24) == 2
+    assert aw(_cache(), part=pkv.SPLIT_BALANCED) == 5    # needs a workspace

@@ -901,3 +901,106 @@ def test_decode_step_u8z_full_size(cfg):
     got = _out_np(out).reshape(wl.B * wl.Hq, wl.D)[rows]
     err = _cmp(got, ref, TOL["u8z"], "bf16", f"u8z full {wl.name}")
     _say(f"  max abs err {err:.3e}")
+
+
+# ---------------------------------------------------------------- sliding window
+
+WINDOW_CASES = [
+    # (workload, overrides, tokens per sequence, window, partition, layout, quant)
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 1, 1, 0, "split", None),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 1, 17, -1, "blocks", None),
+    (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 1, 100, 64, "split", None),
+    (2, dict(B=9, lo=1, hi=700, pool=600), 1, 256, -1, "blocks", None),
+    (2, dict(B=9, lo=1, hi=700, pool=600), 4, 33, -1, "blocks", None),
+    (2, dict(B=9, lo=1, hi=700, pool=600), 7, 130, 128, "split", None),
+    (3, dict(B=24, median=300, lo=1, hi=1000), 1, 200, -1, "blocks", None),    # G = 8
+    (3, dict(B=24, median=300, lo=1, hi=1000), 3, 64, 0, "split", None),
+    (2, dict(B=4, lo=1, hi=300, pool=200, Hq=8, Hkv=8), 16, 40, -1, "split", None),   # G = 1
+    (2, dict(B=6, lo=1, hi=500, pool=400, D=64), 2, 48, -1, "blocks", None),          # D = 64
+    (4, dict(B=2, L=4096), 1, 1000, 512, "split", None),
+    (5, dict(B=10, prefix=256, suffix_hi=300), 1, 300, -1, "blocks", "i8"),
+    (5, dict(B=10, prefix=256, suffix_hi=300), 2, 77, 256, "split", "fp8"),
+    (5, dict(B=10, prefix=256, suffix_hi=300), 1, 129, -1, "blocks", "u8z"),
+]
+
+
+@pytest.mark.parametrize("cfg,over,k,window,part,layout,quant", WINDOW_CASES)
+def test_attention_window(cfg, over, k, window, part, layout, quant):
+    wl = W.make(cfg, quant=quant, **over)
+    _say(f"attention window: {wl.name} {over} k={k} window={window} part={part} {layout} "
+         f"quant={quant}")
+    rng = np.random.default_rng(300 + k + window)
+    q = _mq_q(rng, wl.B, k, wl.Hq, wl.D)
+    d = W.to_device(wl, layout=layout)
+    cache = _dev_cache(d, wl)
+    kc, vc, ks, vs, kz, vz, kvd = wl.k_pool, wl.v_pool, None, None, None, None, wl.kv_dtype
+    if quant:
+        qc = _qcache(quant, wl.num_blocks, wl.Hkv, 16, wl.D, blocks=layout == "blocks")
+        pkv.quantize(cache, qc)
+        cache = qc
+        kc, ks, kz = _oracle_quantize(wl.k_pool, "bf16", quant)
+        vc, vs, vz = _oracle_quantize(wl.v_pool, "bf16", quant)
+        kvd = quant
+    out = pkv.attention_window(cache, _dev_bf16(q), d["tables"], d["lens"], float(wl.scale),
+                               window, partition_tokens=part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.decode_window(q, "bf16", kc, vc, kvd, wl.tables, wl.lens, wl.scale, window,
+                               k_scale=ks, v_scale=vs, k_zero=kz, v_zero=vz)
+    _cmp(_out_np(out), ref, TOL[quant or "bf16"], "f32", f"window {window} k={k}")
+
+
+@pytest.mark.parametrize("part", [0, -1])
+def test_window_zero_is_the_multi_token_call(part):
+    wl = W.make(2, B=6, lo=1, hi=600, pool=300)
+    q = _dev_bf16(_mq_q(np.random.default_rng(5), wl.B, 3, wl.Hq, wl.D))
+    d = W.to_device(wl, layout="blocks")
+    cache = _dev_cache(d, wl)
+    a = pkv.attention_window(cache, q, d["tables"], d["lens"], float(wl.scale), 0,
+                             partition_tokens=part, out_dtype=torch.float32)
+    b = pkv.attention_multi(cache, q, d["tables"], d["lens"], float(wl.scale),
+                            partition_tokens=part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("part", [0, 128, -1])
+def test_window_never_reads_outside_positions(part):
+    """NaN in every K/V row outside the windows, and the table entries of the
+    blocks before each sequence's first window block pointing past the pool:
+    the output is finite and matches the oracle on the original pool."""
+    k, window = 2, 70
+    wl = W.make(2, B=8, lo=1, hi=900, pool=600)
+    rng = np.random.default_rng(61)
+    q = _mq_q(rng, wl.B, k, wl.Hq, wl.D)
+    ref = oracle.decode_window(q, "bf16", wl.k_pool, wl.v_pool, "bf16", wl.tables, wl.lens,
+                               wl.scale, window)
+    kp, vp, tables = wl.k_pool.copy(), wl.v_pool.copy(), wl.tables.copy()
+    nan = np.uint16(0x7FC0)
+    for s, L in enumerate(wl.lens):
+        first = max(0, int(L) - k - window + 1)
+        for t in range(first):
+            kp[tables[s, t // 16], :, t % 16] = nan
+            vp[tables[s, t // 16], :, t % 16] = nan
+        tables[s, :first // 16] = wl.num_blocks + 1000       # never read
+    d = W.to_device(dataclasses.replace(wl, k_pool=kp, v_pool=vp, tables=tables), layout="blocks")
+    out = pkv.attention_window(_dev_cache(d, wl), _dev_bf16(q), d["tables"], d["lens"],
+                               float(wl.scale), window, partition_tokens=part,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _cmp(_out_np(out), ref, TOL["bf16"], "f32", f"window never reads part={part}")
+
+
+def test_window_full_size_long_context():
+    """Long-context workload (8 sequences of 32k tokens) with a 4096-token
+    window, balanced split, per-block layout: the window's blocks only."""
+    wl = _full_workload(4)
+    _say(f"window full: {wl.name} B={wl.B}")
+    d = W.to_device(wl, layout="blocks")
+    q = d["q"].view(wl.B, 1, wl.Hq, wl.D)
+    out = pkv.attention_window(_dev_cache(d, wl), q, d["tables"], d["lens"], float(wl.scale),
+                               4096, partition_tokens=-1, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.decode_window(wl.q[:, None], wl.q_dtype, wl.k_pool, wl.v_pool, wl.kv_dtype,
+                               wl.tables, wl.lens, wl.scale, 4096)
+    err = _cmp(_out_np(out), ref, TOL["bf16"], "bf16", "window 4096 long")
+    _say(f"  max abs err {err:.3e}")
