@@ -8,7 +8,8 @@ precision, built with gcc) through ctypes on numpy arrays in host memory.
 Storage dtypes (numpy): ``f32`` float32, ``bf16`` uint16 bit patterns,
 ``i8`` int8, ``fp8`` uint8 bit patterns of OCP E4M3, ``u8z`` uint8 codes of the
 asymmetric per-row format (with float32 scales and uint8 zero points
-[NB][Hkv][16]).
+[NB][Hkv][16]), ``fp4`` OCP E2M1 codes packed two per uint8 (element 2i in the
+low nibble), so an fp4 pool is [NB][Hkv][16][D/2].
 
 Every function states the passage it follows in ``oracle.c``; the pins that
 tie each one to the pages or to mathematics are in ``tests/test_oracle_*.py``.
@@ -25,9 +26,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "u8z": 4}
+DTYPES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "u8z": 4, "fp4": 5}
 NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "fp8": np.uint8,
-              "u8z": np.uint8}
+              "u8z": np.uint8, "fp4": np.uint8}
 
 _lib = None
 
@@ -60,6 +61,10 @@ def _load():
         lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.orc_e4m3_from_float.restype = ctypes.c_uint8
         lib.orc_e4m3_from_float.argtypes = [F]
+        lib.orc_e2m1_to_double.restype = ctypes.c_double
+        lib.orc_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        lib.orc_e2m1_from_float.restype = ctypes.c_uint8
+        lib.orc_e2m1_from_float.argtypes = [F]
         lib.orc_slot_of.restype = ctypes.c_int32
         lib.orc_slot_of.argtypes = [P, I, I, I, I]
         lib.orc_slot_mapping.restype = None
@@ -140,6 +145,28 @@ def e4m3_from_f32(x) -> np.ndarray:
     return out
 
 
+def e2m1_to_f64(codes) -> np.ndarray:
+    f = np.vectorize(lambda c: _load().orc_e2m1_to_double(int(c)), otypes=[np.float64])
+    return f(np.asarray(codes, dtype=np.uint8))
+
+
+def e2m1_from_f32(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
+    for i in range(flat_in.size):
+        flat_out[i] = lib.orc_e2m1_from_float(float(flat_in[i]))
+    return out
+
+
+def pool_dims(pool, kv_dtype):
+    """(num_blocks, Hkv, block_size, head_dim) of a stored pool (fp4 pools hold
+    head_dim / 2 bytes per row)."""
+    NB, Hkv, bs, last = pool.shape
+    return NB, Hkv, bs, last * 2 if kv_dtype == "fp4" else last
+
+
 def slot_mapping(block_tables, context_lens, block_size=16) -> np.ndarray:
     """Slot of each sequence's newest token (page on KV-cache management, section 二)."""
     bt = _c(block_tables, np.int32)
@@ -168,7 +195,7 @@ def copy_blocks(k_cache, v_cache, dtype, pairs, k_scale=None, v_scale=None, k_ze
     (src, dst) physical block ids, applied in order; scales (and, for the
     asymmetric format, zero points) travel with their block."""
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
-    NB, Hkv, bs, D = k_cache.shape
+    NB, Hkv, bs, D = pool_dims(k_cache, dtype)
     pr = _c(pairs, np.int32).reshape(-1, 2)
     for sc in (k_scale, v_scale):
         assert sc is None or (sc.dtype == np.float32 and sc.flags.c_contiguous)
@@ -181,14 +208,15 @@ def copy_blocks(k_cache, v_cache, dtype, pairs, k_scale=None, v_scale=None, k_ze
 
 def gather(k_cache, v_cache, dtype, block_tables, context_lens):
     """Contiguous [sum L][Hkv][D] copies of each sequence's K and V."""
-    NB, Hkv, bs, D = k_cache.shape
+    NB, Hkv, bs, D = pool_dims(k_cache, dtype)
     bt = _c(block_tables, np.int32)
     lens = _c(context_lens, np.int32)
     cu = np.zeros(lens.shape[0] + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     total = int(cu[-1])
-    ko = np.zeros((total, Hkv, D), dtype=NP_STORAGE[dtype])
-    vo = np.zeros((total, Hkv, D), dtype=NP_STORAGE[dtype])
+    row = k_cache.shape[3]          # stored elements (bytes for fp4) per row
+    ko = np.zeros((total, Hkv, row), dtype=NP_STORAGE[dtype])
+    vo = np.zeros((total, Hkv, row), dtype=NP_STORAGE[dtype])
     _load().orc_gather(_ptr(_c(k_cache, NP_STORAGE[dtype])), _ptr(_c(v_cache, NP_STORAGE[dtype])),
                        DTYPES[dtype], Hkv, bs, D, _ptr(bt), bt.shape[1], _ptr(lens), _ptr(cu),
                        lens.shape[0], _ptr(ko), _ptr(vo))
@@ -220,7 +248,7 @@ def decode(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens, s
                                                         k_scale, v_scale, block_tables,
                                                         context_lens, k_zero, v_zero)
     B, Hq, D = qa.shape
-    NB, Hkv, bs, D2 = kc.shape
+    NB, Hkv, bs, D2 = pool_dims(kc, kv_dtype)
     assert D == D2 and Hq % Hkv == 0
     out = np.zeros((B, Hq, D), dtype=np.float64)
     rc = _load().orc_decode(_ptr(qa), DTYPES[q_dtype], _ptr(kc), _ptr(vc), DTYPES[kv_dtype],
@@ -242,7 +270,7 @@ def decode_multi(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_l
                                                        k_cache, v_cache, kv_dtype, k_scale,
                                                        v_scale, block_tables, context_lens,
                                                        k_zero, v_zero)
-    NB, Hkv, bs, D2 = kc.shape
+    NB, Hkv, bs, D2 = pool_dims(kc, kv_dtype)
     assert D == D2 and Hq % Hkv == 0 and lens.shape[0] == B
     out = np.zeros((B, ntok, Hq, D), dtype=np.float64)
     rc = _load().orc_decode_multi(_ptr(qa), DTYPES[q_dtype], _ptr(kc), _ptr(vc), DTYPES[kv_dtype],
@@ -265,7 +293,7 @@ def decode_window(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_
                                                        k_cache, v_cache, kv_dtype, k_scale,
                                                        v_scale, block_tables, context_lens,
                                                        k_zero, v_zero)
-    NB, Hkv, bs, D2 = kc.shape
+    NB, Hkv, bs, D2 = pool_dims(kc, kv_dtype)
     assert D == D2 and Hq % Hkv == 0 and lens.shape[0] == B
     out = np.zeros((B, ntok, Hq, D), dtype=np.float64)
     rc = _load().orc_decode_window(_ptr(qa), DTYPES[q_dtype], _ptr(kc), _ptr(vc),
@@ -295,7 +323,7 @@ def decode_rows(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_le
                                                         k_scale, v_scale, block_tables,
                                                         context_lens, k_zero, v_zero)
     B, Hq, D = qa.shape
-    NB, Hkv, bs, _ = kc.shape
+    NB, Hkv, bs, _ = pool_dims(kc, kv_dtype)
     r = _c(rows, np.int64)
     out = np.zeros((r.shape[0], D), dtype=np.float64)
     rc = _load().orc_decode_rows(_ptr(qa), DTYPES[q_dtype], _ptr(kc), _ptr(vc), DTYPES[kv_dtype],
@@ -314,7 +342,7 @@ def decode_partials(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, contex
                                                         k_scale, v_scale, block_tables,
                                                         context_lens, k_zero, v_zero)
     B, Hq, D = qa.shape
-    NB, Hkv, bs, _ = kc.shape
+    NB, Hkv, bs, _ = pool_dims(kc, kv_dtype)
     n_parts = max(1, -(-int(lens.max(initial=0)) // partition_tokens))
     m = np.zeros((B, Hq, n_parts), dtype=np.float64)
     l = np.zeros((B, Hq, n_parts), dtype=np.float64)
@@ -341,10 +369,12 @@ def combine_partials(m, l, o) -> np.ndarray:
 
 
 def quantize(src, src_dtype, dst_dtype, block_ids=None):
-    """Symmetric per-(block, head) quantization of one pool; returns (codes, scales)."""
+    """Symmetric per-(block, head) quantization of one pool; returns (codes, scales)
+    (fp4 codes packed two per byte, [NB][Hkv][16][D/2])."""
     s = _c(src, NP_STORAGE[src_dtype])
     NB, Hkv, bs, D = s.shape
-    codes = np.zeros(s.shape, dtype=NP_STORAGE[dst_dtype])
+    codes = np.zeros((NB, Hkv, bs, D // 2 if dst_dtype == "fp4" else D),
+                     dtype=NP_STORAGE[dst_dtype])
     scales = np.zeros((NB, Hkv), dtype=np.float32)
     ids = None if block_ids is None else _c(block_ids, np.int32)
     rc = _load().orc_quantize(_ptr(s), DTYPES[src_dtype], _ptr(codes), DTYPES[dst_dtype],

@@ -48,7 +48,7 @@
 #endif
 
 /* Element type codes understood by the oracle (its own numbering). */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_U8Z = 4 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3, ORC_U8Z = 4, ORC_FP4 = 5 };
 
 /* Number of threads the parallel loops below use (1 without OpenMP).       */
 int orc_max_threads(void) {
@@ -59,13 +59,16 @@ int orc_max_threads(void) {
 #endif
 }
 
-static size_t orc_elem_bytes(int dtype) {
+/* Bits of one stored element; FP4 codes are packed two to a byte, element
+ * 2i in the low nibble and element 2i + 1 in the high nibble.               */
+static size_t orc_elem_bits(int dtype) {
   switch (dtype) {
-    case ORC_F32: return 4;
-    case ORC_BF16: return 2;
-    case ORC_I8: return 1;
-    case ORC_FP8: return 1;
-    case ORC_U8Z: return 1;
+    case ORC_F32: return 32;
+    case ORC_BF16: return 16;
+    case ORC_I8: return 8;
+    case ORC_FP8: return 8;
+    case ORC_U8Z: return 8;
+    case ORC_FP4: return 4;
   }
   return 0;
 }
@@ -145,6 +148,33 @@ uint8_t orc_e4m3_from_float(float x) {
   return (uint8_t)((sign << 7) | mag);
 }
 
+/* OCP 4-bit float E2M1: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa
+ * bit; exponent field 0 encodes the subnormals m/2 (0 and 0.5), every other
+ * pattern (1 + m/2) * 2^(e-1); no infinities, no NaN.  So the eight
+ * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.                                */
+double orc_e2m1_to_double(uint8_t code) {
+  int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -mag : mag;
+}
+
+/* Nearest E2M1 code of x, ties to the code with an even mantissa bit,
+ * magnitudes above 6 clamped to 6; the sign bit copies the sign of x.  The
+ * positive codes 0..7 are in increasing order of value, so the nearest one
+ * is found by scanning them.  NaN input is outside the oracle's domain.     */
+uint8_t orc_e2m1_from_float(float x) {
+  double a = fabs((double)x);
+  int sign = signbit(x) ? 1 : 0;
+  int best = 0;
+  if (a >= 6.0) return (uint8_t)((sign << 3) | 7);   /* saturate */
+  for (int c = 1; c < 8; ++c) {
+    double dc = fabs(orc_e2m1_to_double((uint8_t)c) - a);
+    double db = fabs(orc_e2m1_to_double((uint8_t)best) - a);
+    if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)((sign << 3) | best);
+}
+
 /* Widen one stored KV element to double.  Quantized codes are multiplied by
  * their (block, head) scale, as in [MGMT] section 四 (dequantize: code times
  * scale); the product of an 8-bit code and a binary32 scale is exact in
@@ -158,6 +188,10 @@ static double orc_load_elem(const void* base, size_t idx, int dtype, double scal
     case ORC_I8: return (double)((const int8_t*)base)[idx] * scale;
     case ORC_FP8: return orc_e4m3_to_double(((const uint8_t*)base)[idx]) * scale;
     case ORC_U8Z: return ((double)((const uint8_t*)base)[idx] - zero) * scale;
+    case ORC_FP4: {
+      uint8_t byte = ((const uint8_t*)base)[idx / 2];
+      return orc_e2m1_to_double((uint8_t)((idx & 1) ? byte >> 4 : byte & 15)) * scale;
+    }
   }
   return NAN;
 }
@@ -218,8 +252,8 @@ void orc_slot_mapping(const int32_t* block_tables, int max_blocks, const int32_t
 void orc_cache_write(void* k_cache, void* v_cache, int dtype, int num_blocks, int Hkv, int bs,
                      int D, const void* k_new, const void* v_new, const int32_t* slot_mapping,
                      int n) {
-  size_t eb = orc_elem_bytes(dtype);
-  size_t row = (size_t)D * eb;
+  size_t bits = orc_elem_bits(dtype);
+  size_t row = (size_t)D * bits / 8;
   (void)num_blocks;
   for (int i = 0; i < n; ++i) {
     int32_t slot = slot_mapping[i];
@@ -227,8 +261,8 @@ void orc_cache_write(void* k_cache, void* v_cache, int dtype, int num_blocks, in
     for (int g = 0; g < Hkv; ++g) {
       size_t dst = orc_pool_offset((size_t)(slot / bs), (size_t)g, (size_t)(slot % bs), Hkv, bs, D);
       size_t src = ((size_t)i * Hkv + g) * (size_t)D;
-      memcpy((char*)k_cache + dst * eb, (const char*)k_new + src * eb, row);
-      memcpy((char*)v_cache + dst * eb, (const char*)v_new + src * eb, row);
+      memcpy((char*)k_cache + dst * bits / 8, (const char*)k_new + src * bits / 8, row);
+      memcpy((char*)v_cache + dst * bits / 8, (const char*)v_new + src * bits / 8, row);
     }
   }
 }
@@ -243,8 +277,7 @@ void orc_cache_write(void* k_cache, void* v_cache, int dtype, int num_blocks, in
 void orc_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                      uint8_t* k_zero, uint8_t* v_zero, int dtype, int num_blocks, int Hkv, int bs,
                      int D, const int32_t* pairs, int n) {
-  size_t eb = orc_elem_bytes(dtype);
-  size_t blk = (size_t)Hkv * bs * D * eb;
+  size_t blk = (size_t)Hkv * bs * D * orc_elem_bits(dtype) / 8;
   /* parameters per block: one scale per head, or (asymmetric) one scale and
    * one zero point per (head, row)                                           */
   size_t np = dtype == ORC_U8Z ? (size_t)Hkv * bs : (size_t)Hkv;
@@ -269,16 +302,16 @@ void orc_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scal
 void orc_gather(const void* k_cache, const void* v_cache, int dtype, int Hkv, int bs, int D,
                 const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
                 const int32_t* cu_seqlens, int num_seqs, void* k_out, void* v_out) {
-  size_t eb = orc_elem_bytes(dtype);
-  size_t row = (size_t)D * eb;
+  size_t bits = orc_elem_bits(dtype);
+  size_t row = (size_t)D * bits / 8;
   for (int s = 0; s < num_seqs; ++s) {
     for (int t = 0; t < context_lens[s]; ++t) {
       int32_t b = block_tables[(size_t)s * max_blocks + t / bs];
       for (int g = 0; g < Hkv; ++g) {
         size_t src = orc_pool_offset((size_t)b, (size_t)g, (size_t)(t % bs), Hkv, bs, D);
         size_t dst = ((size_t)(cu_seqlens[s] + t) * Hkv + g) * (size_t)D;
-        memcpy((char*)k_out + dst * eb, (const char*)k_cache + src * eb, row);
-        memcpy((char*)v_out + dst * eb, (const char*)v_cache + src * eb, row);
+        memcpy((char*)k_out + dst * bits / 8, (const char*)k_cache + src * bits / 8, row);
+        memcpy((char*)v_out + dst * bits / 8, (const char*)v_cache + src * bits / 8, row);
       }
     }
   }
@@ -523,18 +556,19 @@ void orc_combine_partials(const double* m, const double* l, const double* o, int
 /* ------------------------------------------------------------------------ */
 /* KV quantization, symmetric with one binary32 scale per (block, KV head)
  * tile of block_size x head_dim values ([MGMT] section 四 quantizes cached
- * K/V to 8 bits and restores them as code * scale; the per-(block, head)
- * symmetric grouping is this build's reading).  With a = max |x| over the
- * whole tile (every row, used or not):
+ * K/V to 8 bits and restores them as code * scale; [CSDN] section 三 adds
+ * FP4; the per-(block, head) symmetric grouping is this build's reading).
+ * With a = max |x| over the whole tile (every row, used or not):
  *   INT8:  scale = a / 127,  code = clamp(rint(x / scale), -127, 127)
  *   FP8:   scale = a / 448,  code = E4M3(x / scale), nearest-even, saturating
+ *   FP4:   scale = a / 6,    code = E2M1(x / scale), nearest-even, saturating
  * a == 0 gives scale 0 and all codes 0.  Divisions and rint are binary32
  * operations with round-to-nearest-even, matching the stored scale format.
  * block_ids == NULL means every block.                                      */
 int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, float* scales,
                  int num_blocks, int Hkv, int bs, int D, const int32_t* block_ids, int n_ids) {
   int n = block_ids ? n_ids : num_blocks;
-  if (dst_dtype != ORC_I8 && dst_dtype != ORC_FP8) return -1;
+  if (dst_dtype != ORC_I8 && dst_dtype != ORC_FP8 && dst_dtype != ORC_FP4) return -1;
   if (src_dtype != ORC_F32 && src_dtype != ORC_BF16) return -1;
 #pragma omp parallel for schedule(static)
   for (long it = 0; it < (long)n * Hkv; ++it) {
@@ -548,7 +582,7 @@ int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, flo
       float ax = fabsf(x);
       if (ax > a) a = ax;
     }
-    sc = (dst_dtype == ORC_I8) ? a / 127.0f : a / 448.0f;
+    sc = (dst_dtype == ORC_I8) ? a / 127.0f : (dst_dtype == ORC_FP8) ? a / 448.0f : a / 6.0f;
     scales[(size_t)b * Hkv + g] = sc;
     for (size_t i = 0; i < cnt; ++i) {
       float x = (float)orc_load_elem(src, base + i, src_dtype, 1.0, 0.0);
@@ -557,8 +591,16 @@ int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, flo
         if (r > 127.0f) r = 127.0f;
         if (r < -127.0f) r = -127.0f;
         ((int8_t*)dst_k)[base + i] = (int8_t)r;
-      } else {
+      } else if (dst_dtype == ORC_FP8) {
         ((uint8_t*)dst_k)[base + i] = (a == 0.0f) ? 0 : orc_e4m3_from_float(x / sc);
+      } else {
+        /* element base + i goes to nibble (base + i) & 1 of byte (base + i) / 2 */
+        uint8_t c = (a == 0.0f) ? 0 : orc_e2m1_from_float(x / sc);
+        uint8_t* byte = (uint8_t*)dst_k + (base + i) / 2;
+        if ((base + i) & 1)
+          *byte = (uint8_t)((*byte & 0x0F) | (c << 4));
+        else
+          *byte = (uint8_t)((*byte & 0xF0) | c);
       }
     }
   }
