@@ -55,11 +55,11 @@ def algorithmic_bytes(wl, ntok=1):
     workloads with a new token its K/V row read and written plus its slot."""
     import numpy as np
 
-    e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1}[wl.quant or wl.kv_dtype]
+    e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1, "fp4": 0.5}[wl.quant or wl.kv_dtype]
     e_q = {"f32": 4, "bf16": 2}[wl.q_dtype]
     L = wl.lens.astype(np.int64)
     nblk = (L + 15) // 16
-    kv = int(L.sum()) * wl.Hkv * wl.D * 2 * e_kv
+    kv = int(int(L.sum()) * wl.Hkv * wl.D * 2 * e_kv)
     tables = int(nblk.sum()) * 4
     if wl.quant == "u8z":       # a binary32 scale and a uint8 zero point per K and V row
         scales = int(L.sum()) * wl.Hkv * 2 * 5
@@ -73,7 +73,7 @@ def algorithmic_bytes(wl, ntok=1):
         # new K/V rows read (in the pool's type, or q's for a quantizing
         # append) and written into the pool, with their row parameters
         e_new = e_q if wl.quant == "u8z" else e_kv
-        write = wl.B * wl.Hkv * wl.D * 2 * (e_new + e_kv)
+        write = int(wl.B * wl.Hkv * wl.D * 2 * (e_new + e_kv))
         if wl.quant == "u8z":
             write += wl.B * wl.Hkv * 2 * 5
     return dict(attention=attention, kv=kv, write=write, step=attention + write)
@@ -117,6 +117,7 @@ class Replica:
             NB, Hkv, bs, D = d["k_pool"].shape
             qt = torch.int8 if wl.quant == "i8" else torch.uint8
             pshape = (NB, Hkv, bs) if wl.quant == "u8z" else (NB, Hkv)
+            Ds = D // 2 if wl.quant == "fp4" else D
             ks = torch.empty(pshape, dtype=torch.float32, device="cuda")
             vs = torch.empty_like(ks)
             kz = vz = None
@@ -125,10 +126,10 @@ class Replica:
                 vz = torch.empty_like(kz)
             if layout == "blocks":
                 qcache = pkv.PagedCache.from_blocks(
-                    torch.empty((NB, 2, Hkv, bs, D), dtype=qt, device="cuda"), wl.quant, ks, vs,
+                    torch.empty((NB, 2, Hkv, bs, Ds), dtype=qt, device="cuda"), wl.quant, ks, vs,
                     kz, vz)
             else:
-                kq = torch.empty((NB, Hkv, bs, D), dtype=qt, device="cuda")
+                kq = torch.empty((NB, Hkv, bs, Ds), dtype=qt, device="cuda")
                 qcache = pkv.PagedCache(kq, torch.empty_like(kq), wl.quant, ks, vs, kz, vz)
             pkv.quantize(cache, qcache)
             for k in ("kv", "k_pool", "v_pool"):
@@ -239,16 +240,18 @@ def op_bench(args):
         quant = args.quant or "i8"
         qt = torch.int8 if quant == "i8" else torch.uint8
         rows = quant == "u8z"
+        Ds = D // 2 if quant == "fp4" else D
+        e_q = 0.5 if quant == "fp4" else 1
         pshape = (NB, Hkv, bs) if rows else (NB, Hkv)
         ks = torch.empty(pshape, dtype=torch.float32, device="cuda")
         vs = torch.empty_like(ks)
         kz = torch.empty(pshape, dtype=torch.uint8, device="cuda") if rows else None
         vz = torch.empty_like(kz) if rows else None
         dst = pkv.PagedCache.from_blocks(
-            torch.empty((NB, 2, Hkv, bs, D), dtype=qt, device="cuda"), quant, ks, vs, kz, vz)
+            torch.empty((NB, 2, Hkv, bs, Ds), dtype=qt, device="cuda"), quant, ks, vs, kz, vz)
         fn = lambda: pkv.quantize(cache, dst)
-        nbytes = 2 * NB * Hkv * bs * D * (e + 1) + (2 * NB * Hkv * bs * 5 if rows
-                                                    else 2 * NB * Hkv * 4)
+        nbytes = int(2 * NB * Hkv * bs * D * (e + e_q)) + (2 * NB * Hkv * bs * 5 if rows
+                                                           else 2 * NB * Hkv * 4)
         what = f"pkv_quantize {wl.kv_dtype}->{quant}, all {NB} blocks"
     else:
         rng = np.random.default_rng(0)
@@ -288,10 +291,11 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=(1, 2, 3, 4, 5))
-    ap.add_argument("--quant", choices=("i8", "fp8", "u8z"), default=None,
-                    help="8-bit pool format: for the quantized-prefix workload (5; default i8) "
-                         "i8, fp8 or u8z (asymmetric per-row uint8); for the decode-step "
-                         "workloads (2-4) u8z, whose step then appends the new token quantized")
+    ap.add_argument("--quant", choices=("i8", "fp8", "u8z", "fp4"), default=None,
+                    help="quantized pool format: for the quantized-prefix workload (5; default "
+                         "i8) i8, fp8, u8z (asymmetric per-row uint8) or fp4 (E2M1); for the "
+                         "decode-step workloads (2-4) u8z, whose step then appends the new "
+                         "token quantized")
     ap.add_argument("--replicas", type=int, default=0,
                     help="input copies cycled through (0: enough for 1.3 GB of pools)")
     ap.add_argument("--partition", type=int, default=None,
@@ -338,8 +342,8 @@ def main():
             wl = dataclasses.replace(wl, quant=args.quant)
     part = args.partition if args.partition is not None else pkv.default_partition(
         wl.B, wl.Hkv, wl.max_blocks)
-    e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1}[wl.quant or wl.kv_dtype]
-    pool_bytes = wl.num_blocks * wl.Hkv * 16 * wl.D * 2 * e_kv
+    e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1, "fp4": 0.5}[wl.quant or wl.kv_dtype]
+    pool_bytes = int(wl.num_blocks * wl.Hkv * 16 * wl.D * 2 * e_kv)
     n_rep = args.replicas or max(2, min(8, math.ceil(1.3e9 / pool_bytes) + 1))
     reps = [Replica(wl, part, args.layout, args.tokens) for _ in range(n_rep)]
     print(f"# workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "

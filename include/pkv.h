@@ -67,8 +67,11 @@ enum {
   PKV_BF16 = 1,     /* bfloat16 (upper half of binary32)                        */
   PKV_I8 = 2,       /* int8 code, value = code * scale                          */
   PKV_FP8_E4M3 = 3, /* OCP E4M3 "fn" code (bias 7, max 448, no inf), value = decoded * scale */
-  PKV_U8_ZP = 4     /* uint8 code with a binary32 scale and a uint8 zero point per
+  PKV_U8_ZP = 4,    /* uint8 code with a binary32 scale and a uint8 zero point per
                        (block, KV head, row): value = (code - zero) * scale */
+  PKV_FP4_E2M1 = 5  /* OCP E2M1 4-bit code (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+                       negatives), two per byte, element 2i in the low nibble of
+                       byte i of its row: value = decoded * scale */
 };
 
 #define PKV_BLOCK_SIZE 16
@@ -93,10 +96,13 @@ enum {
  *     and block_stride = 2 * num_kv_heads * block_size * head_dim; that
  *     layout reads fastest on MI355X (the eight heads' K and V of one block
  *     are one contiguous run).  Must be 0 or at least num_kv_heads *
- *     block_size * head_dim, with block_stride * element size a multiple of
- *     16 bytes; the K and V regions of all blocks must not overlap.
+ *     block_size * head_dim, even, with its size in bytes a multiple of 16;
+ *     the K and V regions of all blocks must not overlap.  Element offsets
+ *     of PKV_FP4_E2M1 pools are halved to give byte offsets (and k_cache /
+ *     v_cache point at bytes).
  *   k_scale, v_scale: [num_blocks][num_kv_heads] binary32 scales, required for
- *     PKV_I8 / PKV_FP8_E4M3; for PKV_U8_ZP [num_blocks][num_kv_heads][block_size]
+ *     PKV_I8 / PKV_FP8_E4M3 / PKV_FP4_E2M1; for PKV_U8_ZP
+ *     [num_blocks][num_kv_heads][block_size]
  *     (one per row); ignored for float pools.
  *   k_zero, v_zero: [num_blocks][num_kv_heads][block_size] uint8 zero points,
  *     required for PKV_U8_ZP and ignored otherwise.  Scales and zero points are
@@ -221,9 +227,10 @@ int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
  *     that is nonzero (contents need not be initialised), else may be NULL
  *   out: device [num_seqs][num_q_heads][head_dim] of out_dtype.
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, I8),
- * (BF16, FP8_E4M3), (BF16, U8_ZP); out_dtype F32 or BF16 (bf16 rounded to
- * nearest even).  8-bit pools are restored as code * scale (I8, FP8_E4M3) or
- * (code - zero) * scale (U8_ZP) on the fly; rows past L are never used, so
+ * (BF16, FP8_E4M3), (BF16, U8_ZP), (BF16, FP4_E2M1); out_dtype F32 or BF16
+ * (bf16 rounded to nearest even).  Quantized pools are restored as
+ * code * scale (I8, FP8_E4M3, FP4_E2M1) or (code - zero) * scale (U8_ZP) on the
+ * fly; rows past L are never used, so
  * their codes and parameters may hold anything. */
 int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -302,6 +309,9 @@ int pkv_attention_window(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
  *   PKV_I8:       scale = a / 127, code = clamp(rint(x / scale), -127, 127)
  *   PKV_FP8_E4M3: scale = a / 448, code = nearest E4M3 (ties to even), values
  *                 beyond 448 in magnitude saturate to +-448
+ *   PKV_FP4_E2M1: scale = a / 6, code = nearest E2M1 (ties to the even
+ *                 mantissa bit), magnitudes beyond 6 saturate to +-6 ([CSDN]
+ *                 section 三: FP4 KV)
  * a == 0 gives scale 0 and zero codes.  With dst PKV_U8_ZP ([MGMT] section 四,
  * KVQuantizationCache with per-channel parameters) every (block, head, row) of
  * head_dim values is quantized on its own, as pkv_cache_write_quant states,
@@ -309,8 +319,8 @@ int pkv_attention_window(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
  * Divisions and rounding are binary32, round-to-nearest-even.  Quantizes
  * src->k_cache into dst->k_cache (scales to dst->k_scale, zero points to
  * dst->k_zero) and src->v_cache into dst->v_cache (dst->v_scale, v_zero).
- *   src: kv_dtype F32 or BF16; dst: kv_dtype I8, FP8_E4M3 or U8_ZP, same
- *   geometry
+ *   src: kv_dtype F32 or BF16; dst: kv_dtype I8, FP8_E4M3, U8_ZP or FP4_E2M1,
+ *   same geometry
  *   block_ids: device int32 [n_ids], or NULL for every block (n_ids ignored). */
 int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* block_ids,
                  int32_t n_ids, void* stream);

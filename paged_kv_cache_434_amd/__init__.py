@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 SPLIT_BALANCED = -1     # partition_tokens value: balanced split (PKV_SPLIT_BALANCED)
-DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "u8z": 4}
+DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "u8z": 4, "fp4": 5}
 BLOCK_SIZE = 16
 
 _lib = None
@@ -115,7 +115,7 @@ def _torch():
 def _storage_dtype(name: str):
     torch = _torch()
     return {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8,
-            "fp8": torch.uint8, "u8z": torch.uint8}[name]
+            "fp8": torch.uint8, "u8z": torch.uint8, "fp4": torch.uint8}[name]
 
 
 def _ptr(t) -> Optional[int]:
@@ -141,11 +141,12 @@ def _need(t, name, dtype=None, ndim=None):
 
 
 class PagedCache:
-    """One layer's K and V pools and, for 8-bit pools, their binary32 scales:
-    [num_blocks][Hkv] for ``i8`` / ``fp8``, [num_blocks][Hkv][16] plus uint8
-    zero points of the same shape for ``u8z`` (the asymmetric per-row format).
-    ``k_cache`` / ``v_cache`` are [num_blocks][Hkv][16][D] tensors whose last
-    three dimensions are dense; the block dimension may be strided, so both
+    """One layer's K and V pools and, for quantized pools, their binary32 scales:
+    [num_blocks][Hkv] for ``i8`` / ``fp8`` / ``fp4``, [num_blocks][Hkv][16] plus
+    uint8 zero points of the same shape for ``u8z`` (the asymmetric per-row
+    format).  ``k_cache`` / ``v_cache`` are [num_blocks][Hkv][16][D] tensors
+    ([num_blocks][Hkv][16][D/2] uint8 for ``fp4``, two codes per byte) whose
+    last three dimensions are dense; the block dimension may be strided, so both
     separate dense pools and the two halves of one [num_blocks][2][Hkv][16][D]
     allocation (see ``from_blocks``) are accepted.  Holds references so the
     tensors outlive the descriptor."""
@@ -169,7 +170,9 @@ class PagedCache:
         if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
             raise ValueError("k_cache and v_cache shapes or strides differ")
         NB, Hkv, bs, D = k_cache.shape
-        if kv_dtype in ("i8", "fp8"):
+        if kv_dtype == "fp4":
+            D *= 2
+        if kv_dtype in ("i8", "fp8", "fp4"):
             _need(k_scale, "k_scale", torch.float32, 2)
             _need(v_scale, "v_scale", torch.float32, 2)
             if tuple(k_scale.shape) != (NB, Hkv) or k_scale.shape != v_scale.shape:
@@ -183,7 +186,7 @@ class PagedCache:
                     raise ValueError(f"{name} must be [num_blocks][num_kv_heads][block_size]")
         else:
             k_zero = v_zero = None
-        stride = int(k_cache.stride(0))
+        stride = int(k_cache.stride(0)) * (2 if kv_dtype == "fp4" else 1)   # in elements
         self.block_stride = 0 if stride == Hkv * bs * D else stride
         self.k_cache, self.v_cache, self.k_scale, self.v_scale = k_cache, v_cache, k_scale, v_scale
         self.k_zero, self.v_zero = k_zero, v_zero
@@ -477,7 +480,7 @@ def gather(cache: PagedCache, block_tables, context_lens, cu_seqlens, total_toke
     _need(context_lens, "context_lens", torch.int32, 1)
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     B = context_lens.shape[0]
-    shape = (total_tokens, cache.num_kv_heads, cache.head_dim)
+    shape = (total_tokens, cache.num_kv_heads, cache.k_cache.shape[3])
     ko = torch.empty(shape, dtype=cache.k_cache.dtype, device=cache.k_cache.device)
     vo = torch.empty(shape, dtype=cache.k_cache.dtype, device=cache.k_cache.device)
     _check("pkv_gather",

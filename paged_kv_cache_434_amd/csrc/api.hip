@@ -14,13 +14,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_cache(const pkv_cache_t* c) {
   if (!c) return PKV_ERR_NULL;
-  if (elem_bytes(c->kv_dtype) == 0) return PKV_ERR_DTYPE;
+  if (elem_bits(c->kv_dtype) == 0) return PKV_ERR_DTYPE;
   if (c->block_size != PKV_BLOCK_SIZE || c->num_blocks < 0 || c->num_kv_heads <= 0 ||
       c->head_dim <= 0)
     return PKV_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!c->k_cache || !c->v_cache) return PKV_ERR_NULL;
-  if (is_q8(c->kv_dtype) && (!c->k_scale || !c->v_scale)) return PKV_ERR_NULL;
+  if (is_quantized(c->kv_dtype) && (!c->k_scale || !c->v_scale)) return PKV_ERR_NULL;
   if (c->kv_dtype == PKV_U8_ZP) {
     if (!c->k_zero || !c->v_zero) return PKV_ERR_NULL;
     // zero points are read four rows per 32-bit load
@@ -30,7 +30,8 @@ int check_cache(const pkv_cache_t* c) {
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_UNSUPPORTED;
   if (c->block_stride != 0) {
     if (c->block_stride < block_elems(*c)) return PKV_ERR_SHAPE;
-    if ((c->block_stride * (int64_t)elem_bytes(c->kv_dtype)) % 16 != 0) return PKV_ERR_UNSUPPORTED;
+    if (c->block_stride % 2 != 0 || elems_to_bytes(c->block_stride, c->kv_dtype) % 16 != 0)
+      return PKV_ERR_UNSUPPORTED;
   }
   return PKV_OK;
 }
@@ -62,9 +63,9 @@ int pkv_version(void) { return 100; }
 
 uint64_t pkv_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                         int32_t head_dim, int32_t dtype) {
-  size_t eb = elem_bytes(dtype);
-  if (eb == 0 || num_blocks < 0 || num_kv_heads < 0 || block_size < 0 || head_dim < 0) return 0;
-  return (uint64_t)num_blocks * num_kv_heads * block_size * head_dim * eb;
+  const int bits = elem_bits(dtype);
+  if (bits == 0 || num_blocks < 0 || num_kv_heads < 0 || block_size < 0 || head_dim < 0) return 0;
+  return (uint64_t)num_blocks * num_kv_heads * block_size * head_dim * bits / 8;
 }
 
 int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -145,11 +146,11 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                          int32_t ntok = 1, int32_t window = 0) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
-  if (elem_bytes(q_dtype) == 0 || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
+  if ((q_dtype != PKV_F32 && q_dtype != PKV_BF16) || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
     return PKV_ERR_DTYPE;
   const int kv = cache->kv_dtype;
   const bool pair_ok = (q_dtype == PKV_F32 && kv == PKV_F32) ||
-                       (q_dtype == PKV_BF16 && (kv == PKV_BF16 || is_q8(kv)));
+                       (q_dtype == PKV_BF16 && (kv == PKV_BF16 || is_quantized(kv)));
   if (!pair_ok) return PKV_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || !split_ok(partition_tokens) ||
       max_blocks_per_seq > INT_MAX / PKV_BLOCK_SIZE)
@@ -242,7 +243,7 @@ int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* 
   if (rc != PKV_OK) return rc;
   rc = check_cache(dst);
   if (rc != PKV_OK) return rc;
-  if ((src->kv_dtype != PKV_F32 && src->kv_dtype != PKV_BF16) || !is_q8(dst->kv_dtype))
+  if ((src->kv_dtype != PKV_F32 && src->kv_dtype != PKV_BF16) || !is_quantized(dst->kv_dtype))
     return PKV_ERR_DTYPE;
   if (src->num_blocks != dst->num_blocks || src->num_kv_heads != dst->num_kv_heads ||
       src->head_dim != dst->head_dim)
@@ -259,7 +260,7 @@ int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t n, v
   if (n < 0 || n > 65535 * 1024) return PKV_ERR_SHAPE;
   if (n == 0) return PKV_OK;
   if (!pairs) return PKV_ERR_NULL;
-  if (block_elems(*cache) * (int64_t)elem_bytes(cache->kv_dtype) / 16 > (int64_t)INT_MAX)
+  if (elems_to_bytes(block_elems(*cache), cache->kv_dtype) / 16 > (int64_t)INT_MAX)
     return PKV_ERR_SHAPE;
   return launch_copy_blocks(*cache, pairs, n, static_cast<hipStream_t>(stream));
 }

@@ -110,9 +110,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 }  // namespace
 
 int launch_copy_blocks(const pkv_cache_t& c, const int32_t* pairs, int n, hipStream_t st) {
-  const bool q8 = is_q8(c.kv_dtype);
+  const bool q8 = is_quantized(c.kv_dtype);
   const bool rows = c.kv_dtype == PKV_U8_ZP;
-  const int chunks = (int)(block_elems(c) * (int64_t)elem_bytes(c.kv_dtype) / 16);
+  const int chunks = (int)(elems_to_bytes(block_elems(c), c.kv_dtype) / 16);
   dim3 grid((unsigned)n, 2), block(256);
   return launch(copy_blocks_kernel, grid, block, st, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache,
                 q8 ? c.k_scale : nullptr, q8 ? c.v_scale : nullptr, rows ? c.k_zero : nullptr,
@@ -128,7 +128,7 @@ int launch_slot_mapping(const int32_t* tables, int max_blocks, const int32_t* le
 
 int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,
                        int n, hipStream_t st) {
-  int row_chunks = (int)(c.head_dim * elem_bytes(c.kv_dtype) / 16);
+  int row_chunks = (int)(elems_to_bytes(c.head_dim, c.kv_dtype) / 16);
   int64_t threads = (int64_t)n * c.num_kv_heads * row_chunks;
   dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   return launch(cache_write_kernel, grid, block, st, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache,
@@ -139,7 +139,7 @@ int launch_cache_write(const pkv_cache_t& c, const void* k, const void* v, const
 int launch_gather(const pkv_cache_t& c, const int32_t* tables, int max_blocks,
                   const int32_t* lens, const int32_t* cu, int num_seqs, void* ko, void* vo,
                   hipStream_t st) {
-  int row_chunks = (int)(c.head_dim * elem_bytes(c.kv_dtype) / 16);
+  int row_chunks = (int)(elems_to_bytes(c.head_dim, c.kv_dtype) / 16);
   dim3 grid((unsigned)((int64_t)max_blocks * num_seqs)), block(256);
   return launch(gather_kernel, grid, block, st, (const uint8_t*)c.k_cache,
                 (const uint8_t*)c.v_cache, tables, max_blocks, lens, cu, c.num_kv_heads,

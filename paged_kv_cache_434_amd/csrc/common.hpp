@@ -14,30 +14,38 @@ namespace pkv {
 constexpr int kBlock = PKV_BLOCK_SIZE;  // tokens per KV block
 constexpr int kWave = 64;               // CDNA wavefront width
 
-inline size_t elem_bytes(int dtype) {
+// Bits of one stored element (FP4 codes are packed two per byte), 0 for an
+// unknown type.
+inline int elem_bits(int dtype) {
   switch (dtype) {
-    case PKV_F32: return 4;
-    case PKV_BF16: return 2;
-    case PKV_I8: return 1;
-    case PKV_FP8_E4M3: return 1;
-    case PKV_U8_ZP: return 1;
+    case PKV_F32: return 32;
+    case PKV_BF16: return 16;
+    case PKV_I8: return 8;
+    case PKV_FP8_E4M3: return 8;
+    case PKV_U8_ZP: return 8;
+    case PKV_FP4_E2M1: return 4;
     default: return 0;
   }
 }
+
+// Bytes of n stored elements (n even for FP4).
+inline int64_t elems_to_bytes(int64_t n, int dtype) { return n * elem_bits(dtype) / 8; }
 
 // Elements of one block of one pool (every KV head's tile).
 inline int64_t block_elems(const pkv_cache_t& c) {
   return (int64_t)c.num_kv_heads * c.block_size * c.head_dim;
 }
 
-inline bool is_q8(int dtype) {
-  return dtype == PKV_I8 || dtype == PKV_FP8_E4M3 || dtype == PKV_U8_ZP;
+// Pools of codes with binary32 scales (and, for PKV_U8_ZP, zero points).
+inline bool is_quantized(int dtype) {
+  return dtype == PKV_I8 || dtype == PKV_FP8_E4M3 || dtype == PKV_U8_ZP ||
+         dtype == PKV_FP4_E2M1;
 }
 
 // Bytes from one block to the next in k_cache / v_cache.
 inline size_t block_stride_bytes(const pkv_cache_t& c) {
   const int64_t e = c.block_stride != 0 ? c.block_stride : block_elems(c);
-  return (size_t)e * elem_bytes(c.kv_dtype);
+  return (size_t)elems_to_bytes(e, c.kv_dtype);
 }
 
 // Launch through hipLaunchKernel so the launch status comes back directly

@@ -79,7 +79,7 @@ constexpr int kMaxDevices = 64;
 constexpr float kNoMax = -3.0e38f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 
-enum { KV_BF16 = 0, KV_I8 = 1, KV_FP8 = 2, KV_U8Z = 3 };
+enum { KV_BF16 = 0, KV_I8 = 1, KV_FP8 = 2, KV_U8Z = 3, KV_FP4 = 4 };
 enum { OUT_F32 = 0, OUT_BF16 = 1 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -136,6 +136,21 @@ __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
   hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// 32 E2M1 codes (16 bytes, two per byte, low nibble first) -> 32 bf16
+// values (four 16-byte chunks), exact: the gfx950 conversion instruction
+// turns the two codes of one byte into two bf16 values.
+__device__ __forceinline__ void widen32_fp4(u32x4 c, u32x4 (&o)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = c[k];
+    o[k] = u32x4{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3))};
+  }
+}
+
 template <int D, int OUT>
 __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v) {
   if constexpr (OUT == OUT_F32) {
@@ -149,7 +164,8 @@ __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: q bf16; KV bf16, int8 or E4M3; D = 64 or 128; G <= 16.
+// MFMA path: q bf16; KV bf16, int8, E4M3, asymmetric uint8 or E2M1; D = 64 or
+// 128; G <= 16.
 
 // Launch-wide arguments of the MFMA kernels.
 struct MfmaArgs {
@@ -242,9 +258,12 @@ template <int D, int KV, int OUT, int NST, bool MQ>
 __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, int L, int b0,
                                              int b1, int slot, bool whole, int tok0,
                                              uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_p) {
-  constexpr int kEsz = (KV == KV_BF16) ? 2 : 1;
-  constexpr int kTile = kBlock * D * kEsz;  // bytes of one (block, head) tile in HBM
-  constexpr int kLoads = kTile / 1024;      // 16-byte loads per lane per tile
+  constexpr int kBits = KV == KV_BF16 ? 16 : KV == KV_FP4 ? 4 : 8;
+  constexpr int kTile = kBlock * D * kBits / 8;  // bytes of one (block, head) tile in HBM
+  // 16-byte loads per lane per tile (a 512-byte tile leaves lanes 32-63 idle)
+  constexpr int kLoads = kTile >= 1024 ? kTile / 1024 : 1;
+  // one binary32 scale per (block, head) for K and for V
+  constexpr bool kBlockScale = KV == KV_I8 || KV == KV_FP8 || KV == KV_FP4;
   constexpr int kNKK = D / 32;              // QK^T instructions per block
   constexpr int kNT = D / 16;               // PV instructions per block
   const int lane = threadIdx.x;
@@ -337,7 +356,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     const int c1 = min(c0 + 64, b1);
     const int tab = (c0 + lane < c1) ? trow[c0 + lane] : -1;
     float ks_l = 1.f, vs_l = 1.f;
-    if constexpr (KV == KV_I8 || KV == KV_FP8) {
+    if constexpr (kBlockScale) {
       if (tab >= 0 && tab < num_blocks) {
         ks_l = a.ksc[(size_t)tab * hkv + g];
         vs_l = a.vsc[(size_t)tab * hkv + g];
@@ -390,6 +409,21 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) =
               (row < valid && row >= vlo) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+        } else if constexpr (KV == KV_FP4) {
+          const int e0 = (i * 1024 + lane * 16) * 2;   // first of this lane's 32 codes
+          const int row = e0 / D, col = e0 % D;
+          if (row < kBlock) {
+            u32x4 kw[4], vw[4];
+            widen32_fp4(kr[i], kw);
+            widen32_fp4(vr[i], vw);
+            const bool vok = row < valid && row >= vlo;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + c)) = kw[c];
+              *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + c)) =
+                  vok ? vw[c] : u32x4{0u, 0u, 0u, 0u};
+            }
+          }
         } else {
           const int byte = (i * 64 + lane) * 16;    // first code of this chunk
           const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
@@ -416,7 +450,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         }
       }
       float kscale = 1.f, vscale = 1.f;
-      if constexpr (KV == KV_I8 || KV == KV_FP8) {
+      if constexpr (kBlockScale) {
         if (b < c1) {
           kscale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ks_l), b - c0));
           vscale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs_l), b - c0));
@@ -1082,6 +1116,12 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
                      decode_mfma_balanced_kernel<D, KV_I8, OUT, true>)
                 : go(decode_mfma_kernel<D, KV_I8, OUT, false>,
                      decode_mfma_balanced_kernel<D, KV_I8, OUT, false>);
+        break;
+      case PKV_FP4_E2M1:
+        rc = mq ? go(decode_mfma_kernel<D, KV_FP4, OUT, true>,
+                     decode_mfma_balanced_kernel<D, KV_FP4, OUT, true>)
+                : go(decode_mfma_kernel<D, KV_FP4, OUT, false>,
+                     decode_mfma_balanced_kernel<D, KV_FP4, OUT, false>);
         break;
       case PKV_U8_ZP:
         rc = mq ? go(decode_mfma_kernel<D, KV_U8Z, OUT, true>,

@@ -10,7 +10,9 @@
 // binary32 division and round-to-nearest-even for every element.  FP8 codes
 // follow the OCP E4M3 definition (bias 7, subnormal quantum 2^-9, largest
 // finite 448, no infinities), computed from the exponent and a rounded
-// 3-bit mantissa.
+// 3-bit mantissa; FP4 codes the OCP E2M1 definition (bias 1, subnormal
+// quantum 1/2, largest 6), packed two per byte, element 2i in the low nibble
+// (the [CSDN] article's section 三 lists FP4 beside INT8 and FP8 for KV).
 #include "common.hpp"
 
 namespace pkv {
@@ -39,7 +41,31 @@ __device__ __forceinline__ uint8_t e4m3_encode(float y) {
   return (uint8_t)((sign << 7) | mag);
 }
 
-template <typename SrcT, int D, bool FP8>
+// Nearest E2M1 code of y (ties to the even mantissa bit), magnitudes >= 6
+// clamp to 6; the sign bit is the sign of y.  y must not be NaN.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  const uint32_t sign = __float_as_uint(y) >> 31;
+  const float ay = fabsf(y);
+  uint32_t mag;
+  if (ay >= 6.0f) {
+    mag = 7;
+  } else if (ay < 1.0f) {                  // 0, 0.5 and (rounding up) 1.0
+    mag = (uint32_t)rintf(ay * 2.0f);
+  } else {
+    int e = (int)((__float_as_uint(ay) >> 23) & 0xFF) - 127;   // 0..2
+    uint32_t mi = (uint32_t)rintf(ldexpf(ay, 1 - e));          // 2..4
+    if (mi == 4) {
+      mi = 2;
+      e += 1;
+    }
+    mag = ((uint32_t)(e + 1) << 1) | (mi - 2);
+  }
+  return (sign << 3) | mag;
+}
+
+enum { Q_I8 = 0, Q_FP8 = 1, Q_FP4 = 2 };
+
+template <typename SrcT, int D, int MODE>
 __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ ksrc,
                                                       const SrcT* __restrict__ vsrc,
                                                       uint8_t* __restrict__ kdst,
@@ -60,7 +86,8 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
   if (b < 0 || b >= num_blocks) return;
   const bool is_v = blockIdx.y != 0;
   const SrcT* src = (is_v ? vsrc : ksrc) + (size_t)b * src_stride + (size_t)g * kElems;
-  uint8_t* dst = (is_v ? vdst : kdst) + (size_t)b * dst_stride + (size_t)g * kElems;
+  uint8_t* dst = (is_v ? vdst : kdst) + (size_t)b * dst_stride +
+                 (size_t)g * kElems / (MODE == Q_FP4 ? 2 : 1);
 
   // lane owns values [ld*64*kVec + lane*kVec, +kVec) for each load ld
   float x[kPerLane];
@@ -83,7 +110,7 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) a = fmaxf(a, fabsf(x[i]));
   a = wave_max(a);
-  const float sc = FP8 ? a / 448.0f : a / 127.0f;
+  const float sc = MODE == Q_FP8 ? a / 448.0f : MODE == Q_FP4 ? a / 6.0f : a / 127.0f;
   if (lane == 0) (is_v ? vscale : kscale)[(size_t)b * hkv + g] = sc;
 
   uint8_t c[kPerLane];
@@ -91,8 +118,10 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
   for (int i = 0; i < kPerLane; ++i) {
     if (a == 0.0f) {
       c[i] = 0;
-    } else if constexpr (FP8) {
+    } else if constexpr (MODE == Q_FP8) {
       c[i] = e4m3_encode(x[i] / sc);
+    } else if constexpr (MODE == Q_FP4) {
+      c[i] = (uint8_t)e2m1_encode(x[i] / sc);
     } else {
       float r = rintf(x[i] / sc);
       r = fminf(fmaxf(r, -127.0f), 127.0f);
@@ -100,8 +129,20 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
     }
   }
   // codes go back in the same element order: kVec bytes per load per lane
+  // (kVec / 2 for FP4, two codes per byte)
 #pragma unroll
   for (int ld = 0; ld < kLoads; ++ld) {
+    if constexpr (MODE == Q_FP4) {
+      uint8_t* p = dst + ((size_t)ld * kWave * kVec + lane * kVec) / 2;
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) w |= (uint32_t)c[ld * kVec + e] << (4 * e);
+      if constexpr (kVec == 8)
+        *reinterpret_cast<uint32_t*>(p) = w;
+      else
+        *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
+      continue;
+    }
     uint8_t* p = dst + (size_t)ld * kWave * kVec + lane * kVec;
     if constexpr (kVec == 4) {
       uint32_t w = 0;
@@ -120,11 +161,11 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
   }
 }
 
-template <typename SrcT, int D, bool FP8>
+template <typename SrcT, int D, int MODE>
 int launch_q(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n,
              hipStream_t st) {
   dim3 grid((unsigned)(n * src.num_kv_heads), 2), block(kWave);
-  return launch(quantize_kernel<SrcT, D, FP8>, grid, block, st, (const SrcT*)src.k_cache,
+  return launch(quantize_kernel<SrcT, D, MODE>, grid, block, st, (const SrcT*)src.k_cache,
                 (const SrcT*)src.v_cache, (uint8_t*)dst.k_cache, (uint8_t*)dst.v_cache,
                 dst.k_scale, dst.v_scale, ids, src.num_kv_heads, src.num_blocks,
                 (int64_t)(block_stride_bytes(src) / sizeof(SrcT)), (int64_t)block_stride_bytes(dst));
@@ -308,9 +349,12 @@ int launch_cwq(const pkv_cache_t& c, const void* k, const void* v, const int32_t
 template <typename SrcT, int D>
 int launch_qd(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n,
               hipStream_t st) {
-  if (dst.kv_dtype == PKV_U8_ZP) return launch_qrows<SrcT, D>(src, dst, ids, n, st);
-  return dst.kv_dtype == PKV_FP8_E4M3 ? launch_q<SrcT, D, true>(src, dst, ids, n, st)
-                                      : launch_q<SrcT, D, false>(src, dst, ids, n, st);
+  switch (dst.kv_dtype) {
+    case PKV_U8_ZP: return launch_qrows<SrcT, D>(src, dst, ids, n, st);
+    case PKV_FP8_E4M3: return launch_q<SrcT, D, Q_FP8>(src, dst, ids, n, st);
+    case PKV_FP4_E2M1: return launch_q<SrcT, D, Q_FP4>(src, dst, ids, n, st);
+    default: return launch_q<SrcT, D, Q_I8>(src, dst, ids, n, st);
+  }
 }
 
 }  // namespace

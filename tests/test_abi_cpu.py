@@ -233,3 +233,19 @@ def test_window_entry_point_rejects_bad_arguments():
     assert aw(_cache(kv_dtype=0), qd=0) == 6             # fp32 pools: not on this path
     assert aw(_cache(), part=24) == 2
     assert aw(_cache(), part=pkv.SPLIT_BALANCED) == 5    # needs a workspace
+
+
+def test_fp4_pool_validation():
+    lib = pkv.lib()
+    assert _decode(_cache(kv_dtype=5)) == 1                              # scales required
+    fp4 = _cache(kv_dtype=5, k_scale=FAKE, v_scale=FAKE)
+    assert _decode(fp4, q_dtype=0) == 3                                  # bf16 queries only
+    assert _decode(fp4, B=0) == 0
+    assert _decode(_cache(kv_dtype=5, k_scale=FAKE, v_scale=FAKE, block_stride=2 * 2 * 16 * 128 + 1)) == 6
+    assert _decode(_cache(kv_dtype=5, k_scale=FAKE, v_scale=FAKE, block_stride=2 * 16 * 128 + 16)) == 6
+    # a byte-copying append cannot write into it
+    assert lib.pkv_cache_write(ctypes.byref(fp4), FAKE, FAKE, FAKE, 3, None) == 6
+    # pool size: half a byte per element
+    assert pkv.pool_bytes(10, 8, 128, "fp4") == 10 * 8 * 16 * 128 // 2
+    q = lambda a, b: lib.pkv_quantize(ctypes.byref(a), ctypes.byref(b), None, 0, None)
+    assert q(fp4, fp4) == 3
