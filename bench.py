@@ -49,7 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("paged_kv_cache_434_amd/csrc/decode.hip", "paged_kv_cache_434_amd/csrc/common.hpp")
 
 
-def algorithmic_bytes(wl, ntok=1):
+def algorithmic_bytes(wl, ntok=1, window=0):
     """Bytes the method must move for one step: K/V of every context token,
     the used block-table entries, 8-bit scales, q in and out, lengths, and for
     workloads with a new token its K/V row read and written plus its slot."""
@@ -59,6 +59,10 @@ def algorithmic_bytes(wl, ntok=1):
     e_q = {"f32": 4, "bf16": 2}[wl.q_dtype]
     L = wl.lens.astype(np.int64)
     nblk = (L + 15) // 16
+    if window > 0:
+        # only the positions some query's window covers: the last W + k - 1
+        L = np.minimum(L, window + ntok - 1)
+        nblk = (L + 15) // 16
     kv = int(int(L.sum()) * wl.Hkv * wl.D * 2 * e_kv)
     tables = int(nblk.sum()) * 4
     if wl.quant == "u8z":       # a binary32 scale and a uint8 zero point per K and V row
@@ -69,7 +73,7 @@ def algorithmic_bytes(wl, ntok=1):
     lens = wl.B * 4
     attention = kv + tables + scales + q_out + lens
     write = 0
-    if wl.write and ntok == 1:
+    if wl.write and ntok == 1 and window == 0:
         # new K/V rows read (in the pool's type, or q's for a quantizing
         # append) and written into the pool, with their row parameters
         e_new = e_q if wl.quant == "u8z" else e_kv
@@ -104,7 +108,7 @@ class Replica:
     """One independent copy of the workload's device inputs plus a prepared
     step call."""
 
-    def __init__(self, wl, part, layout, ntok=1):
+    def __init__(self, wl, part, layout, ntok=1, window=0):
         import numpy as np
         import torch
         import paged_kv_cache_434_amd as pkv
@@ -137,7 +141,7 @@ class Replica:
             cache = qcache
         out_dtype = torch.float32 if wl.q_dtype == "f32" else torch.bfloat16
         ws = pkv.alloc_workspace(wl.B, wl.Hq, wl.D, wl.max_blocks, part)
-        if ntok > 1:
+        if ntok > 1 or window > 0:
             # several query tokens per sequence (their K/V already in the pool)
             rng = np.random.default_rng(1)
             q = torch.from_numpy(W.to_bf16_bits(rng.standard_normal(
@@ -148,7 +152,8 @@ class Replica:
             self.out = torch.empty((wl.B, ntok, wl.Hq, wl.D), dtype=out_dtype, device="cuda")
             self.call = lambda: pkv.attention_multi(cache, q, tables, lens, scale,
                                                     partition_tokens=part, workspace=ws,
-                                                    out=self.out)
+                                                    out=self.out,
+                                                    window=window if window > 0 else None)
         elif wl.write:
             self.call, self.out = pkv.prepare_decode_step(
                 cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"], float(wl.scale),
@@ -309,6 +314,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per sequence (>1: multi-token attention, e.g. verifying "
                          "drafted tokens; their K/V are taken as already written)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (>0: attention over each query's most recent "
+                         "window only; no append)")
     ap.add_argument("--op", choices=("step", "quantize", "copy_blocks"), default="step",
                     help="what to time: the decode step (default) or another operation")
     args = ap.parse_args()
@@ -345,7 +353,7 @@ def main():
     e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1, "fp4": 0.5}[wl.quant or wl.kv_dtype]
     pool_bytes = int(wl.num_blocks * wl.Hkv * 16 * wl.D * 2 * e_kv)
     n_rep = args.replicas or max(2, min(8, math.ceil(1.3e9 / pool_bytes) + 1))
-    reps = [Replica(wl, part, args.layout, args.tokens) for _ in range(n_rep)]
+    reps = [Replica(wl, part, args.layout, args.tokens, args.window) for _ in range(n_rep)]
     print(f"# workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
           f"sum(L)={int(wl.lens.sum())} pool={wl.num_blocks} quant={wl.quant} "
           f"partition={part} layout={args.layout} replicas={len(reps)}",
@@ -375,11 +383,12 @@ def main():
     torch.cuda.synchronize()
     kern_s = statistics.mean(a.elapsed_time(b) for a, b in evs) / 1e3
 
-    ab = algorithmic_bytes(wl, args.tokens)
+    ab = algorithmic_bytes(wl, args.tokens, args.window)
     value = ab["step"] / step_s / 1e9
     achieved = ab["step"] / kern_s / 1e9
     key = (f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/{part}"
-           + (f"/tokens{args.tokens}" if args.tokens > 1 else ""))
+           + (f"/tokens{args.tokens}" if args.tokens > 1 else "")
+           + (f"/window{args.window}" if args.window > 0 else ""))
     traffic = recorded_traffic(key)
     e_q = {"f32": "f32", "bf16": "bf16"}[wl.q_dtype]
     line = {
@@ -402,7 +411,11 @@ def main():
                    "split": "balanced" if part == pkv.SPLIT_BALANCED else "fixed",
                    "layout": args.layout, "replicas": len(reps),
                    "query_tokens_per_seq": args.tokens,
-                   "step": (f"paged attention of {args.tokens} query tokens per sequence + "
+                   "window": args.window,
+                   "step": (f"sliding-window paged attention ({args.window} tokens) of "
+                            f"{args.tokens} query token(s) per sequence + partition combine")
+                           if args.window > 0 else
+                           (f"paged attention of {args.tokens} query tokens per sequence + "
                             "partition combine") if args.tokens > 1 else
                            ("decode step: quantizing append of position L-1 (own launch) + "
                             "paged attention + partition combine") if wl.write and wl.quant else
@@ -419,7 +432,7 @@ def main():
                      "kernel": "the step's kernels (decode attention, then the combine)",
                      "bytes_per_launch": ab["step"]},
     }
-    if not args.no_cpu_baseline and args.tokens == 1:
+    if not args.no_cpu_baseline and args.tokens == 1 and args.window == 0:
         med, runs, threads = cpu_baseline(wl)
         line["cpu_baseline"] = {
             "value": round(ab["step"] / med / 1e9, 3), "unit": "GB/s", "cores": threads,
