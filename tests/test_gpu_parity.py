@@ -1040,3 +1040,26 @@ def test_fp4_gather_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(ko.cpu().numpy(), ko_ref)
     assert np.array_equal(vo.cpu().numpy(), vo_ref)
+
+
+@pytest.mark.parametrize("part", [0, 64, -1])
+def test_decode_step_u8z_equals_append_then_attention(part):
+    """The append fused into the attention launch stores the same bytes as
+    pkv_cache_write_quant and gives the same output as attention after it."""
+    wl = W.make(2, B=9, lens=[1, 15, 16, 17, 32, 33, 300, 0, 511], hi=600, pool=300)
+    d = W.to_device(wl, layout="blocks")
+    qa = _qcache("u8z", wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
+    qb = _qcache("u8z", wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
+    pkv.quantize(_dev_cache(d, wl), qa)
+    pkv.quantize(_dev_cache(d, wl), qb)
+    fused = pkv.decode_step(qa, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"],
+                            float(wl.scale), partition_tokens=part, out_dtype=torch.float32)
+    slots = pkv.slot_mapping(d["tables"], d["lens"])
+    pkv.cache_write_quant(qb, d["k_new"], d["v_new"], slots)
+    sep = pkv.attention_decode(qb, d["q"], d["tables"], d["lens"], float(wl.scale),
+                               partition_tokens=part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for x, y in ((qa.k_cache, qb.k_cache), (qa.v_cache, qb.v_cache), (qa.k_scale, qb.k_scale),
+                 (qa.v_scale, qb.v_scale), (qa.k_zero, qb.k_zero), (qa.v_zero, qb.v_zero)):
+        assert torch.equal(x, y)
+    assert torch.equal(fused, sep)
