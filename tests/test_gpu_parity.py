@@ -238,6 +238,9 @@ SMALL = [
     (2, dict(B=4, lo=1, hi=300, pool=200, Hq=16, Hkv=1), -1),        # G = 16
     (2, dict(B=4, lo=1, hi=300, pool=200, Hq=6, Hkv=2), -1),         # G = 3
     (2, dict(B=6, lo=1, hi=500, pool=400, D=64), -1),                # bf16, D = 64
+    (2, dict(B=600, lo=1, hi=200, pool=5000), -1),                   # lengths beyond the 256 kept in registers
+    (2, dict(B=40, lo=1, hi=300, pool=800, Hq=32, Hkv=32), -1),     # 32 KV heads
+    (2, dict(B=40, lo=1, hi=300, pool=800, Hq=32, Hkv=32), 64),
 ]
 
 
