@@ -201,6 +201,36 @@ def cpu_baseline(wl, budget_s=10.0):
     return statistics.median(times), len(times), oracle.max_threads()
 
 
+def achievable_context():
+    """What plain torch device ops reach on this GPU in the same process, as
+    context for the roofline fraction (the peak stays the published 8 TB/s):
+    a 1 GiB device copy (bytes read + written per second) and a sum over
+    1 GiB of bfloat16 (bytes read per second); best of five each."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        t = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) / 1e3)
+        return min(t)
+
+    copy_s = best(lambda: dst.copy_(src))
+    sum_s = best(lambda: src.sum(dtype=torch.float32))
+    del src, dst
+    return {"device_copy_GBps": round(2 * n / copy_s / 1e9, 1),
+            "device_sum_read_GBps": round(n / sum_s / 1e9, 1),
+            "note": "torch ops on 1 GiB in this process; context only"}
+
+
 def copy_calibration():
     """A plain device-to-device copy of 1 GiB, five times: under rocprofv3
     --pmc FETCH_SIZE / WRITE_SIZE it gives the counters' reading for a known
@@ -440,6 +470,8 @@ def main():
             "sample": (f"the whole workload ({wl.B} sequences, {int(wl.lens.sum())} context "
                        f"tokens) per run, median of {runs} runs of {med:.3f} s; "
                        f"{wl.B / med:.1f} seq-steps/s")}
+    if args.tokens == 1 and args.window == 0:
+        line["achievable"] = achievable_context()
     print(json.dumps(line), flush=True)
 
 
