@@ -31,9 +31,11 @@
 //      and the running maximum only moves (rescaling the accumulator) when the
 //      block maximum exceeds it by more than 8, so p <= 2^8;
 //   5. O^T += V^T P on the matrix cores: v_mfma_f32_16x16x16_bf16 with A = V^T
-//      read transposed from LDS and B = P, which the QK^T result already holds
-//      in the B-operand layout (4 consecutive tokens per lane, head = lane % 16);
-//      for 8-bit KV, P is multiplied by the block's V scale first.
+//      and B = P, which the QK^T result already holds in the B-operand layout
+//      (4 consecutive tokens per lane, head = lane % 16); V^T comes from the
+//      row-major LDS tile through gfx950's transposing LDS read (one 8-byte
+//      read per instruction instead of four 2-byte ones); for 8-bit KV, P is
+//      multiplied by the block's V scale first.
 // Asymmetric per-row pools (value = (code - zero) * scale for each row) run
 // the matrix cores on the raw codes: row t's logit is
 // scale_t * (q . code_t - zero_t * sum(q)) and the output is
@@ -524,15 +526,20 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         }
       }
 
-      // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n]
+      // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n], i < 4.
+      // ds_read_b64_tr_b16 works on groups of 16 lanes: each lane reads 4
+      // consecutive bf16 and lane 4a + b of the group receives element b of
+      // the words read by lanes a, a + 4, a + 8, a + 12.  So lane n of group j
+      // reads row 4j + n / 4, columns 16 t + 4 (n % 4) .. + 3 (one 8-byte
+      // piece of a 16-byte LDS chunk).
+      const int vrow = 4 * j + (n >> 2);
 #pragma unroll
       for (int t = 0; t < kNT; ++t) {
-        const int d = 16 * t + n;
-        u16x4 vv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vv[i] = *reinterpret_cast<const uint16_t*>(lds_v + lds_off<D>(4 * j + i, d >> 3) +
-                                                     (d & 7) * 2);
+        const int col = 16 * t + 4 * (n & 3);
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(lds_v + lds_off<D>(vrow, col >> 3) +
+                                                       (col & 7) * 2));
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pop,
                                                           acc[t], 0, 0, 0);
       }
