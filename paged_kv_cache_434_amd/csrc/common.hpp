@@ -76,6 +76,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Orders one wavefront's LDS accesses where its lanes exchange data through
+// LDS.  The hardware already completes a wave's LDS operations in issue
+// order; the fences stop the compiler from treating the other lanes' stores
+// as absent, which would let it reuse a value that a lane loaded before them
+// or move a load above them.  No instruction is emitted.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

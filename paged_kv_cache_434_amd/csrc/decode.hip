@@ -402,6 +402,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
       const int vlo = lo_seg - b * kBlock;                          // rows below: outside
 
+      // the previous block's LDS reads come before this block's writes
+      wave_sync();
       // ---- stage into LDS as bf16 (V rows past L zeroed)
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
@@ -465,6 +467,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       if constexpr (KV == KV_U8Z) {
         const uint32_t pw = pr[0] | pr[1] | pr[2] | pr[3];
         if (lane < 40) *reinterpret_cast<uint32_t*>(lds_p + 4 * lane) = pw;
+      }
+      // every lane's LDS writes come before any lane reads them back
+      wave_sync();
+      if constexpr (KV == KV_U8Z) {
         ks4 = *reinterpret_cast<const f32x4*>(lds_p + 16 * j);
         vs4 = *reinterpret_cast<const f32x4*>(lds_p + 64 + 16 * j);
         kzw = *reinterpret_cast<const uint32_t*>(lds_p + 128 + 4 * j);
