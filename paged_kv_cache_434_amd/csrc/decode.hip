@@ -219,6 +219,11 @@ __device__ __forceinline__ int seq_blocks(int L, int ntok, int window) {
   return L > 0 ? (L + kBlock - 1) / kBlock - first_block(L, ntok, window) : 0;
 }
 
+// 2^x for the softmax weights: the hardware instruction alone.  A weight
+// below 2^-126 of the running maximum comes out as zero rather than as a
+// denormal, which no output can tell apart.
+__device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -261,7 +266,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
                                              int b1, int slot, bool whole, int tok0,
                                              uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_p) {
   constexpr int kBits = KV == KV_BF16 ? 16 : KV == KV_FP4 ? 4 : 8;
-  constexpr int kTile = kBlock * D * kBits / 8;  // bytes of one (block, head) tile in HBM
+  constexpr int kRowBytes = D * kBits / 8;       // bytes of one token's row in HBM
+  constexpr int kTile = kBlock * kRowBytes;      // bytes of one (block, head) tile in HBM
   // 16-byte loads per lane per tile (a 512-byte tile leaves lanes 32-63 idle)
   constexpr int kLoads = kTile >= 1024 ? kTile / 1024 : 1;
   // one binary32 scale per (block, head) for K and for V
@@ -310,8 +316,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     for (int kk = 0; kk < kNKK; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qop[kk][e]);
-    qsum += __shfl_xor(qsum, 16, kWave);
-    qsum += __shfl_xor(qsum, 32, kWave);
+    qsum = rows_sum(qsum);
   }
   const float qoff = 128.f * qsum;
 
@@ -371,11 +376,15 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     // scales in lanes 16-31, its K zero points (4 per dword) in lanes 32-35
     // and its V zero points in lanes 36-39; every other lane's offset lies
     // outside the descriptor's range and reads zero.
-    auto load_tile = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], u32x4& pr, int ph) {
+    auto load_tile = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], u32x4& pr, int ph, int bl) {
       const bool in = ph >= 0 && ph < num_blocks;
       const size_t off = in ? (size_t)ph * blk_stride : 0;
       const rsrc_t rk = make_rsrc(kbase + off, in ? kTile : 0);
-      const rsrc_t rv = make_rsrc(vbase + off, in ? kTile : 0);
+      // V rows at or past the end are outside the descriptor and load as
+      // zeros: bf16 and E4M3 bytes there may encode NaN or infinity, which a
+      // zero weight would not cancel
+      const int vrows = __builtin_amdgcn_readfirstlane(min(max(L - bl * kBlock, 0), kBlock));
+      const rsrc_t rv = make_rsrc(vbase + off, in ? vrows * kRowBytes : 0);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         kr[i] = buffer_load16(rk, i * 1024 + lane * 16);
@@ -402,17 +411,23 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
       const int vlo = lo_seg - b * kBlock;                          // rows below: outside
 
+      // V rows past the end arrive as zeros (see load_tile); rows below a
+      // window's first position are zeroed here, for the codes that can
+      // encode NaN or infinity (bf16, E4M3).  INT8, uint8 and E2M1 codes are
+      // finite, so their rows with zero weight add exactly nothing.
+      constexpr bool kZeroLow = KV == KV_BF16 || KV == KV_FP8;
+      const bool vlow = kZeroLow && vlo > 0;
+
       // the previous block's LDS reads come before this block's writes
       wave_sync();
-      // ---- stage into LDS as bf16 (V rows past L zeroed)
+      // ---- stage into LDS as bf16
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         if constexpr (KV == KV_BF16) {
           const int chunk = i * 64 + lane;          // 16-byte chunk of the tile
           const int row = chunk / (D / 8), ch = chunk % (D / 8);
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
-          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) =
-              (row < valid && row >= vlo) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) = vr[i];
         } else if constexpr (KV == KV_FP4) {
           const int e0 = (i * 1024 + lane * 16) * 2;   // first of this lane's 32 codes
           const int row = e0 / D, col = e0 % D;
@@ -420,12 +435,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             u32x4 kw[4], vw[4];
             widen32_fp4(kr[i], kw);
             widen32_fp4(vr[i], vw);
-            const bool vok = row < valid && row >= vlo;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + c)) = kw[c];
-              *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + c)) =
-                  vok ? vw[c] : u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + c)) = vw[c];
             }
           }
         } else {
@@ -434,11 +447,26 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           u32x4 klo, khi, vlo4, vhi;
           widen16<KV>(kr[i], klo, khi);
           widen16<KV>(vr[i], vlo4, vhi);
-          if (row >= valid || row < vlo) vlo4 = vhi = u32x4{0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo4;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
+        }
+      }
+      if constexpr (kZeroLow) {
+        if (vlow) {   // overwrite the V rows below the window with zeros
+#pragma unroll
+          for (int i = 0; i < kLoads; ++i) {
+            const int chunk = i * 64 + lane;
+            const int rb = KV == KV_BF16 ? D * 2 : D;   // tile bytes per row
+            const int row = chunk * 16 / rb;
+            const int ch = KV == KV_BF16 ? chunk % (D / 8) : (chunk * 16 % D) / 8;
+            if (row < vlo) {
+              *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) = u32x4{0u, 0u, 0u, 0u};
+              if constexpr (KV != KV_BF16)
+                *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch + 1)) = u32x4{0u, 0u, 0u, 0u};
+            }
+          }
         }
       }
       if constexpr (KV == KV_BF16) {
@@ -479,7 +507,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
       // ---- refill this buffer with block b+NST (zero-length if absent)
       ph = phys_of(b + NST);
-      load_tile(kr, vr, pr, ph);
+      load_tile(kr, vr, pr, ph, b + NST);
 
       // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
       f32x4 sv = {0.f, 0.f, 0.f, 0.f};
@@ -489,28 +517,55 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
       }
 
+      // ---- V^T operands of O^T += V^T P, read now so that their LDS latency
+      // passes during the softmax.  Lane (j, n) supplies V[4j + i][16 t + n],
+      // i < 4.  ds_read_b64_tr_b16 works on groups of 16 lanes: each lane
+      // reads 4 consecutive bf16 and lane 4a + b of the group receives element
+      // b of the words read by lanes a, a + 4, a + 8, a + 12.  So lane n of
+      // group j reads row 4j + n / 4, columns 16 t + 4 (n % 4) .. + 3 (one
+      // 8-byte piece of a 16-byte LDS chunk).
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      s16x4 vt[kNT];
+      {
+        const int vrow = 4 * j + (n >> 2);
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+          const int col = 16 * t + 4 * (n & 3);
+          vt[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(lds_v + lds_off<D>(vrow, col >> 3) +
+                                                         (col & 7) * 2));
+        }
+      }
+
       // ---- online softmax (base 2)
       const float cb = a.scale_log2 * kscale;
       float x[4];
       float mx = -INFINITY;
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
       const int vmin = lo_col - b * kBlock;   // this column's first row in its window
+      // one query token per sequence: every row of a block is in range for
+      // every column unless the block is the last (or, with a window, the
+      // first) of the sequence, so the per-row selects are skipped
+      const bool full = !MQ && vcol >= kBlock && vmin <= 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float y;
         if constexpr (KV == KV_U8Z)
-          y = (sv[i] - (float)((kzw >> (8 * i)) & 0xFFu) * qsum) * (cb * ks4[i]);
+          x[i] = (sv[i] - (float)((kzw >> (8 * i)) & 0xFFu) * qsum) * (cb * ks4[i]);
         else
-          y = ((KV == KV_I8) ? sv[i] - qoff : sv[i]) * cb;
-        x[i] = (4 * j + i < vcol && 4 * j + i >= vmin) ? y : -INFINITY;
-        mx = fmaxf(mx, x[i]);
+          x[i] = ((KV == KV_I8) ? sv[i] - qoff : sv[i]) * cb;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(4 * j + i < vcol && 4 * j + i >= vmin)) x[i] = -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[i]);
+      mx = rows_max(mx);
       const bool bump = mx > m + kRescaleSlack;
       if (__any(bump)) {
         const float mnew = bump ? mx : m;
-        const float alpha = exp2f(m - mnew);
+        const float alpha = exp2_weight(m - mnew);
         lsum *= alpha;
         if constexpr (KV == KV_I8 || KV == KV_U8Z) psum *= alpha;
 #pragma unroll
@@ -520,11 +575,12 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       bf16x4 pop;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pe = exp2f(x[i] - m);
+        const float pe = exp2_weight(x[i] - m);
         lsum += pe;
         if constexpr (KV == KV_U8Z) {
           // rows past the end have p = 0 but may hold any scale
-          pop[i] = static_cast<__bf16>(4 * j + i < vcol && 4 * j + i >= vmin ? pe * vs4[i] : 0.f);
+          pop[i] = static_cast<__bf16>(
+              full || (4 * j + i < vcol && 4 * j + i >= vmin) ? pe * vs4[i] : 0.f);
           psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
         } else {
           pop[i] = static_cast<__bf16>(pe * vscale);
@@ -532,23 +588,11 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         }
       }
 
-      // ---- O^T += V^T P: lane (j, n) supplies V[4j + i][16 t + n], i < 4.
-      // ds_read_b64_tr_b16 works on groups of 16 lanes: each lane reads 4
-      // consecutive bf16 and lane 4a + b of the group receives element b of
-      // the words read by lanes a, a + 4, a + 8, a + 12.  So lane n of group j
-      // reads row 4j + n / 4, columns 16 t + 4 (n % 4) .. + 3 (one 8-byte
-      // piece of a 16-byte LDS chunk).
-      const int vrow = 4 * j + (n >> 2);
+      // ---- O^T += V^T P
 #pragma unroll
-      for (int t = 0; t < kNT; ++t) {
-        const int col = 16 * t + 4 * (n & 3);
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        const s16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(lds_v + lds_off<D>(vrow, col >> 3) +
-                                                       (col & 7) * 2));
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pop,
+      for (int t = 0; t < kNT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt[t]), pop,
                                                           acc[t], 0, 0, 0);
-      }
     };
 
     // NST register buffers in a ring: buffer i holds block b with b % NST == i
@@ -557,7 +601,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       ph[i] = phys_of(c0 + i);
-      load_tile(kr[i], vr[i], pr[i], ph[i]);
+      load_tile(kr[i], vr[i], pr[i], ph[i], c0 + i);
     }
     for (int b = c0; b < c1; b += NST) {
 #pragma unroll
@@ -567,13 +611,11 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   }
 
   // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
-  float lt = lsum + __shfl_xor(lsum, 16, kWave);
-  lt += __shfl_xor(lt, 32, kWave);
+  const float lt = rows_sum(lsum);
   if constexpr (KV == KV_I8 || KV == KV_U8Z) {
     // the V codes entered as c + 128: take 128 * sum(P) off every output row;
     // asymmetric rows: take sum_t P_t zero_t off
-    float pt = psum + __shfl_xor(psum, 16, kWave);
-    pt += __shfl_xor(pt, 32, kWave);
+    const float pt = rows_sum(psum);
     const float voff = KV == KV_I8 ? 128.f * pt : pt;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[t] -= voff;
