@@ -94,13 +94,15 @@ __device__ __forceinline__ void wave_sync() {
 // v_permlane32_swap the upper 32 lanes of its first for the lower 32 of its
 // second; given a value twice, each lane ends up with its own value in one
 // result and its partner's in the other.
+// (The max is IEEE maximum, which passes a NaN on; it needs no operand
+// quieting, unlike fmaxf.)
 __device__ __forceinline__ float rows_max(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t w = __float_as_uint(v);
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float rows_sum(float v) {

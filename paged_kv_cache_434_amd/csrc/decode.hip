@@ -560,7 +560,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           if (!(4 * j + i < vcol && 4 * j + i >= vmin)) x[i] = -INFINITY;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[i]);
+      for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
       mx = rows_max(mx);
       const bool bump = mx > m + kRescaleSlack;
       if (__any(bump)) {
@@ -572,20 +572,24 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
         m = mnew;
       }
-      bf16x4 pop;
+      f32x4 pw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pe = exp2_weight(x[i] - m);
         lsum += pe;
-        if constexpr (KV == KV_U8Z) {
-          // rows past the end have p = 0 but may hold any scale
-          pop[i] = static_cast<__bf16>(
-              full || (4 * j + i < vcol && 4 * j + i >= vmin) ? pe * vs4[i] : 0.f);
+        if constexpr (KV == KV_U8Z)   // rows past the end have p = 0 but may hold any scale
+          pw[i] = full || (4 * j + i < vcol && 4 * j + i >= vmin) ? pe * vs4[i] : 0.f;
+        else
+          pw[i] = pe * vscale;
+      }
+      const bf16x4 pop = __builtin_convertvector(pw, bf16x4);   // two paired conversions
+      if constexpr (KV == KV_U8Z) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
           psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
-        } else {
-          pop[i] = static_cast<__bf16>(pe * vscale);
-          if constexpr (KV == KV_I8) psum += static_cast<float>(pop[i]);
-        }
+      } else if constexpr (KV == KV_I8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) psum += static_cast<float>(pop[i]);
       }
 
       // ---- O^T += V^T P
