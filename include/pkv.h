@@ -312,7 +312,9 @@ int pkv_attention_window(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
  *   PKV_FP4_E2M1: scale = a / 6, code = nearest E2M1 (ties to the even
  *                 mantissa bit), magnitudes beyond 6 saturate to +-6 ([CSDN]
  *                 section 三: FP4 KV)
- * a == 0 gives scale 0 and zero codes.  With dst PKV_U8_ZP ([MGMT] section 四,
+ * a == 0 gives scale 0 and zero codes; src values must be finite (the codes
+ * of a tile holding NaN or infinity are unspecified).  With dst PKV_U8_ZP
+ * ([MGMT] section 四,
  * KVQuantizationCache with per-channel parameters) every (block, head, row) of
  * head_dim values is quantized on its own, as pkv_cache_write_quant states,
  * and its scale and zero point go to that row of the parameter arrays.

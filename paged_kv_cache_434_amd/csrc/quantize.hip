@@ -9,58 +9,41 @@
 // coalesced 16-byte loads into registers, a wave-wide max of |x|, then
 // binary32 division and round-to-nearest-even for every element.  FP8 codes
 // follow the OCP E4M3 definition (bias 7, subnormal quantum 2^-9, largest
-// finite 448, no infinities), computed from the exponent and a rounded
-// 3-bit mantissa; FP4 codes the OCP E2M1 definition (bias 1, subnormal
-// quantum 1/2, largest 6), packed two per byte, element 2i in the low nibble
-// (the [CSDN] article's section 三 lists FP4 beside INT8 and FP8 for KV).
+// finite 448, no infinities); FP4 codes the OCP E2M1 definition (bias 1,
+// subnormal quantum 1/2, largest 6), packed two per byte, element 2i in the
+// low nibble (the [CSDN] article's section 三 lists FP4 beside INT8 and FP8
+// for KV).  Both come from gfx950's conversion instructions, two codes per
+// instruction, after a clamp to the largest finite value.  For every finite
+// binary32 input they give the nearest code with ties to the even mantissa
+// (an exhaustive run against an encoder written from the definitions found
+// no difference).
 #include "common.hpp"
 
 namespace pkv {
 
 namespace {
 
-// Nearest E4M3 code of y (ties to even mantissa), magnitudes >= 448 clamp to
-// 448; the sign bit is the sign of y.  y must not be NaN.
-__device__ __forceinline__ uint8_t e4m3_encode(float y) {
-  uint32_t sign = __float_as_uint(y) >> 31;
-  float ay = fabsf(y);
-  uint32_t mag;
-  if (ay >= 448.0f) {
-    mag = 0x7E;
-  } else if (ay < 0.015625f) {                 // below 2^-6: multiples of 2^-9
-    mag = (uint32_t)rintf(ay * 512.0f);        // 0..8; 8 is the smallest normal
-  } else {
-    int e = (int)((__float_as_uint(ay) >> 23) & 0xFF) - 127;  // floor(log2 ay), -6..8
-    uint32_t mi = (uint32_t)rintf(ldexpf(ay, 3 - e));         // 8..16
-    if (mi == 16) {
-      mi = 8;
-      e += 1;
-    }
-    mag = ((uint32_t)(e + 7) << 3) | (mi - 8);
-  }
-  return (uint8_t)((sign << 7) | mag);
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// E4M3 codes of four values (element e in byte e): gfx950's OCP conversion
+// rounds to nearest, ties to the even mantissa; clamping to +-448 first gives
+// the saturation.
+__device__ __forceinline__ uint32_t e4m3_word(float y0, float y1, float y2, float y3) {
+  auto c = [](float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); };
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c(y0), c(y1), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c(y2), c(y3), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
-// Nearest E2M1 code of y (ties to the even mantissa bit), magnitudes >= 6
-// clamp to 6; the sign bit is the sign of y.  y must not be NaN.
-__device__ __forceinline__ uint32_t e2m1_encode(float y) {
-  const uint32_t sign = __float_as_uint(y) >> 31;
-  const float ay = fabsf(y);
-  uint32_t mag;
-  if (ay >= 6.0f) {
-    mag = 7;
-  } else if (ay < 1.0f) {                  // 0, 0.5 and (rounding up) 1.0
-    mag = (uint32_t)rintf(ay * 2.0f);
-  } else {
-    int e = (int)((__float_as_uint(ay) >> 23) & 0xFF) - 127;   // 0..2
-    uint32_t mi = (uint32_t)rintf(ldexpf(ay, 1 - e));          // 2..4
-    if (mi == 4) {
-      mi = 2;
-      e += 1;
-    }
-    mag = ((uint32_t)(e + 1) << 1) | (mi - 2);
-  }
-  return (sign << 3) | mag;
+// E2M1 codes of two values in one byte (the first in the low nibble), put
+// into byte `sel` of `w`: the OCP conversion rounds to nearest, ties to the
+// even mantissa bit; clamping to +-6 gives the saturation.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __builtin_amdgcn_fmed3f(y0, -6.0f, 6.0f),
+                                                 __builtin_amdgcn_fmed3f(y1, -6.0f, 6.0f), 1.0f,
+                                                 SEL);
 }
 
 enum { Q_I8 = 0, Q_FP8 = 1, Q_FP4 = 2 };
@@ -113,50 +96,62 @@ __global__ __launch_bounds__(64) void quantize_kernel(const SrcT* __restrict__ k
   const float sc = MODE == Q_FP8 ? a / 448.0f : MODE == Q_FP4 ? a / 6.0f : a / 127.0f;
   if (lane == 0) (is_v ? vscale : kscale)[(size_t)b * hkv + g] = sc;
 
-  uint8_t c[kPerLane];
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
-    if (a == 0.0f) {
-      c[i] = 0;
-    } else if constexpr (MODE == Q_FP8) {
-      c[i] = e4m3_encode(x[i] / sc);
-    } else if constexpr (MODE == Q_FP4) {
-      c[i] = (uint8_t)e2m1_encode(x[i] / sc);
-    } else {
-      float r = rintf(x[i] / sc);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      c[i] = (uint8_t)(int8_t)(int)r;
-    }
-  }
   // codes go back in the same element order: kVec bytes per load per lane
-  // (kVec / 2 for FP4, two codes per byte)
+  // (kVec / 2 for FP4, two codes per byte); a == 0 gives zero codes
+  const bool zero = a == 0.0f;
 #pragma unroll
   for (int ld = 0; ld < kLoads; ++ld) {
+    const float* y = x + ld * kVec;
+    auto q = [&](int e) { return y[e] / sc; };
     if constexpr (MODE == Q_FP4) {
       uint8_t* p = dst + ((size_t)ld * kWave * kVec + lane * kVec) / 2;
       uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) w |= (uint32_t)c[ld * kVec + e] << (4 * e);
+      if (!zero) {
+        w = e2m1_pair<0>(w, q(0), q(1));
+        w = e2m1_pair<1>(w, q(2), q(3));
+        if constexpr (kVec == 8) {
+          w = e2m1_pair<2>(w, q(4), q(5));
+          w = e2m1_pair<3>(w, q(6), q(7));
+        }
+      }
       if constexpr (kVec == 8)
         *reinterpret_cast<uint32_t*>(p) = w;
       else
         *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
-      continue;
-    }
-    uint8_t* p = dst + (size_t)ld * kWave * kVec + lane * kVec;
-    if constexpr (kVec == 4) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w |= (uint32_t)c[ld * 4 + e] << (8 * e);
-      *reinterpret_cast<uint32_t*>(p) = w;
-    } else {
-      uint2 w = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w.x |= (uint32_t)c[ld * 8 + e] << (8 * e);
-        w.y |= (uint32_t)c[ld * 8 + 4 + e] << (8 * e);
+    } else if constexpr (MODE == Q_FP8) {
+      uint8_t* p = dst + (size_t)ld * kWave * kVec + lane * kVec;
+      uint32_t w0 = 0, w1 = 0;
+      if (!zero) {
+        w0 = e4m3_word(q(0), q(1), q(2), q(3));
+        if constexpr (kVec == 8) w1 = e4m3_word(q(4), q(5), q(6), q(7));
       }
-      *reinterpret_cast<uint2*>(p) = w;
+      if constexpr (kVec == 4)
+        *reinterpret_cast<uint32_t*>(p) = w0;
+      else
+        *reinterpret_cast<uint2*>(p) = uint2{w0, w1};
+    } else {
+      uint8_t c[kVec];
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        float r = rintf(q(e));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        c[e] = zero ? 0 : (uint8_t)(int8_t)(int)r;
+      }
+      uint8_t* p = dst + (size_t)ld * kWave * kVec + lane * kVec;
+      if constexpr (kVec == 4) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= (uint32_t)c[e] << (8 * e);
+        *reinterpret_cast<uint32_t*>(p) = w;
+      } else {
+        uint2 w = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w.x |= (uint32_t)c[e] << (8 * e);
+          w.y |= (uint32_t)c[4 + e] << (8 * e);
+        }
+        *reinterpret_cast<uint2*>(p) = w;
+      }
     }
   }
 }

@@ -191,6 +191,40 @@ def test_quantize_bit_exact(src, dst, D):
     assert np.array_equal(qc.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
 
 
+@pytest.mark.parametrize("dst", ["fp8", "fp4"])
+def test_quantize_ties_signs_and_subnormals_bit_exact(dst):
+    """Tiles whose largest magnitude is the format's largest finite value, so
+    the scale is exactly 1 and each value is encoded as it stands: every code
+    value, every midpoint between neighbouring codes (ties go to the even
+    mantissa), signed zeros and binary32 values far below the smallest
+    subnormal code, in both signs."""
+    decode = oracle.e4m3_to_f64 if dst == "fp8" else oracle.e2m1_to_f64
+    top = 448.0 if dst == "fp8" else 6.0
+    n_codes = 0x7F if dst == "fp8" else 8
+    pos = np.unique(decode(np.arange(n_codes, dtype=np.uint8)))       # 0 .. top
+    mids = (pos[:-1] + pos[1:]) / 2
+    tiny = np.array([2.0 ** -12, 2.0 ** -20, 1e-30, 1e-40])
+    vals = np.concatenate([pos, mids, tiny])
+    vals = np.concatenate([vals, -vals, [-0.0, top]]).astype(np.float32)
+    NB, Hkv, D = 3, 2, 128
+    x = np.zeros((NB, Hkv, 16, D), np.float32)
+    flat = x.reshape(NB * Hkv, -1)
+    for t in range(NB * Hkv):
+        row = np.roll(vals, 17 * t)
+        flat[t, :row.size] = row
+        flat[t, -1] = top                   # the tile maximum: scale exactly 1
+    kc, ks = oracle.quantize(x, "f32", dst)
+    vc, vs = oracle.quantize(-x, "f32", dst)
+    assert np.all(ks == 1.0)
+    scache = pkv.PagedCache(torch.from_numpy(x).cuda(), torch.from_numpy(-x).cuda(), "f32")
+    qc = _qcache(dst, NB, Hkv, 16, D, fill=7)
+    pkv.quantize(scache, qc)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc.k_cache.cpu().numpy(), kc)
+    assert np.array_equal(qc.v_cache.cpu().numpy(), vc)
+    assert np.array_equal(qc.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+
+
 def test_quantize_block_subset_leaves_others_untouched():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((10, 2, 16, 128)).astype(np.float32)
