@@ -983,6 +983,64 @@ def test_attention_window(cfg, over, k, window, part, layout, quant):
     _cmp(_out_np(out), ref, TOL[quant or "bf16"], "f32", f"window {window} k={k}")
 
 
+@pytest.mark.parametrize("quant", ["i8", "fp8", "u8z", "fp4"])
+@pytest.mark.parametrize("window,part", [(0, -1), (50, -1), (50, 64)])
+def test_quantized_rows_outside_range_do_not_matter(quant, window, part):
+    """Every row of a used block that no query may see (past the sequence's
+    end, or below its window) is overwritten with garbage: NaN codes for E4M3,
+    random bytes for INT8 and E2M1, random codes with NaN scales for per-row
+    uint8.  The output is bit-identical to that over the untouched pool: those
+    rows have weight exactly zero and their values never reach a product."""
+    wl = W.make(2, B=8, lens=[1, 15, 16, 17, 40, 333, 64, 600], hi=600, pool=300)
+    _say(f"garbage outside range: {quant} window={window} part={part}")
+    rng = np.random.default_rng(900 + window + part)
+    d = W.to_device(wl)
+    qc = _qcache(quant, wl.num_blocks, wl.Hkv, 16, wl.D)
+    pkv.quantize(_dev_cache(d, wl), qc)
+    q = _dev_bf16(_mq_q(rng, wl.B, 1, wl.Hq, wl.D))
+
+    def run(cache):
+        o = pkv.attention_window(cache, q, d["tables"], d["lens"], float(wl.scale), window,
+                                 partition_tokens=part, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return o.clone()
+
+    base = run(qc)
+    used = set()                                   # (block, row) some query may see
+    touched = set()                                # blocks some sequence walks
+    for s_, L in enumerate(wl.lens):
+        L = int(L)
+        first = max(0, L - window) if window > 0 else 0
+        for t in range(first, L):
+            used.add((int(wl.tables[s_, t // 16]), t % 16))
+        for b in range(first // 16, (L + 15) // 16):
+            touched.add(int(wl.tables[s_, b]))
+    rows = [(b, r) for b in sorted(touched) for r in range(16) if (b, r) not in used]
+    assert len(rows) >= 40
+    kc, vc = qc.k_cache.cpu().numpy(), qc.v_cache.cpu().numpy()
+    for b, r in rows:
+        for pool in (kc, vc):
+            if quant == "fp8":
+                pool[b, :, r] = 0x7F                   # E4M3 NaN
+            else:
+                pool[b, :, r] = rng.integers(0, 256, size=pool[b, :, r].shape).astype(pool.dtype)
+    scales = {}
+    if quant == "u8z":
+        for name in ("k_scale", "v_scale", "k_zero", "v_zero"):
+            arr = getattr(qc, name).cpu().numpy()
+            for b, r in rows:
+                arr[b, :, r] = np.nan if arr.dtype == np.float32 else rng.integers(0, 256)
+            scales[name] = torch.from_numpy(arr).cuda()
+    else:
+        scales = dict(k_scale=qc.k_scale, v_scale=qc.v_scale)
+    garbage = pkv.PagedCache(torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), quant,
+                             scales["k_scale"], scales["v_scale"], scales.get("k_zero"),
+                             scales.get("v_zero"))
+    out = run(garbage)
+    assert torch.isfinite(out).all()
+    assert torch.equal(out, base)
+
+
 @pytest.mark.parametrize("part", [0, -1])
 def test_window_zero_is_the_multi_token_call(part):
     wl = W.make(2, B=6, lo=1, hi=600, pool=300)
