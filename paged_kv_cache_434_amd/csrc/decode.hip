@@ -19,7 +19,8 @@
 //      the partition's block-table entries are loaded once, 64 per vector
 //      load, and broadcast from a lane, so no table read sits in front of a
 //      tile load;
-//   2. 8-bit codes are widened to bf16 (exact), then both tiles are written to
+//   2. 8-bit codes are widened to bf16 (exact; INT8 and uint8 K codes to fp16
+//      1024 + u, also exact, for an fp16 QK^T), then both tiles are written to
 //      LDS with the 16-byte chunks of row t XOR-swizzled by t, so the
 //      row-per-lane and column-per-lane reads below are free of bank conflicts;
 //   3. S = K q^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = K rows
@@ -69,6 +70,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 // native clang vector (HIP's u32x4 is a wrapper struct that can keep arrays of
 // it out of registers)
@@ -120,9 +122,11 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // INT8: the sign bit is flipped, so code c becomes u = c + 128 in [1, 255];
 // an unsigned byte converts to binary32 in one instruction and u < 256 has at
 // most 8 significant bits, so its binary32 upper half is u in bf16 exactly.
-// The kernel subtracts the offset afterwards: 128 * sum(q) from each logit
-// and 128 * sum(p) from each output column.  Asymmetric uint8 codes are
-// widened the same way without the flip.
+// The kernel subtracts the offset afterwards: 128 * sum(p) from each output
+// column.  Asymmetric uint8 codes are widened the same way without the flip.
+// (This widening serves V; INT8 and uint8 K codes take the cheaper fp16 route
+// of widen16_k16, because QK^T may run in fp16 where P V may not: P carries
+// the block's V scale, which fp16's range cannot hold in general.)
 template <int KV>
 __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
   const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
@@ -144,6 +148,25 @@ __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
       o[2 * i] = __builtin_bit_cast(uint32_t, a);
       o[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
     }
+  }
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+  hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// 16 INT8 or uint8 K codes -> 16 fp16 values 1024 + u, exact (u = c + 128
+// for INT8, the raw code for uint8): fp16 1024 has the bits 0x6400 and a unit
+// in the last place of 1, so a byte permute that puts code u under the byte
+// 0x64 makes 1024 + u, two codes per permute.  The logit takes the
+// (1024 + offset) * sum(q) back off.
+template <int KV>
+__device__ __forceinline__ void widen16_k16(u32x4 c, u32x4& lo, u32x4& hi) {
+  constexpr uint32_t kExp = 0x64646464u;
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = KV == KV_I8 ? c[i] ^ 0x80808080u : c[i];
+    o[2 * i] = __builtin_amdgcn_perm(kExp, u, 0x04010400u);       // u0, u1
+    o[2 * i + 1] = __builtin_amdgcn_perm(kExp, u, 0x04030402u);   // u2, u3
   }
   lo = u32x4{o[0], o[1], o[2], o[3]};
   hi = u32x4{o[4], o[5], o[6], o[7]};
@@ -318,18 +341,36 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       qop[kk] = has_head ? v : bf16x8{};
     }
   }
-  // INT8 codes enter the MFMA as c + 128 (see widen16): each logit then holds
-  // 128 * sum_d q[h][d] too, which is taken off again before the softmax;
-  // asymmetric rows take off zero_t * sum_d q[h][d]
-  float qsum = 0.f;
-  if constexpr (KV == KV_I8 || KV == KV_U8Z) {
+  float qsum = 0.f;   // sum of the scaled fp16 queries of this lane's head
+  // INT8 and uint8 K codes enter QK^T as fp16 1024 + u (see widen16_k16), so
+  // the queries do too: scaled per head by 2^qe, which puts the head's largest
+  // |q| in [2^14, 2^15) and keeps every value finite in fp16 (bf16 values
+  // within 2^29 of that largest one convert exactly).  The logit then takes
+  // (1024 + offset) * sum(q) off and multiplies by 2^-qe.
+  constexpr bool kK16 = KV == KV_I8 || KV == KV_U8Z;
+  f16x8 qoh[kNKK];
+  float qinv = 1.f;
+  if constexpr (kK16) {
+    float mq = 0.f;
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qop[kk][e]);
+      for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(static_cast<float>(qop[kk][e])));
+    mq = rows_max(mq);
+    const int qe = mq > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mq) : 0;
+    qinv = __builtin_ldexpf(1.f, -qe);
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qoh[kk][e] = static_cast<_Float16>(__builtin_ldexpf(static_cast<float>(qop[kk][e]), qe));
+        qsum += static_cast<float>(qoh[kk][e]);
+      }
     qsum = rows_sum(qsum);
   }
-  const float qoff = 128.f * qsum;
+  // INT8: each logit holds (1024 + 128) * sum(q) on top; uint8 subtracts
+  // (1024 + zero point) * sum(q) per row
+  const float qoff = (KV == KV_I8 ? 1152.f : 1024.f) * qsum;
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = a.blk_stride;
@@ -456,7 +497,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           const int byte = (i * 64 + lane) * 16;    // first code of this chunk
           const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
           u32x4 klo, khi, vlo4, vhi;
-          widen16<KV>(kr[i], klo, khi);
+          if constexpr (kK16)
+            widen16_k16<KV>(kr[i], klo, khi);
+          else
+            widen16<KV>(kr[i], klo, khi);
           widen16<KV>(vr[i], vlo4, vhi);
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
@@ -524,8 +568,13 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       f32x4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < kNKK; ++kk) {
-        bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
-        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
+        if constexpr (kK16) {
+          const f16x8 kop = *reinterpret_cast<const f16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
+          sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qoh[kk], sv, 0, 0, 0);
+        } else {
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
+          sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
+        }
       }
 
       // ---- V^T operands of O^T += V^T P, read now so that their LDS latency
@@ -549,7 +598,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
 
       // ---- online softmax (base 2)
-      const float cb = a.scale_log2 * kscale;
+      const float cb = a.scale_log2 * kscale * qinv;
       float x[4];
       float mx = -INFINITY;
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
@@ -561,7 +610,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (KV == KV_U8Z)
-          x[i] = (sv[i] - (float)((kzw >> (8 * i)) & 0xFFu) * qsum) * (cb * ks4[i]);
+          x[i] = (sv[i] - __builtin_fmaf((float)((kzw >> (8 * i)) & 0xFFu), qsum, qoff)) *
+                 (cb * ks4[i]);
         else
           x[i] = ((KV == KV_I8) ? sv[i] - qoff : sv[i]) * cb;
       }
