@@ -71,6 +71,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 // native clang vector (HIP's u32x4 is a wrapper struct that can keep arrays of
 // it out of registers)
@@ -400,6 +401,14 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
   float m = kNoMax;   // running reference maximum (log2 units)
   float lsum = 0.f;   // this lane's share of the softmax denominator
+  // INT8: V codes enter P V as fp16 1024 + u too, and P, which carries the
+  // block's V scale, as fp16.  To keep P finite it carries the V scale times
+  // vfac = 2^-E, chosen per 64-block chunk so that the chunk's largest V scale
+  // times vfac lies in [2^6, 2^7): P <= 2^8 * 2^7 < 65504.  The accumulator is
+  // rescaled (exactly, by a power of two) when vfac changes between chunks and
+  // divided by vfac at the end.
+  constexpr bool kV16 = KV == KV_I8;
+  float vfac = 0.f;
   float psum = 0.f;   // INT8: this lane's share of sum(P), rescaled like the accumulator;
                       // asymmetric rows: of sum_t P_t zero_t, likewise
 
@@ -419,6 +428,20 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       if (tab >= 0 && tab < num_blocks) {
         ks_l = a.ksc[(size_t)tab * hkv + g];
         vs_l = a.vsc[(size_t)tab * hkv + g];
+      }
+    }
+    if constexpr (kV16) {
+      const float vmax = wave_max(tab >= 0 && tab < num_blocks ? fabsf(vs_l) : 0.f);
+      const float f = vmax > 0.f ? __builtin_ldexpf(1.f, 7 - __builtin_amdgcn_frexp_expf(vmax))
+                                 : 1.f;
+      if (f != vfac) {
+        if (vfac > 0.f) {
+          const float r = f / vfac;
+#pragma unroll
+          for (int t = 0; t < kNT; ++t) acc[t] *= r;
+          psum *= r;
+        }
+        vfac = f;
       }
     }
     auto phys_of = [&](int b) -> int {
@@ -501,7 +524,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             widen16_k16<KV>(kr[i], klo, khi);
           else
             widen16<KV>(kr[i], klo, khi);
-          widen16<KV>(vr[i], vlo4, vhi);
+          if constexpr (kV16)
+            widen16_k16<KV>(vr[i], vlo4, vhi);
+          else
+            widen16<KV>(vr[i], vlo4, vhi);
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo4;
@@ -641,23 +667,34 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         if constexpr (KV == KV_U8Z)   // rows past the end have p = 0 but may hold any scale
           pw[i] = full || (4 * j + i < vcol && 4 * j + i >= vmin) ? pe * vs4[i] : 0.f;
         else
-          pw[i] = pe * vscale;
+          pw[i] = pe * (kV16 ? vscale * vfac : vscale);
       }
-      const bf16x4 pop = __builtin_convertvector(pw, bf16x4);   // two paired conversions
-      if constexpr (KV == KV_U8Z) {
+      if constexpr (kV16) {
+        // two paired conversions (toward zero: under 2^-10 relative, finer
+        // than bf16 to nearest); sum(P) is taken over the converted values
+        const f16x4 poh = __builtin_bit_cast(
+            f16x4, __builtin_shufflevector(__builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]),
+                                           __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]), 0, 1, 2, 3));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
-      } else if constexpr (KV == KV_I8) {
+        for (int i = 0; i < 4; ++i) psum += static_cast<float>(poh[i]);
+        // ---- O^T += V^T P
 #pragma unroll
-        for (int i = 0; i < 4; ++i) psum += static_cast<float>(pop[i]);
+        for (int t = 0; t < kNT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt[t]), poh,
+                                                        acc[t], 0, 0, 0);
+      } else {
+        const bf16x4 pop = __builtin_convertvector(pw, bf16x4);   // two paired conversions
+        if constexpr (KV == KV_U8Z) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
+        }
+        // ---- O^T += V^T P
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt[t]),
+                                                            pop, acc[t], 0, 0, 0);
       }
-
-      // ---- O^T += V^T P
-#pragma unroll
-      for (int t = 0; t < kNT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt[t]), pop,
-                                                          acc[t], 0, 0, 0);
     };
 
     // NST register buffers in a ring: buffer i holds block b with b % NST == i
@@ -678,16 +715,16 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
   const float lt = rows_sum(lsum);
   if constexpr (KV == KV_I8 || KV == KV_U8Z) {
-    // the V codes entered as c + 128: take 128 * sum(P) off every output row;
-    // asymmetric rows: take sum_t P_t zero_t off
+    // INT8 V codes entered as fp16 1024 + (c + 128): take 1152 * sum(P) off
+    // every output row; asymmetric rows: take sum_t P_t zero_t off
     const float pt = rows_sum(psum);
-    const float voff = KV == KV_I8 ? 128.f * pt : pt;
+    const float voff = KV == KV_I8 ? 1152.f * pt : pt;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[t] -= voff;
   }
   // a column that saw no key (a query token before the start, or a piece
   // past its causal limit) has lt == 0: zero output, zero weight
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv = lt > 0.f ? (kV16 ? 1.0f / (lt * vfac) : 1.0f / lt) : 0.f;
   if (!has_head) return;
   if (whole) {
 #pragma unroll
@@ -750,8 +787,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 #ifndef PKV_BAL_STAGES_Q8
 #define PKV_BAL_STAGES_Q8 2
 #endif
+// INT8 (one query token) asks for three wavefronts per SIMD: with its fp16
+// P V it needs 170 registers and would otherwise drop to two (measured on the
+// shared-prefix INT8 workload: 91.8 us at two, 87.4 us at three, where two
+// registers are spilled: one 8-byte scratch store and reload per two blocks).
 template <int D, int KV, int OUT, bool MQ>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_BAL_WAVES))) void
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    KV == KV_I8 && !MQ ? 3 : PKV_BAL_WAVES))) void
 decode_mfma_balanced_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
