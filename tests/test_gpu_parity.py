@@ -306,6 +306,44 @@ def test_attention_quant_small(quant, part):
     _cmp(_out_np(out), ref, TOL[quant], "f32", f"quant {quant}")
 
 
+@pytest.mark.parametrize("quant", ["i8", "u8z", "fp8"])
+@pytest.mark.parametrize("part", [0, -1])
+def test_quant_attention_extreme_scales(quant, part):
+    # K/V values spanning 1e-5 .. 1e4 between blocks, where the largest scale
+    # among a sequence's first 64 blocks is below the rest's for even
+    # sequences and above it for odd ones (a whole-context segment walks its
+    # blocks in chunks of 64), and queries scaled by 1e4, 1 or 1e-4 per
+    # sequence.  The bound is the unit-scale tolerance times the largest value
+    # scale the sequence attends over.
+    wl = W.make(2, B=6, lo=1100, hi=2400, pool=None)
+    rng = np.random.default_rng(11)
+    exps = np.array([-5, -3, 0, 2, 4])
+    fac = np.ones(wl.k_pool.shape[0])
+    big = np.ones(wl.B)
+    for s in range(wl.B):
+        nb = (int(wl.lens[s]) + 15) // 16
+        low, high = exps[:3], exps[2:]
+        first, rest = (low, high) if s % 2 == 0 else (high, low)
+        for b in range(nb):
+            fac[wl.tables[s, b]] = 10.0 ** rng.choice(first if b < 64 else rest)
+        big[s] = max(1.0, fac[wl.tables[s, :nb]].max())
+    f4 = fac[:, None, None, None].astype(np.float32)
+    kp = W.to_bf16_bits(W.bf16_bits_to_f32(wl.k_pool) * f4)
+    vp = W.to_bf16_bits(W.bf16_bits_to_f32(wl.v_pool) * f4)
+    qf = np.array([1e4, 1.0, 1e-4], dtype=np.float32)[np.arange(wl.B) % 3][:, None, None]
+    q = W.to_bf16_bits(W.bf16_bits_to_f32(wl.q) * qf)
+    wl = dataclasses.replace(wl, k_pool=kp, v_pool=vp, q=q)
+    _say(f"attention extreme scales: {quant} part={part}")
+    d = W.to_device(wl)
+    out, _ = _step(wl, d, part, torch.float32, quant)
+    ref, _ = _oracle_step(wl, quant)
+    got = _out_np(out)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref).max(axis=(1, 2))
+    _say(f"  largest error / value scale: {np.max(err / big):.2e}")
+    assert np.all(err <= TOL[quant] * big), (err / big, big)
+
+
 def test_fp8_code_decode_exact():
     # one-token sequences: the output is the single V row, decode(code) * scale,
     # exactly (weight 1, scale 1): covers all 254 finite E4M3 codes
