@@ -36,7 +36,10 @@
 //      (4 consecutive tokens per lane, head = lane % 16); V^T comes from the
 //      row-major LDS tile through gfx950's transposing LDS read (one 8-byte
 //      read per instruction instead of four 2-byte ones); for 8-bit KV, P is
-//      multiplied by the block's V scale first.
+//      multiplied by the block's V scale first.  INT8 K and V codes (and
+//      uint8 K codes) take an fp16 route instead: a byte permute makes two fp16
+//      values 1024 + u at a time, and the products run on the fp16 MFMAs (see
+//      widen16_k16).
 // Asymmetric per-row pools (value = (code - zero) * scale for each row) run
 // the matrix cores on the raw codes: row t's logit is
 // scale_t * (q . code_t - zero_t * sum(q)) and the output is
