@@ -59,9 +59,9 @@ def test_workspace_sizes():
     assert ws >= rows * parts * (128 + 2) * 4 and ws % 256 == 0
     assert lib.pkv_decode_workspace_bytes(8, 32, 128, 2048, 500) == 0    # not a multiple of 16
     assert lib.pkv_decode_workspace_bytes(8, 32, 128, 2048, -2) == 0     # negative, not balanced
-    # balanced split: ceil(max_blocks / 8) + 1 slots per row, plus one count per sequence
+    # balanced split: ceil(max_blocks / 16) + 1 slots per row, plus one count per sequence
     wb = lib.pkv_decode_workspace_bytes(8, 32, 128, 2048, pkv.SPLIT_BALANCED)
-    slots = 2048 // 8 + 1
+    slots = 2048 // 16 + 1
     assert wb >= rows * slots * (128 + 2) * 4 + 8 * 4 and wb % 256 == 0
     assert lib.pkv_decode_workspace_bytes(3, 4, 64, 1, pkv.SPLIT_BALANCED) > 0
 
