@@ -802,11 +802,17 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_p[KV == KV_U8Z ? 160 : 16];
   const int lane = threadIdx.x;
+  // launch index: KV head fastest, then the pass over the query tokens, then
+  // the range.  The passes of one (range, KV head) are launched side by side
+  // and land on the same XCD, so a later pass finds the tiles the first one
+  // fetched in that XCD's L2.
+  const int passes = (a.ntok + a.tok_per_pass - 1) / a.tok_per_pass;
   const int g = blockIdx.x % a.hkv;
-  const int v = blockIdx.x / a.hkv;
-  const int V = gridDim.x / a.hkv;
+  const int pass = (blockIdx.x / a.hkv) % passes;
+  const int v = blockIdx.x / (a.hkv * passes);
+  const int V = gridDim.x / (a.hkv * passes);
   const int B = a.num_seqs;
-  const int tok0 = blockIdx.y * a.tok_per_pass;
+  const int tok0 = pass * a.tok_per_pass;
 
   // The lengths of the first kLenChunks * 64 sequences are loaded once, all
   // at the same time, and kept in registers for both passes and the walk.
@@ -882,7 +888,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int vf = R0 / per;
     const int K = (R1 - 1) / per - vf + 1;
     const int slot = v - vf;
-    if (g == 0 && blockIdx.y == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
+    if (g == 0 && pass == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
     // 8-bit tiles are half the bytes of bf16 ones: they may keep more blocks in flight
     constexpr int kStages = KV == KV_BF16 ? PKV_BAL_STAGES : PKV_BAL_STAGES_Q8;
     mfma_segment<D, KV, OUT, kStages, MQ>(a, s, g, L, fb + x - R0, fb + e - R0, slot, K == 1,
@@ -1265,7 +1271,7 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         // the wavefronts make half the pieces (4 tokens: 118.6 -> 115.9 us on
         // the 8B shape; 2 and 8 tokens gain 1.6 % and 3 %)
         const int64_t waves = (int64_t)pl.cus * per_cu / (a.ntok > 1 ? 2 : 1);
-        dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv), (unsigned)pl.passes);
+        dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv * pl.passes));
         return launch(balanced_kernel, grid, block, st, m);
       }
       dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts), (unsigned)pl.passes);
