@@ -60,6 +60,7 @@
 // kernel combines them with the log-sum-exp rule; a sequence that fits in one
 // partition is written directly.
 #include <atomic>
+#include <type_traits>
 #include <mutex>
 #include <unordered_map>
 
@@ -108,10 +109,19 @@ constexpr int kCpolNT = 2;
 // K/V tile loads carry the non-temporal hint: a tile is read once per step
 // (unless blocks are shared between sequences), and streaming the tiles lets
 // the caches keep what every wavefront reads again: block tables, lengths,
-// queries.  Measured on the Llama-3-8B-shape step: 117.1 -> 107.2 us.
+// queries.  Measured on the Llama-3-8B-shape step: 117.1 -> 107.2 us.  The
+// exception is a launch whose later passes over the query tokens read the
+// same tiles again (kMqPasses below): there plain loads keep them in L2.
+template <int CPOL>
 __device__ __forceinline__ u32x4 buffer_load16_kv(rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNT));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
+
+// Query-token modes of the MFMA kernels (template parameter MQ): one token
+// per sequence; several tokens that fit one pass (k * G <= 16 columns); and
+// several passes, whose wavefronts for one (range, KV head) run side by side
+// and share the tiles through L2 (balanced split only).
+enum { kMqOne = 0, kMqPass = 1, kMqPasses = 2 };
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of bf16
 // rows of D elements, chunks XOR-swizzled by the row index.
@@ -299,7 +309,7 @@ __device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g, int t
 // its logical blocks [b0, b1).  `whole`: the range is the whole context, so the
 // normalised rows go to `out`; otherwise the partial (max, sum, output) goes
 // to partial slot `slot` of each row.
-template <int D, int KV, int OUT, int NST, bool MQ>
+template <int D, int KV, int OUT, int NST, int MQ>
 __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, int L, int b0,
                                              int b1, int slot, bool whole, int tok0,
                                              uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_p) {
@@ -465,8 +475,9 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const rsrc_t rv = make_rsrc(vbase + off, in ? vrows * kRowBytes : 0);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        kr[i] = buffer_load16_kv(rk, i * 1024 + lane * 16);
-        vr[i] = buffer_load16_kv(rv, i * 1024 + lane * 16);
+        constexpr int kCpol = MQ == kMqPasses ? 0 : kCpolNT;
+        kr[i] = buffer_load16_kv<kCpol>(rk, i * 1024 + lane * 16);
+        vr[i] = buffer_load16_kv<kCpol>(rv, i * 1024 + lane * 16);
       }
       if constexpr (KV == KV_U8Z) {
         const size_t row0 = in ? ((size_t)ph * hkv + g) * kBlock : 0;
@@ -747,7 +758,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
 // Fixed split: one wavefront per (sequence, KV head, partition of
 // part_blocks blocks); the launch index is decoded KV-head-fastest.
-template <int D, int KV, int OUT, bool MQ>
+template <int D, int KV, int OUT, int MQ>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
@@ -794,7 +805,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 // P V it needs 170 registers and would otherwise drop to two (measured on the
 // shared-prefix INT8 workload: 91.8 us at two, 87.4 us at three, where two
 // registers are spilled: one 8-byte scratch store and reload per two blocks).
-template <int D, int KV, int OUT, bool MQ>
+template <int D, int KV, int OUT, int MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     KV == KV_I8 && !MQ ? 3 : PKV_BAL_WAVES))) void
 decode_mfma_balanced_kernel(MfmaArgs a) {
@@ -1277,38 +1288,27 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
       dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts), (unsigned)pl.passes);
       return launch(fixed_kernel, grid, block, st, m, pl.n_parts);
     };
-    const bool mq = a.ntok > 1;
+    // multi-pass launches of the balanced split get the cached-load kernel;
+    // the fixed split launches its passes as separate grid rows, which do not
+    // run side by side, so it keeps the streaming one
+    const int mq = a.ntok <= 1 ? kMqOne : (pl.balanced && pl.passes > 1 ? kMqPasses : kMqPass);
+    auto by_kv = [&](auto kv) {
+      constexpr int KV = decltype(kv)::value;
+      if (mq == kMqOne)
+        return go(decode_mfma_kernel<D, KV, OUT, kMqOne>,
+                  decode_mfma_balanced_kernel<D, KV, OUT, kMqOne>);
+      if (mq == kMqPass)
+        return go(decode_mfma_kernel<D, KV, OUT, kMqPass>,
+                  decode_mfma_balanced_kernel<D, KV, OUT, kMqPass>);
+      return go(decode_mfma_kernel<D, KV, OUT, kMqPass>,
+                decode_mfma_balanced_kernel<D, KV, OUT, kMqPasses>);
+    };
     switch (c.kv_dtype) {
-      case PKV_BF16:
-        rc = mq ? go(decode_mfma_kernel<D, KV_BF16, OUT, true>,
-                     decode_mfma_balanced_kernel<D, KV_BF16, OUT, true>)
-                : go(decode_mfma_kernel<D, KV_BF16, OUT, false>,
-                     decode_mfma_balanced_kernel<D, KV_BF16, OUT, false>);
-        break;
-      case PKV_I8:
-        rc = mq ? go(decode_mfma_kernel<D, KV_I8, OUT, true>,
-                     decode_mfma_balanced_kernel<D, KV_I8, OUT, true>)
-                : go(decode_mfma_kernel<D, KV_I8, OUT, false>,
-                     decode_mfma_balanced_kernel<D, KV_I8, OUT, false>);
-        break;
-      case PKV_FP4_E2M1:
-        rc = mq ? go(decode_mfma_kernel<D, KV_FP4, OUT, true>,
-                     decode_mfma_balanced_kernel<D, KV_FP4, OUT, true>)
-                : go(decode_mfma_kernel<D, KV_FP4, OUT, false>,
-                     decode_mfma_balanced_kernel<D, KV_FP4, OUT, false>);
-        break;
-      case PKV_U8_ZP:
-        rc = mq ? go(decode_mfma_kernel<D, KV_U8Z, OUT, true>,
-                     decode_mfma_balanced_kernel<D, KV_U8Z, OUT, true>)
-                : go(decode_mfma_kernel<D, KV_U8Z, OUT, false>,
-                     decode_mfma_balanced_kernel<D, KV_U8Z, OUT, false>);
-        break;
-      default:
-        rc = mq ? go(decode_mfma_kernel<D, KV_FP8, OUT, true>,
-                     decode_mfma_balanced_kernel<D, KV_FP8, OUT, true>)
-                : go(decode_mfma_kernel<D, KV_FP8, OUT, false>,
-                     decode_mfma_balanced_kernel<D, KV_FP8, OUT, false>);
-        break;
+      case PKV_BF16: rc = by_kv(std::integral_constant<int, KV_BF16>{}); break;
+      case PKV_I8: rc = by_kv(std::integral_constant<int, KV_I8>{}); break;
+      case PKV_FP4_E2M1: rc = by_kv(std::integral_constant<int, KV_FP4>{}); break;
+      case PKV_U8_ZP: rc = by_kv(std::integral_constant<int, KV_U8Z>{}); break;
+      default: rc = by_kv(std::integral_constant<int, KV_FP8>{}); break;
     }
   }
   // no combine when nothing can be split: a fixed split with one partition
