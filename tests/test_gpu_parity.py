@@ -754,6 +754,14 @@ MQ_CASES = [
     (5, dict(B=8, prefix=128, suffix_hi=200), 4, -1, "blocks", "u8z"),
     (5, dict(B=8, prefix=128, suffix_hi=200), 1, 0, "split", "u8z"),
     (5, dict(B=8, prefix=128, suffix_hi=200), 4, -1, "blocks", "fp4"),
+    # balanced split with several passes (their wavefronts run side by side
+    # and load the tiles without the non-temporal hint)
+    (3, dict(B=12, median=200, lo=1, hi=700), 4, -1, "blocks", None),  # G = 8, 2 passes
+    (2, dict(B=4, lo=1, hi=300, pool=200, Hq=8, Hkv=8), 40, -1, "split", None),   # 3 passes
+    (5, dict(B=8, prefix=128, suffix_hi=200), 6, -1, "blocks", "i8"),
+    (5, dict(B=8, prefix=128, suffix_hi=200), 5, -1, "split", "fp8"),
+    (5, dict(B=8, prefix=128, suffix_hi=200), 6, -1, "blocks", "u8z"),
+    (5, dict(B=8, prefix=128, suffix_hi=200), 8, -1, "blocks", "fp4"),
 ]
 
 
@@ -993,6 +1001,7 @@ WINDOW_CASES = [
     (5, dict(B=10, prefix=256, suffix_hi=300), 2, 77, 256, "split", "fp8"),
     (5, dict(B=10, prefix=256, suffix_hi=300), 1, 129, -1, "blocks", "u8z"),
     (5, dict(B=10, prefix=256, suffix_hi=300), 2, 200, 256, "split", "fp4"),
+    (2, dict(B=6, lo=1, hi=600, pool=300), 6, 100, -1, "blocks", None),   # 2 passes
 ]
 
 
