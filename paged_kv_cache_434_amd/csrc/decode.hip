@@ -123,12 +123,23 @@ __device__ __forceinline__ u32x4 buffer_load16_kv(rsrc_t r, int off) {
 // and share the tiles through L2 (balanced split only).
 enum { kMqOne = 0, kMqPass = 1, kMqPasses = 2 };
 
-// Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of bf16
-// rows of D elements, chunks XOR-swizzled by the row index.
-template <int D>
+// Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of
+// 16-bit rows of D elements, chunks XOR-swizzled by the row index, so the
+// column-per-lane QK^T reads (16 rows, one chunk) are free of bank conflicts.
+// LDS serves 128 bytes, eight 16-byte accesses, per cycle.  A bf16 tile is
+// staged by eight lanes writing eight consecutive chunks of a row.  A tile
+// widened from 8-bit codes at D = 128 is staged by each lane writing chunks
+// 2m and then 2m + 1 of its row (E2M1: 4m + c), so eight lanes would cover 256
+// bytes and meet every bank twice.  For those tiles the chunk index is rotated
+// first (c -> c / 2 + 8 (c % 2)), which spreads each write over all eight
+// bank groups; at D = 64 a row is one 128-byte sweep and the plain swizzle
+// already does.
+template <int D, int KV>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   constexpr int kChunks = D / 8;
-  return row * (D * 2) + ((chunk ^ (row & (kChunks - 1))) << 4);
+  constexpr bool kRotate = KV != KV_BF16 && D == 128;
+  const int c = kRotate ? (chunk >> 1) | ((chunk & 1) * (kChunks / 2)) : chunk;
+  return row * (D * 2) + ((c ^ (row & (kChunks - 1))) << 4);
 }
 
 // 16 8-bit codes -> 16 bf16 values (two 16-byte chunks), exact.
@@ -515,8 +526,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         if constexpr (KV == KV_BF16) {
           const int chunk = i * 64 + lane;          // 16-byte chunk of the tile
           const int row = chunk / (D / 8), ch = chunk % (D / 8);
-          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, ch)) = kr[i];
-          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) = vr[i];
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, ch)) = kr[i];
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, ch)) = vr[i];
         } else if constexpr (KV == KV_FP4) {
           const int e0 = (i * 1024 + lane * 16) * 2;   // first of this lane's 32 codes
           const int row = e0 / D, col = e0 % D;
@@ -526,8 +537,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             widen32_fp4(vr[i], vw);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + c)) = kw[c];
-              *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + c)) = vw[c];
+              *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8 + c)) = kw[c];
+              *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8 + c)) = vw[c];
             }
           }
         } else {
@@ -542,10 +553,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             widen16_k16<KV>(vr[i], vlo4, vhi);
           else
             widen16<KV>(vr[i], vlo4, vhi);
-          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8)) = klo;
-          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(row, col / 8 + 1)) = khi;
-          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8)) = vlo4;
-          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, col / 8 + 1)) = vhi;
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8)) = klo;
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8 + 1)) = khi;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8)) = vlo4;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8 + 1)) = vhi;
         }
       }
       if constexpr (kZeroLow) {
@@ -557,17 +568,17 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             const int row = chunk * 16 / rb;
             const int ch = KV == KV_BF16 ? chunk % (D / 8) : (chunk * 16 % D) / 8;
             if (row < vlo) {
-              *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch)) = u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, ch)) = u32x4{0u, 0u, 0u, 0u};
               if constexpr (KV != KV_BF16)
-                *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(row, ch + 1)) = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, ch + 1)) = u32x4{0u, 0u, 0u, 0u};
             }
           }
         }
       }
       if constexpr (KV == KV_BF16) {
         if (b == new_b && lane < kRowChunks) {   // the appended token's row
-          *reinterpret_cast<u32x4*>(lds_k + lds_off<D>(new_r, lane)) = knew;
-          *reinterpret_cast<u32x4*>(lds_v + lds_off<D>(new_r, lane)) = vnew;
+          *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(new_r, lane)) = knew;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(new_r, lane)) = vnew;
           if (cur_ok) {
             const size_t dst = (size_t)cur * blk_stride + (size_t)g * kTile + new_r * (D * 2) +
                                lane * 16;
@@ -609,10 +620,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
       for (int kk = 0; kk < kNKK; ++kk) {
         if constexpr (kK16) {
-          const f16x8 kop = *reinterpret_cast<const f16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
+          const f16x8 kop = *reinterpret_cast<const f16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
           sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qoh[kk], sv, 0, 0, 0);
         } else {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(n, 4 * kk + j));
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
           sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
         }
       }
@@ -632,7 +643,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         for (int t = 0; t < kNT; ++t) {
           const int col = 16 * t + 4 * (n & 3);
           vt[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(lds_v + lds_off<D>(vrow, col >> 3) +
+              (__attribute__((address_space(3))) s16x4*)(lds_v + lds_off<D, KV>(vrow, col >> 3) +
                                                          (col & 7) * 2));
         }
       }
