@@ -1147,8 +1147,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ws
   const float l0 = lane < kstride ? lrow[lane] : 0.f;
   // the first kSpec partial rows (most sequences have no more pieces), read
   // before the count is known through a descriptor bounded to the row's slots
-  constexpr int kSpec = SPEC;
-  constexpr int kSpecLoads = kSpec / kRowsPerLoad;
+  constexpr int kSpecLoads = SPEC > kRowsPerLoad ? SPEC / kRowsPerLoad : 1;
+  constexpr int kSpec = kSpecLoads * kRowsPerLoad;
   const int sub0 = lane / kCols, col0 = lane % kCols;
   const rsrc_t rspec = make_rsrc(ws_o + (size_t)row * kstride * D, kstride * D * 4);
   u32x4 spec[kSpecLoads];
@@ -1242,6 +1242,7 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
   const float sl2 = a.scale * kLog2e;
   dim3 block(kWave);
   int rc;
+  int64_t ranges = 0;   // balanced split: wavefronts per KV head (and pass)
   if (c.kv_dtype == PKV_F32) {
     dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts));
     rc = launch(decode_f32_kernel<D, OUT, 16>, grid, block, st, (const float*)a.q,
@@ -1294,6 +1295,7 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         // the wavefronts make half the pieces (4 tokens: 118.6 -> 115.9 us on
         // the 8B shape; 2 and 8 tokens gain 1.6 % and 3 %)
         const int64_t waves = (int64_t)pl.cus * per_cu / (a.ntok > 1 ? 2 : 1);
+        ranges = (waves + hkv - 1) / hkv;
         dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv * pl.passes));
         return launch(balanced_kernel, grid, block, st, m);
       }
@@ -1326,17 +1328,21 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
   // no combine when nothing can be split: a fixed split with one partition
   if (rc != PKV_OK || pl.kstride <= 1 || (!pl.balanced && pl.n_parts <= 1)) return rc;
   dim3 rgrid((unsigned)((int64_t)a.num_seqs * a.ntok * hq));
-  // several query tokens: k times the rows, and half the wavefronts make
-  // fewer pieces per sequence, so 4 rows are read ahead of the count instead
-  // of 8 (4 tokens on the 8B shape: 116.8 -> 114.0 us; 8 tokens 149.0 ->
-  // 142.9 us)
+  // The combine reads the first partial rows of a row before it knows the
+  // piece count.  With ranges wavefronts per KV head and B sequences, a
+  // sequence has about 1 + ranges / B pieces: read that many rounded up to 2,
+  // 4 or 8 (8B shape: 5 pieces, 8 rows; 70B shape: 2 pieces, 2 rows; several
+  // query tokens on the 8B shape, half the wavefronts: 3 pieces, 4 rows).
   auto combine = [&](auto kernel) {
     return launch(kernel, rgrid, block, st, (const float*)pl.ws_m, (const float*)pl.ws_l,
                   (const float*)pl.ws_o,
                   (const int32_t*)(pl.balanced ? pl.ws_count : nullptr), a.lens, a.max_blocks,
                   a.ntok * hq, pl.part_blocks, pl.kstride, a.ntok, a.window, a.out);
   };
-  return a.ntok > 1 ? combine(reduce_kernel<D, OUT, 4>) : combine(reduce_kernel<D, OUT, 8>);
+  const int64_t pieces = pl.balanced ? 1 + ranges / a.num_seqs : 8;
+  if (pieces <= 2) return combine(reduce_kernel<D, OUT, 2>);
+  if (pieces <= 4) return combine(reduce_kernel<D, OUT, 4>);
+  return combine(reduce_kernel<D, OUT, 8>);
 }
 
 }  // namespace
