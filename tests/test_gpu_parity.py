@@ -344,6 +344,23 @@ def test_quant_attention_extreme_scales(quant, part):
     assert np.all(err <= TOL[quant] * big), (err / big, big)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_balanced_split_many_sequences_few_long(D):
+    # many short sequences (about two pieces each, so the combine reads only a
+    # few partial rows ahead of the count) and a few long ones with many
+    # pieces, which must still be combined in full
+    rng = np.random.default_rng(33)
+    B = 600
+    lens = rng.integers(1, 200, size=B)
+    lens[rng.choice(B, 6, replace=False)] = rng.integers(3000, 4096, size=6)
+    wl = W.make(2, B=B, lens=lens.tolist(), hi=4096, pool=None, D=D)
+    _say(f"balanced split, many sequences: D={D} sum(L)={int(wl.lens.sum())}")
+    d = W.to_device(wl)
+    out, _ = _step(wl, d, -1, torch.float32)
+    ref, _ = _oracle_step(wl)
+    _cmp(_out_np(out), ref, TOL["bf16"], "f32", f"many sequences D={D}")
+
+
 def test_fp8_code_decode_exact():
     # one-token sequences: the output is the single V row, decode(code) * scale,
     # exactly (weight 1, scale 1): covers all 254 finite E4M3 codes
