@@ -283,12 +283,6 @@ __device__ __forceinline__ int seq_blocks(int L, int ntok, int window) {
 // denormal, which no output can tell apart.
 __device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // Inclusive prefix sum across the wavefront (lane order).
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -859,12 +853,17 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     return r;
   };
 
-  // pass 1: total blocks per KV head; zero rows of empty sequences
-  int total = 0;
+  // pass 1: total blocks per KV head, from the inclusive prefix of each
+  // 64-sequence chunk (the first chunk's is kept for pass 2, which then needs
+  // no second scan when there are at most 64 sequences); zero rows of empty
+  // sequences
+  int total = 0, incl0 = 0;
   for (int base = 0; base < B; base += kWave) {
     const int si = base + lane;
     const int Ll = len_chunk(base);
-    total += wave_sum_i(seq_blocks(Ll, a.ntok, a.window));
+    const int inc = wave_incl_scan(seq_blocks(Ll, a.ntok, a.window));
+    if (base == 0) incl0 = inc;
+    total += readlane_i(inc, kWave - 1);
     if (v == 0) {
       uint64_t empty = __ballot(si < B && Ll == 0);
       while (empty) {
@@ -889,7 +888,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   for (; base < B; base += kWave) {
     Lreg = len_chunk(base);
     const int nb = seq_blocks(Lreg, a.ntok, a.window);
-    incl = wave_incl_scan(nb) + carry;
+    incl = (base == 0 ? incl0 : wave_incl_scan(nb)) + carry;
     const uint64_t hit = __ballot(nb > 0 && incl - nb <= x0 && x0 < incl);
     if (hit) {
       const int hl = __ffsll((unsigned long long)hit) - 1;
