@@ -1290,10 +1290,15 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         // one generation: as many wavefronts as the GPU holds at once
         const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(balanced_kernel));
         if (per_cu <= 0) return (int)PKV_ERR_HIP;
-        // several query tokens write k times the partial rows per piece: half
-        // the wavefronts make half the pieces (4 tokens: 118.6 -> 115.9 us on
-        // the 8B shape; 2 and 8 tokens gain 1.6 % and 3 %)
-        const int64_t waves = (int64_t)pl.cus * per_cu / (a.ntok > 1 ? 2 : 1);
+        // several query tokens write k times the partial rows per piece.  bf16
+        // steps are bound by HBM with wavefronts to spare, so a quarter of a
+        // generation makes a quarter of the pieces (8B shape, 4 tokens: 118.6
+        // us at a full generation, 113.8 at half, 109.6 at a quarter; a sixth
+        // collapses to 135 us).  The 8- and 4-bit kernels are bound by their
+        // arithmetic and need every wavefront (shared prefix, 4 tokens, E4M3:
+        // 100.7 us at a full generation, 116.8 at half).
+        const int64_t div = a.ntok > 1 && c.kv_dtype == PKV_BF16 ? 4 : 1;
+        const int64_t waves = (int64_t)pl.cus * per_cu / div;
         ranges = (waves + hkv - 1) / hkv;
         dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv * pl.passes));
         return launch(balanced_kernel, grid, block, st, m);
