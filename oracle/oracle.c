@@ -35,7 +35,8 @@
  * max finite 448), round-to-nearest-even with saturation.  The asymmetric
  * per-row format (uint8 code, binary32 scale, uint8 zero point per (block,
  * head, row)) follows [MGMT] section 四's KVQuantizationCache in binary32,
- * with a zero-width row stored as scale 0, zero point 0, codes 0.
+ * with each row's range widened to hold 0 (so the zero point never clamps)
+ * and an all-zero row stored as scale 0, zero point 0, codes 0.
  *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
@@ -609,42 +610,47 @@ int orc_quantize(const void* src, int src_dtype, void* dst_k, int dst_dtype, flo
 
 /* ------------------------------------------------------------------------ */
 /* Asymmetric uint8 quantization of one row of n values, [MGMT] section 四,
- * KVQuantizationCache.quantize_key with per_channel on: the minimum and the
- * maximum are taken along the last (head_dim) axis, so every (head, token)
- * row gets its own parameters:
- *   scale      = (max - min) / 255
- *   zero_point = clamp(round(-min / scale), 0, 255)
- *   code       = clamp(round((x - min) / scale), 0, 255)
- * and dequantize_key restores (code - zero_point) * scale.  The page computes
- * in the tensor's own 16-bit type; here every step is a binary32 operation
- * (the stored scale's type), and round is to nearest, ties to even, as
- * torch.round does.  A row whose values are all equal has scale 0, where the
- * page's divisions are undefined: it is stored as scale 0, zero point 0 and
- * codes 0.  Note the page's clamp of the zero point: a row with no negative
- * value gets zero point 0 and restores as about x - min.                    */
+ * KVQuantizationCache with per_channel on: the parameters come from the
+ * minimum and maximum along the last (head_dim) axis, so every (head, token)
+ * row gets its own scale and zero point, and dequantize_key restores
+ * (code - zero_point) * scale.  The page's quantize_key takes the code
+ * relative to the row minimum and clamps the zero point to [0, 255]; for a
+ * row without negative values (or without positive ones) the zero point then
+ * clamps and the restore formula returns about x - min (x - max).  The
+ * reading taken here is the affine quantizer that the restore formula
+ * inverts: the range is widened to hold 0, so the zero point is the code of
+ * 0 and never clamps, and each value takes the code whose restored value is
+ * nearest:
+ *   lo = min(min x, 0), hi = max(max x, 0)
+ *   scale      = (hi - lo) / 255
+ *   zero_point = clamp(round(-lo / scale), 0, 255)
+ *   code       = clamp(round(x / scale) + zero_point, 0, 255)
+ * so (code - zero_point) * scale is within scale / 2 of x.  Every step is a
+ * binary32 operation (the stored scale's type; the page computes in the
+ * tensor's 16-bit type) and round is to nearest, ties to even, as
+ * torch.round does.  An all-zero row has scale 0 (the divisions are then
+ * undefined) and is stored as scale 0, zero point 0 and codes 0.            */
 void orc_quantize_row_asym(const float* x, int n, uint8_t* codes, float* scale_out,
                            uint8_t* zero_out) {
-  float mn = x[0], mx = x[0], sc;
-  for (int i = 1; i < n; ++i) {
-    if (x[i] < mn) mn = x[i];
-    if (x[i] > mx) mx = x[i];
+  float lo = 0.0f, hi = 0.0f, sc, z;
+  for (int i = 0; i < n; ++i) {
+    if (x[i] < lo) lo = x[i];
+    if (x[i] > hi) hi = x[i];
   }
-  sc = (mx - mn) / 255.0f;
+  sc = (hi - lo) / 255.0f;
   if (sc == 0.0f) {
     *scale_out = 0.0f;
     *zero_out = 0;
     for (int i = 0; i < n; ++i) codes[i] = 0;
     return;
   }
-  {
-    float z = rintf(-mn / sc);
-    if (z < 0.0f) z = 0.0f;
-    if (z > 255.0f) z = 255.0f;
-    *scale_out = sc;
-    *zero_out = (uint8_t)z;
-  }
+  z = rintf(-lo / sc);
+  if (z < 0.0f) z = 0.0f;
+  if (z > 255.0f) z = 255.0f;
+  *scale_out = sc;
+  *zero_out = (uint8_t)z;
   for (int i = 0; i < n; ++i) {
-    float c = rintf((x[i] - mn) / sc);
+    float c = rintf(x[i] / sc) + z;
     if (c < 0.0f) c = 0.0f;
     if (c > 255.0f) c = 255.0f;
     codes[i] = (uint8_t)c;

@@ -29,31 +29,57 @@ def test_worked_rows(case):
     assert deq.tolist() == case["dequantized"]
 
 
-def test_constant_and_zero_rows():
-    for v in (0.0, 0.75, -3.5):
+def test_zero_and_constant_rows():
+    """An all-zero row is stored as scale 0, zero point 0, codes 0.  A
+    constant nonzero row v spans [min(v, 0), max(v, 0)], so every value maps
+    to the end code (255 for v > 0, 0 for v < 0) and restores within half a
+    step of v."""
+    codes, sc, zp = oracle.quantize_row_asym(np.zeros(64, np.float32))
+    assert sc == 0 and zp == 0 and not codes.any()
+    for v in (0.75, -3.5, 1e-30):
         codes, sc, zp = oracle.quantize_row_asym(np.full(64, v, np.float32))
-        assert sc == 0 and zp == 0 and not codes.any()
+        assert sc > 0 and zp == (0 if v > 0 else 255)
+        assert np.all(codes == (255 if v > 0 else 0))
+        deq = (codes.astype(np.float64) - float(zp)) * np.float64(sc)
+        assert np.max(np.abs(deq - np.float64(np.float32(v)))) <= np.float64(sc) * (0.5 + 2.0 ** -16)
+
+
+def _check_row(x):
+    """Bounds that hold for any finite row: the range [min(x, 0), max(x, 0)]
+    spans 255 steps (to binary32 rounding), 0 restores exactly, the row's
+    extreme values take the end codes (within one code for the end whose
+    quotient is rounded), and every value restores within half a step plus
+    the binary32 rounding of the quotient x / scale (|x / scale| <= 255, so
+    at most 256 * 2^-24 of a step)."""
+    codes, sc, zp = oracle.quantize_row_asym(x)
+    x64 = x.astype(np.float64)
+    lo, hi = min(x64.min(), 0.0), max(x64.max(), 0.0)
+    assert abs(255.0 * np.float64(sc) - (hi - lo)) <= (hi - lo) * 2.0 ** -22
+    assert abs(float(zp) - (-lo / np.float64(sc))) <= 0.5 + 1e-4
+    if x64.min() < 0:
+        assert codes[int(np.argmin(x))] == 0
+    if x64.max() > 0:
+        assert codes[int(np.argmax(x))] >= 254
+    deq = (codes.astype(np.float64) - float(zp)) * np.float64(sc)
+    assert np.max(np.abs(deq - x64)) <= np.float64(sc) * (0.5 + 2.0 ** -16)
+    return codes, sc, zp
 
 
 def test_random_rows_bounds():
-    """Rows that contain both signs: the minimum maps to 0, the maximum to
-    255, 255 * scale equals max - min to binary32 rounding, and the restored
-    value is within one scale step of x (half a step from the code, half a
-    step from the rounded zero point)."""
     rng = np.random.default_rng(5)
     for n in (64, 128):
         for trial in range(200):
             x = (rng.standard_normal(n) * rng.choice([1e-3, 1.0, 40.0])).astype(np.float32)
-            x[rng.integers(n)] = -abs(x[rng.integers(n)]) - 1e-6   # ensure a negative
-            x[rng.integers(n)] = abs(x[rng.integers(n)]) + 1e-6    # and a positive value
-            codes, sc, zp = oracle.quantize_row_asym(x)
-            lo, hi = int(np.argmin(x)), int(np.argmax(x))
-            assert codes[lo] == 0 and codes[hi] == 255
-            rng_w = np.float64(x.max()) - np.float64(x.min())
-            assert abs(255.0 * np.float64(sc) - rng_w) <= rng_w * 2.0 ** -22
-            assert 0 <= zp <= 255
-            deq = (codes.astype(np.float64) - float(zp)) * np.float64(sc)
-            assert np.max(np.abs(deq - x.astype(np.float64))) <= np.float64(sc) * (1 + 2.0 ** -18)
+            kind = trial % 3
+            if kind == 1:
+                x = np.abs(x) + np.float32(rng.choice([0.0, 0.5, 30.0]))    # no negative value
+            elif kind == 2:
+                x = -np.abs(x) - np.float32(rng.choice([0.0, 0.5, 30.0]))   # no positive value
+            codes, sc, zp = _check_row(x.astype(np.float32))
+            if kind == 1:
+                assert zp == 0
+            if kind == 2:
+                assert zp == 255
 
 
 @pytest.mark.parametrize("src", ["f32", "bf16"])
@@ -62,7 +88,7 @@ def test_pool_quantizer_is_rowwise(src):
     at the right place; unlisted blocks stay zero."""
     rng = np.random.default_rng(6)
     x = rng.standard_normal((5, 3, BS, 64)).astype(np.float32)
-    x[1, 2, 7] = 0.25                                     # a constant row
+    x[1, 2, 7] = 0.0                                      # an all-zero row
     xs = W.to_bf16_bits(x) if src == "bf16" else x
     xf = W.bf16_bits_to_f32(xs) if src == "bf16" else xs
     ids = np.array([4, 1, 2], np.int32)
