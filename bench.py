@@ -72,6 +72,7 @@ def algorithmic_bytes(wl, ntok=1, window=0):
     q_out = wl.B * ntok * wl.Hq * wl.D * 2 * e_q
     lens = wl.B * 4
     attention = kv + tables + scales + q_out + lens
+    q_out_tables_lens = tables + q_out + lens
     write = 0
     if wl.write and ntok == 1 and window == 0:
         # new K/V rows read (in the pool's type, or q's for a quantizing
@@ -80,7 +81,45 @@ def algorithmic_bytes(wl, ntok=1, window=0):
         write = int(wl.B * wl.Hkv * wl.D * 2 * (e_new + e_kv))
         if wl.quant == "u8z":
             write += wl.B * wl.Hkv * 2 * 5
-    return dict(attention=attention, kv=kv, write=write, step=attention + write)
+    return dict(attention=attention, kv=kv, write=write, step=attention + write,
+                q_out_tables_lens=q_out_tables_lens)
+
+
+def unique_bytes(wl, ntok=1, window=0):
+    """Bytes of the distinct K/V rows (and their scales) a step reads: a
+    physical row that several sequences share (a common prefix) counts once.
+    With no sharing this equals the K/V part of algorithmic_bytes."""
+    import numpy as np
+
+    e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1, "fp4": 0.5}[wl.quant or wl.kv_dtype]
+    rows = {}
+    for s in range(wl.B):
+        L = int(wl.lens[s])
+        first = 0
+        if window > 0:
+            first = max(0, L - ntok + 1 - window)
+        for j in range(first // 16, -(-L // 16)):
+            b = int(wl.tables[s, j])
+            rows[b] = max(rows.get(b, 0), min(16, L - 16 * j))
+    n_rows = int(sum(rows.values()))
+    kv = int(n_rows * wl.Hkv * wl.D * 2 * e_kv)
+    if wl.quant == "u8z":
+        scales = n_rows * wl.Hkv * 2 * 5
+    else:
+        scales = len(rows) * wl.Hkv * 2 * 4 if wl.quant else 0
+    return dict(kv=kv, scales=scales, rows=n_rows, blocks=len(rows))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def kernel_source_hash() -> str:
@@ -158,11 +197,17 @@ class Replica:
             self.call, self.out = pkv.prepare_decode_step(
                 cache, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"], float(wl.scale),
                 partition_tokens=part, workspace=ws, out_dtype=out_dtype)
+            # the same step without the append: attention and the combine only
+            self.attention_only, _ = pkv.prepare_attention_decode(
+                cache, d["q"], d["tables"], d["lens"], float(wl.scale), partition_tokens=part,
+                workspace=ws, out=self.out)
         else:
             self.call, self.out = pkv.prepare_attention_decode(
                 cache, d["q"], d["tables"], d["lens"], float(wl.scale), partition_tokens=part,
                 workspace=ws, out_dtype=out_dtype)
         self.d, self.cache = d, cache
+        if not hasattr(self, "attention_only"):
+            self.attention_only = None
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -413,6 +458,20 @@ def main():
     torch.cuda.synchronize()
     kern_s = statistics.mean(a.elapsed_time(b) for a, b in evs) / 1e3
 
+    def event_time(fn_of):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        for i in range(K):
+            evs[i][0].record(stream)
+            fn_of(reps[i % len(reps)])()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) for a, b in evs) / 1e3
+
+    attn_s = None
+    if reps[0].attention_only is not None:
+        attn_s = event_time(lambda r: r.attention_only)
+
     ab = algorithmic_bytes(wl, args.tokens, args.window)
     value = ab["step"] / step_s / 1e9
     achieved = ab["step"] / kern_s / 1e9
@@ -455,6 +514,7 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(wl.B / step_s, 1),
         "kernel_ms_per_step": round(kern_s * 1e3, 4),
+        "attention_only_ms": None if attn_s is None else round(attn_s * 1e3, 4),
         "bytes_per_step": ab["step"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -462,11 +522,19 @@ def main():
                      "kernel": "the step's kernels (decode attention, then the combine)",
                      "bytes_per_launch": ab["step"]},
     }
+    if wl.quant or args.workload == 5:
+        # blocks shared between sequences are read once from HBM at best: the
+        # distinct rows' bytes beside the logical ones
+        ub = unique_bytes(wl, args.tokens, args.window)
+        ubytes = ub["kv"] + ub["scales"] + ab["q_out_tables_lens"] + ab["write"]
+        line["unique_bytes_per_step"] = ubytes
+        line["unique_GBps"] = round(ubytes / kern_s / 1e9, 1)
+        line["unique_frac_of_peak"] = round(ubytes / kern_s / 1e9 / HBM_PEAK_GBS, 4)
     if not args.no_cpu_baseline and args.tokens == 1 and args.window == 0:
         med, runs, threads = cpu_baseline(wl)
         line["cpu_baseline"] = {
             "value": round(ab["step"] / med / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": (f"the whole workload ({wl.B} sequences, {int(wl.lens.sum())} context "
                        f"tokens) per run, median of {runs} runs of {med:.3f} s; "
                        f"{wl.B / med:.1f} seq-steps/s")}

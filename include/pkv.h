@@ -170,12 +170,15 @@ int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
 
 /* Quantized append ([KVC] "KV Cache 的本质": each step appends the new token's
  * K and V; [MGMT] section 四, KVQuantizationCache.quantize_key with per-channel
- * parameters): for i < n with slot = slot_mapping[i] in range, each KV head's
- * row k[i][g][:] (and v[i][g][:]) is quantized on its own,
- *   scale = (max - min) / 255, zero = clamp(rint(-min / scale), 0, 255),
- *   code  = clamp(rint((x - min) / scale), 0, 255),
- * every step a binary32 operation rounding to nearest even; a row whose values
- * are all equal is stored as scale 0, zero 0, codes 0.  The codes go to row
+ * parameters, restored as (code - zero) * scale): for i < n with slot =
+ * slot_mapping[i] in range, each KV head's row k[i][g][:] (and v[i][g][:]) is
+ * quantized on its own over its range widened to hold 0,
+ *   lo = min(min x, 0), hi = max(max x, 0), scale = (hi - lo) / 255,
+ *   zero = clamp(rint(-lo / scale), 0, 255),
+ *   code = clamp(rint(x / scale) + zero, 0, 255),
+ * every step a binary32 operation rounding to nearest even, so every value
+ * restores within half a step; an all-zero row is stored as scale 0, zero 0,
+ * codes 0.  The codes go to row
  * slot % 16 of block slot / 16 and the scale and zero point to the same row
  * of k_scale / k_zero (v_scale / v_zero); no other row changes.  Bit-exact
  * with pkv_quantize of the same values.
@@ -187,13 +190,19 @@ int pkv_cache_write_quant(const pkv_cache_t* cache, const void* k, const void* v
                           void* stream);
 
 /* Workspace bytes pkv_attention_decode / pkv_decode_step need for the given
- * split: per (sequence, query head) and partial slot a running maximum, a sum
- * and a head_dim output row, all binary32, plus one int32 per sequence, each
- * part 256-byte aligned.  Fixed split (partition_tokens > 0, a multiple of
- * 16): one slot per partition; returns 0 when one partition covers
- * max_blocks_per_seq * 16 tokens or partition_tokens == 0 (no workspace
- * needed).  Balanced split (PKV_SPLIT_BALANCED): ceil(max_blocks_per_seq / 8)
- * + 1 slots.  Returns 0 for invalid sizes. */
+ * split.  The pages describe no split of a context; this is the standard
+ * partition-and-reduce of softmax attention (each partition of a long context
+ * leaves a partial maximum, sum and output, and a second pass combines them
+ * with the log-sum-exp rule, which equals the unsplit softmax up to
+ * rounding).  Per (sequence, query head) and partial slot
+ * a running maximum, a sum and a head_dim output row, all binary32, plus one
+ * int32 per sequence, each part 256-byte aligned.  Fixed split
+ * (partition_tokens > 0, a multiple of 16): one slot per partition; returns 0
+ * when one partition covers max_blocks_per_seq * 16 tokens or
+ * partition_tokens == 0 (no workspace needed).  Balanced split
+ * (PKV_SPLIT_BALANCED): ceil(max_blocks_per_seq / 16) + 1 slots (a range
+ * holds at least 16 blocks, so a sequence meets at most that many ranges).
+ * Returns 0 for invalid sizes. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_tokens);
 
@@ -341,8 +350,12 @@ int pkv_quantize(const pkv_cache_t* src, const pkv_cache_t* dst, const int32_t* 
 int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t n, void* stream);
 
 /* Gather (diagnostic): copies each sequence's K and V, in logical order, into
- * contiguous rows k_out[cu_seqlens[s] + t][g][:] for t < context_lens[s].
- * Bit-exact copy of the stored elements (codes for 8-bit pools).
+ * contiguous rows k_out[cu_seqlens[s] + t][g][:] for t < context_lens[s]:
+ * the logical-to-physical translation of [KVC] "PagedAttention：vLLM 的显存碎片
+ * 治理" (a sequence's block table maps its logical blocks to physical ones,
+ * which need not be contiguous) undone into one contiguous copy, so that a
+ * test can compare a sequence's cached K/V byte for byte.  Bit-exact copy of
+ * the stored elements (codes for 8- and 4-bit pools).
  *   cu_seqlens: device int32 [num_seqs + 1], cu_seqlens[s+1] = cu_seqlens[s] + L_s
  *   k_out, v_out: device [cu_seqlens[num_seqs]][num_kv_heads][head_dim]. */
 int pkv_gather(const pkv_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,

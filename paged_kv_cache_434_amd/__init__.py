@@ -297,6 +297,29 @@ def alloc_workspace(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, partiti
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+def _check_query_out(cache, q, out, tensors, lead):
+    """Shape and device checks of a decode-family call, made before any
+    pointer is taken: q is [*lead][Hq][head_dim] with the pool's head_dim and
+    Hq a multiple of its KV heads, out (if given) has q's shape, and every
+    other tensor lives on q's device.  The kernels index q, out and the
+    workspace with the pool's head_dim, so a mismatch here would otherwise
+    read or write out of bounds."""
+    if q.dim() != len(lead) + 2:
+        raise ValueError(f"q must have {len(lead) + 2} dims")
+    Hq, D = q.shape[-2], q.shape[-1]
+    if D != cache.head_dim:
+        raise ValueError(f"q has head_dim {D}, the pool {cache.head_dim}")
+    if Hq % cache.num_kv_heads != 0:
+        raise ValueError(f"{Hq} query heads are not a multiple of {cache.num_kv_heads} KV heads")
+    if tuple(q.shape[:-2]) != tuple(lead):
+        raise ValueError(f"q's leading dims {tuple(q.shape[:-2])} differ from {tuple(lead)}")
+    if out is not None and tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q.shape)}")
+    for name, t in tensors:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+
+
 def _decode_call(cache: PagedCache, q, block_tables, context_lens, scale: float,
                  partition_tokens: int, workspace, out, out_dtype, stream, append):
     """Checks and marshals one decode call; returns (name, function, args, out,
@@ -305,10 +328,17 @@ def _decode_call(cache: PagedCache, q, block_tables, context_lens, scale: float,
     qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
     if qd is None:
         raise TypeError("q must be float32 or bfloat16")
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs][num_q_heads][head_dim]")
+    B, Hq, D = q.shape
+    _check_query_out(cache, q, out, (("block_tables", block_tables),
+                                     ("context_lens", context_lens), ("out", out),
+                                     ("workspace", workspace),
+                                     ("k_new", None if append is None else append[0]),
+                                     ("v_new", None if append is None else append[1])), (B,))
     _need(q, "q", None, 3)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
-    B, Hq, D = q.shape
     if context_lens.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("q, block_tables and context_lens disagree on the batch size")
     if append is not None:
@@ -375,10 +405,15 @@ def attention_multi(cache: PagedCache, q, block_tables, context_lens, scale: flo
     qd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
     if qd is None:
         raise TypeError("q must be float32 or bfloat16")
+    if q.dim() != 4:
+        raise ValueError("q must be [num_seqs][tokens_per_seq][num_q_heads][head_dim]")
+    B, k, Hq, D = q.shape
+    _check_query_out(cache, q, out, (("block_tables", block_tables),
+                                     ("context_lens", context_lens), ("out", out),
+                                     ("workspace", workspace)), (B, k))
     _need(q, "q", None, 4)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
-    B, k, Hq, D = q.shape
     if context_lens.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("q, block_tables and context_lens disagree on the batch size")
     od = out_dtype or (out.dtype if out is not None else q.dtype)

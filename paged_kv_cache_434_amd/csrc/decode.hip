@@ -799,20 +799,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 // its first block records for the combine kernel.  The eight wavefronts of one
 // v are consecutive launch indices, so they run side by side on different XCDs
 // and read the eight heads of the same blocks at the same time.
-#ifndef PKV_BAL_STAGES
-#define PKV_BAL_STAGES 2
-#define PKV_BAL_WAVES 2
-#endif
-#ifndef PKV_BAL_STAGES_Q8
-#define PKV_BAL_STAGES_Q8 2
-#endif
-// INT8 (one query token) asks for three wavefronts per SIMD: with its fp16
-// P V it needs 170 registers and would otherwise drop to two (measured on the
-// shared-prefix INT8 workload: 91.8 us at two, 87.4 us at three, where two
-// registers are spilled: one 8-byte scratch store and reload per two blocks).
+//
+// Two blocks in flight per wavefront and two wavefronts per SIMD for every
+// format (three or four blocks in flight, and other occupancies, measured
+// slower).  INT8 (one query token) asks for three wavefronts per SIMD: with
+// its fp16 P V it needs 170 registers and would otherwise drop to two
+// (measured on the shared-prefix INT8 workload: 91.8 us at two, 87.4 us at
+// three, where two registers are spilled: one 8-byte scratch store and
+// reload per two blocks).
+constexpr int kBalStages = 2;
+constexpr int kBalWaves = 2;
 template <int D, int KV, int OUT, int MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
-    KV == KV_I8 && !MQ ? 3 : PKV_BAL_WAVES))) void
+    KV == KV_I8 && !MQ ? 3 : kBalWaves))) void
 decode_mfma_balanced_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
@@ -910,9 +909,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int K = (R1 - 1) / per - vf + 1;
     const int slot = v - vf;
     if (g == 0 && pass == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
-    // 8-bit tiles are half the bytes of bf16 ones: they may keep more blocks in flight
-    constexpr int kStages = KV == KV_BF16 ? PKV_BAL_STAGES : PKV_BAL_STAGES_Q8;
-    mfma_segment<D, KV, OUT, kStages, MQ>(a, s, g, L, fb + x - R0, fb + e - R0, slot, K == 1,
+    mfma_segment<D, KV, OUT, kBalStages, MQ>(a, s, g, L, fb + x - R0, fb + e - R0, slot, K == 1,
                                           tok0, lds_k, lds_v, lds_p);
     if (e >= x1) break;
     x = e;

@@ -4,6 +4,8 @@
 // section's asymmetric scheme (KVQuantizationCache with per-channel
 // parameters): uint8 codes with a scale and a zero point per (head, token)
 // row of head_dim values, which also makes a one-token append local to its row.
+// The per-row codes are those that the page's restore formula (code - zero)
+// * scale inverts, over the row's range widened to hold 0 (see AsymRow).
 //
 // One wavefront per (block, KV head, K-or-V) tile of 16 x head_dim values:
 // coalesced 16-byte loads into registers, a wave-wide max of |x|, then
@@ -182,21 +184,28 @@ int launch_q(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids,
                 (int64_t)(block_stride_bytes(src) / sizeof(SrcT)), (int64_t)block_stride_bytes(dst));
 }
 
-// Asymmetric row parameters and codes (binary32 steps, ties to even):
-// scale = (max - min) / 255, zero = clamp(rint(-min / scale), 0, 255),
-// code = clamp(rint((x - min) / scale), 0, 255); a zero-width row (scale 0)
-// gets zero 0 and codes 0.
+// Asymmetric row parameters and codes (binary32 steps, ties to even).  The
+// row's range is widened to hold 0, so the zero point is the code of 0 and
+// never clamps, and each value takes the code whose restored value
+// (code - zero) * scale is nearest:
+//   lo = min(row min, 0), hi = max(row max, 0), scale = (hi - lo) / 255,
+//   zero = clamp(rint(-lo / scale), 0, 255),
+//   code = clamp(rint(x / scale) + zero, 0, 255);
+// an all-zero row (scale 0) gets zero 0 and codes 0.
 struct AsymRow {
-  float mn, sc;
+  float sc, zf;
   uint8_t zero;
-  __device__ __forceinline__ AsymRow(float lo, float hi) : mn(lo) {
+  __device__ __forceinline__ AsymRow(float lo, float hi) {
+    lo = fminf(lo, 0.0f);
+    hi = fmaxf(hi, 0.0f);
     sc = (hi - lo) / 255.0f;
-    zero = 0;
-    if (sc != 0.0f) zero = (uint8_t)fminf(fmaxf(rintf(-lo / sc), 0.0f), 255.0f);
+    zf = 0.0f;
+    if (sc != 0.0f) zf = fminf(fmaxf(rintf(-lo / sc), 0.0f), 255.0f);
+    zero = (uint8_t)zf;
   }
   __device__ __forceinline__ uint32_t code(float x) const {
     if (sc == 0.0f) return 0u;
-    return (uint32_t)fminf(fmaxf(rintf((x - mn) / sc), 0.0f), 255.0f);
+    return (uint32_t)fminf(fmaxf(rintf(x / sc) + zf, 0.0f), 255.0f);
   }
 };
 

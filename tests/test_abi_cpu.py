@@ -249,3 +249,46 @@ def test_fp4_pool_validation():
     assert pkv.pool_bytes(10, 8, 128, "fp4") == 10 * 8 * 16 * 128 // 2
     q = lambda a, b: lib.pkv_quantize(ctypes.byref(a), ctypes.byref(b), None, 0, None)
     assert q(fp4, fp4) == 3
+
+
+def test_binding_rejects_mismatched_query_and_output_shapes():
+    """The decode wrappers check q's head_dim against the pool's, the output's
+    shape against q's and the devices of the other tensors, before any pointer
+    is taken (the kernels index q, out and the workspace with the pool's
+    head_dim).  CPU tensors suffice: the checks come before the device check."""
+    import types
+
+    import torch
+
+    cache = types.SimpleNamespace(head_dim=128, num_kv_heads=8, kv_dtype="bf16")
+    B, Hq = 3, 32
+    tables = torch.zeros((B, 4), dtype=torch.int32)
+    lens = torch.ones(B, dtype=torch.int32)
+    q = torch.zeros((B, Hq, 128), dtype=torch.bfloat16)
+    cases = [
+        (torch.zeros((B, Hq, 64), dtype=torch.bfloat16), None),       # head_dim 64 != 128
+        (torch.zeros((B, 12, 128), dtype=torch.bfloat16), None),      # 12 % 8 != 0
+        (q, torch.zeros((B, Hq, 64), dtype=torch.bfloat16)),          # short out
+        (q, torch.zeros((B - 1, Hq, 128), dtype=torch.bfloat16)),     # out batch
+        (torch.zeros((B, Hq), dtype=torch.bfloat16), None),           # q dims
+    ]
+    for qq, out in cases:
+        with pytest.raises(ValueError):
+            pkv.attention_decode(cache, qq, tables, lens, 0.1, out=out)
+        with pytest.raises(ValueError):
+            pkv.decode_step(cache, qq, q[:, :8], q[:, :8], tables, lens, 0.1, out=out)
+    q4 = q.view(B, 1, Hq, 128)
+    for qq, out in [(torch.zeros((B, 2, Hq, 64), dtype=torch.bfloat16), None),
+                    (q4, torch.zeros((B, 2, Hq, 128), dtype=torch.bfloat16)),
+                    (q4, torch.zeros((B, 1, Hq, 127), dtype=torch.bfloat16)),
+                    (q, None)]:
+        with pytest.raises(ValueError):
+            pkv.attention_multi(cache, qq, tables, lens, 0.1, out=out)
+        with pytest.raises(ValueError):
+            pkv.attention_window(cache, qq, tables, lens, 0.1, 16, out=out)
+    # a tensor on another device than q
+    meta = torch.empty((B, 4), dtype=torch.int32, device="meta")
+    with pytest.raises(ValueError):
+        pkv.attention_decode(cache, q, meta, lens, 0.1)
+    with pytest.raises(ValueError):
+        pkv.attention_multi(cache, q4, tables, lens.to("meta"), 0.1)

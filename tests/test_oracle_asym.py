@@ -220,3 +220,25 @@ def test_copy_blocks_moves_row_parameters():
         a[[4, 0]] = a[[1, 6]]
     for got, want in zip((kc, vc, ks, vs, kz, vz), ref):
         assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_one_signed_rows_attend_like_the_source(sign):
+    """Rows of one sign (|N(0,1)| + 2 or its negative): attention over the
+    restored per-row pool stays within 5e-2 of attention over the source
+    values, since every value restores within half a step (scale below
+    4.5 / 255 for these rows).  Under the page listing's clamped zero point
+    the same rows would restore as x - min (or x - max), about 2 away."""
+    rng = np.random.default_rng(12)
+    lens = [1, 16, 40, 75]
+    Hq, Hkv, D = 8, 2, 64
+    d = tiny_paged(rng, lens, Hq, Hkv, D, dtype="f32", q_dtype="bf16")
+    k = (sign * (np.abs(d["k"]) + 2)).astype(np.float32)
+    v = (sign * (np.abs(d["v"]) + 2)).astype(np.float32)
+    kc, ks, kz = oracle.quantize_asym(k, "f32")
+    vc, vs, vz = oracle.quantize_asym(v, "f32")
+    assert np.all(kz == (0 if sign > 0 else 255)) and np.all(vz == kz)
+    out = oracle.decode(d["q"], "bf16", kc, vc, "u8z", d["tables"], d["lens"], 0.125,
+                        k_scale=ks, v_scale=vs, k_zero=kz, v_zero=vz)
+    src = oracle.decode(d["q"], "bf16", k, v, "f32", d["tables"], d["lens"], 0.125)
+    assert np.max(np.abs(out - src)) <= 5e-2
