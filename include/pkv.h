@@ -266,6 +266,28 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
                     float scale, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
 
+/* pkv_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and pool update
+ * as pkv_decode_step; the split partials go to a fixed array of 32 MiB
+ * (33554432 bytes) in device memory that the library holds on every GPU it
+ * runs on until the process ends.  Requests whose
+ * pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ * max_blocks_per_seq, partition_tokens) exceeds 32 MiB return
+ * PKV_ERR_WORKSPACE (the Llama-3-8B shape with 64 sequences of up to 4096
+ * tokens and the balanced split needs 18.1 MB).  The call allocates nothing:
+ * no hipMalloc, hipFree or allocating library routine.  All calls on one GPU
+ * share that GPU's array and nothing in it needs clearing between calls;
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different threads without ordering) race on it and give unspecified
+ * results. */
+int pkv_decode_step_noalloc(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                            const void* k, const void* v, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                            int32_t partition_tokens, void* out, int32_t out_dtype,
+                            void* stream);
+
 /* Paged attention for several query tokens per sequence ([KVC] "投机解码":
  * the large model checks k drafted tokens in one forward pass; "Continuous
  * Batching": a long prompt is fed in chunks).  The last k = tokens_per_seq of

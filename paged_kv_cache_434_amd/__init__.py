@@ -71,6 +71,8 @@ def _load():
                                                     ctypes.c_size_t, P, I32, P]),
             "pkv_decode_step": (ctypes.c_int, [C, P, I32, P, P, P, I32, P, I32, I32, F, I32, P,
                                                ctypes.c_size_t, P, I32, P]),
+            "pkv_decode_step_noalloc": (ctypes.c_int, [C, P, I32, P, P, P, I32, P, I32, I32, F,
+                                                       I32, P, I32, P]),
             "pkv_attention_multi": (ctypes.c_int, [C, P, I32, I32, P, I32, P, I32, I32, F, I32, P,
                                                    ctypes.c_size_t, P, I32, P]),
             "pkv_attention_window": (ctypes.c_int, [C, P, I32, I32, I32, P, I32, P, I32, I32, F,
@@ -98,6 +100,7 @@ EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_m
                     "pkv_slot_mapping_tokens", "pkv_attention_multi", "pkv_attention_window",
                     "pkv_cache_write", "pkv_cache_write_quant", "pkv_decode_workspace_bytes",
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
+                    "pkv_decode_step_noalloc",
                     "pkv_quantize", "pkv_copy_blocks",
                     "pkv_gather", "pkv_validate_tables")
 
@@ -392,6 +395,27 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, 
                                           partition_tokens, workspace, out, out_dtype, stream,
                                           (k_new, v_new))
     _check(name, fn(*args))
+    return out
+
+
+NOALLOC_MAX_WORKSPACE = 32 << 20   # bytes of the library's fixed scratch array
+
+
+def decode_step_noalloc(cache: PagedCache, q, k_new, v_new, block_tables, context_lens,
+                        scale: float, partition_tokens: int = 0, out=None, out_dtype=None,
+                        stream=None):
+    """decode_step through pkv_decode_step_noalloc: the split partials go to the
+    library's fixed per-GPU scratch array instead of a workspace, so nothing
+    is allocated beyond ``out`` (pass ``out`` to allocate nothing at all).
+    Calls that overlap in time on one GPU race on that array."""
+    name, fn, args, out, _ = _decode_call(cache, q, block_tables, context_lens, scale, 0,
+                                          None, out, out_dtype, stream, (k_new, v_new))
+    # pkv_decode_step's arguments (desc, q, q dtype, k, v, tables, max blocks,
+    # lens, B, Hq, scale | partition, workspace, bytes | out, out dtype,
+    # stream) without the workspace and its size
+    assert len(args) == 17
+    args = args[:11] + (partition_tokens,) + args[14:]
+    _check("pkv_decode_step_noalloc", _load().pkv_decode_step_noalloc(*args))
     return out
 
 

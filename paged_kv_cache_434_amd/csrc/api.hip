@@ -4,11 +4,43 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 
 using namespace pkv;
 
 namespace {
+
+// ---- fixed scratch of pkv_decode_step_noalloc ------------------------------
+// The split partials of the allocation-free decode step live in this array,
+// one copy on every GPU the library runs on, held until the process ends.  In
+// host code `scratch` only names the symbol: its device address is looked up
+// once per device with hipGetSymbolAddress and only that address is passed
+// to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> scratch_addr[kScratchDevices];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device), or null if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  p = scratch_addr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  scratch_addr[dev].store(q, std::memory_order_release);
+  return q;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -143,7 +175,7 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                          int32_t num_seqs, int32_t num_q_heads, float scale,
                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                          void* out, int32_t out_dtype, void* stream, bool append,
-                         int32_t ntok = 1, int32_t window = 0) {
+                         int32_t ntok = 1, int32_t window = 0, bool use_scratch = false) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   if ((q_dtype != PKV_F32 && q_dtype != PKV_BF16) || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
@@ -176,6 +208,12 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   if (np > 1) {
     size_t need = decode_workspace_layout((int64_t)num_seqs * ntok * num_q_heads, np,
                                           cache->head_dim, num_seqs, nullptr, nullptr, nullptr);
+    if (use_scratch) {
+      if (need > kScratchBytes) return PKV_ERR_WORKSPACE;
+      workspace = scratch_on_current_device();
+      if (!workspace) return PKV_ERR_HIP;
+      workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
   }
@@ -213,6 +251,17 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
   return decode_common(cache, q, q_dtype, k, v, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, partition_tokens, workspace, workspace_bytes,
                        out, out_dtype, stream, true);
+}
+
+int pkv_decode_step_noalloc(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                            const void* k, const void* v, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, float scale,
+                            int32_t partition_tokens, void* out, int32_t out_dtype,
+                            void* stream) {
+  return decode_common(cache, q, q_dtype, k, v, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, partition_tokens, nullptr, 0, out,
+                       out_dtype, stream, true, 1, 0, true);
 }
 
 int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype,

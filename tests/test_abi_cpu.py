@@ -292,3 +292,29 @@ def test_binding_rejects_mismatched_query_and_output_shapes():
         pkv.attention_decode(cache, q, meta, lens, 0.1)
     with pytest.raises(ValueError):
         pkv.attention_multi(cache, q4, tables, lens.to("meta"), 0.1)
+
+
+def test_decode_step_noalloc_rejects_bad_arguments():
+    """The allocation-free decode step validates like pkv_decode_step and
+    rejects, before any HIP call, a split whose partials would not fit its
+    fixed 32 MiB scratch array."""
+    lib = pkv.lib()
+    c = _cache(num_blocks=20000, num_kv_heads=8)
+
+    def step(B=64, Hq=32, maxb=256, part=pkv.SPLIT_BALANCED, q=FAKE, k=FAKE, out=FAKE):
+        return lib.pkv_decode_step_noalloc(ctypes.byref(c), q, 1, k, FAKE, FAKE, maxb, FAKE, B,
+                                           Hq, ctypes.c_float(0.1), part, out, 1, None)
+
+    assert step(Hq=12) == 2                            # Hq % Hkv != 0
+    assert step(q=None) == 1
+    assert step(k=None) == 1
+    assert step(part=24) == 2
+    assert step(B=0) == 0                              # nothing to do, no launch
+    # 256 sequences x 64 query heads of up to 8192 tokens: the partials need
+    # ~277 MB, beyond the 32 MiB array
+    big = lib.pkv_decode_workspace_bytes(256, 64, 128, 512, pkv.SPLIT_BALANCED)
+    assert big > pkv.NOALLOC_MAX_WORKSPACE
+    assert step(B=256, Hq=64, maxb=512) == 5
+    # the Llama-3-8B shape fits
+    assert lib.pkv_decode_workspace_bytes(64, 32, 128, 256, pkv.SPLIT_BALANCED) <= \
+        pkv.NOALLOC_MAX_WORKSPACE
