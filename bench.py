@@ -147,7 +147,7 @@ class Replica:
     """One independent copy of the workload's device inputs plus a prepared
     step call."""
 
-    def __init__(self, wl, part, layout, ntok=1, window=0):
+    def __init__(self, wl, part, layout, ntok=1, window=0, prefix_blocks=0):
         import numpy as np
         import torch
         import paged_kv_cache_434_amd as pkv
@@ -201,6 +201,12 @@ class Replica:
             self.attention_only, _ = pkv.prepare_attention_decode(
                 cache, d["q"], d["tables"], d["lens"], float(wl.scale), partition_tokens=part,
                 workspace=ws, out=self.out)
+        elif prefix_blocks > 0:
+            # the tables share their first prefix_blocks entries (a common prompt)
+            ws = pkv.alloc_workspace(wl.B, wl.Hq, wl.D, wl.max_blocks, pkv.SPLIT_BALANCED)
+            self.call, self.out = pkv.prepare_attention_prefix(
+                cache, d["q"], d["tables"], d["lens"], float(wl.scale), prefix_blocks,
+                workspace=ws, out_dtype=out_dtype)
         else:
             self.call, self.out = pkv.prepare_attention_decode(
                 cache, d["q"], d["tables"], d["lens"], float(wl.scale), partition_tokens=part,
@@ -392,6 +398,10 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (>0: attention over each query's most recent "
                          "window only; no append)")
+    ap.add_argument("--prefix-blocks", type=int, default=-1,
+                    help="shared-prefix attention over that many common table entries "
+                         "(-1: the workload's shared prefix for workload 5, none otherwise; "
+                         "0: the general attention path)")
     ap.add_argument("--op", choices=("step", "quantize", "copy_blocks"), default="step",
                     help="what to time: the decode step (default) or another operation")
     args = ap.parse_args()
@@ -428,7 +438,15 @@ def main():
     e_kv = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "u8z": 1, "fp4": 0.5}[wl.quant or wl.kv_dtype]
     pool_bytes = int(wl.num_blocks * wl.Hkv * 16 * wl.D * 2 * e_kv)
     n_rep = args.replicas or max(2, min(8, math.ceil(1.3e9 / pool_bytes) + 1))
-    reps = [Replica(wl, part, args.layout, args.tokens, args.window) for _ in range(n_rep)]
+    prefix_blocks = args.prefix_blocks
+    if prefix_blocks < 0:
+        prefix_blocks = W.SPECS[5]["prefix"] // 16 if args.workload == 5 else 0
+    if prefix_blocks > 0 and (wl.write or args.tokens > 1 or args.window > 0):
+        sys.exit("--prefix-blocks applies to attention over the shared-prefix workload (5)")
+    if prefix_blocks > 0:
+        part = pkv.SPLIT_BALANCED
+    reps = [Replica(wl, part, args.layout, args.tokens, args.window, prefix_blocks)
+            for _ in range(n_rep)]
     print(f"# workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
           f"sum(L)={int(wl.lens.sum())} pool={wl.num_blocks} quant={wl.quant} "
           f"partition={part} layout={args.layout} replicas={len(reps)}",
@@ -475,7 +493,8 @@ def main():
     ab = algorithmic_bytes(wl, args.tokens, args.window)
     value = ab["step"] / step_s / 1e9
     achieved = ab["step"] / kern_s / 1e9
-    key = (f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/{part}"
+    key = (f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/"
+           + (f"prefix{prefix_blocks}" if prefix_blocks > 0 else f"{part}")
            + (f"/tokens{args.tokens}" if args.tokens > 1 else "")
            + (f"/window{args.window}" if args.window > 0 else ""))
     traffic = recorded_traffic(key)
@@ -497,7 +516,9 @@ def main():
                    "num_kv_heads": wl.Hkv, "head_dim": wl.D, "block_size": 16,
                    "kv_dtype": wl.quant or wl.kv_dtype, "sum_context": int(wl.lens.sum()),
                    "pool_blocks": wl.num_blocks, "partition_tokens": part,
-                   "split": "balanced" if part == pkv.SPLIT_BALANCED else "fixed",
+                   "split": ("shared prefix" if prefix_blocks > 0 else
+                             "balanced" if part == pkv.SPLIT_BALANCED else "fixed"),
+                   "prefix_blocks": prefix_blocks,
                    "layout": args.layout, "replicas": len(reps),
                    "query_tokens_per_seq": args.tokens,
                    "window": args.window,
@@ -510,6 +531,9 @@ def main():
                             "paged attention + partition combine") if wl.write and wl.quant else
                            ("decode step: slot of position L-1 + cache write + paged attention "
                             "(one launch) + partition combine") if wl.write else
+                           (f"shared-prefix paged attention ({prefix_blocks} common blocks run "
+                            "once per group of sequences) + partition combine")
+                           if prefix_blocks > 0 else
                            "paged attention over a quantized pool + partition combine"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(wl.B / step_s, 1),
@@ -530,6 +554,13 @@ def main():
         line["unique_bytes_per_step"] = ubytes
         line["unique_GBps"] = round(ubytes / kern_s / 1e9, 1)
         line["unique_frac_of_peak"] = round(ubytes / kern_s / 1e9 / HBM_PEAK_GBS, 4)
+        if ubytes < ab["step"]:
+            # the HBM roofline is priced on the bytes HBM must deliver: a
+            # shared block's bytes once; the logical figure stays in `value`
+            line["roofline"].update(
+                achieved=round(ubytes / kern_s / 1e9, 1),
+                frac=round(ubytes / kern_s / 1e9 / HBM_PEAK_GBS, 4), bytes_per_launch=ubytes,
+                note="unique bytes (each shared block once); value counts them per sequence")
     if not args.no_cpu_baseline and args.tokens == 1 and args.window == 0:
         med, runs, threads = cpu_baseline(wl)
         line["cpu_baseline"] = {

@@ -200,8 +200,10 @@ int pkv_cache_write_quant(const pkv_cache_t* cache, const void* k, const void* v
  * (partition_tokens > 0, a multiple of 16): one slot per partition; returns 0
  * when one partition covers max_blocks_per_seq * 16 tokens or
  * partition_tokens == 0 (no workspace needed).  Balanced split
- * (PKV_SPLIT_BALANCED): ceil(max_blocks_per_seq / 16) + 1 slots (a range
- * holds at least 16 blocks, so a sequence meets at most that many ranges).
+ * (PKV_SPLIT_BALANCED, also for pkv_attention_prefix): ceil(max_blocks_per_seq
+ * / 16) + 3 slots (a range holds at least 16 blocks, so a run of n blocks
+ * meets at most ceil((n - 1) / 16) + 1 ranges, and a shared prefix cuts a
+ * sequence's blocks into two runs).
  * Returns 0 for invalid sizes. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_tokens);
@@ -266,6 +268,29 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
                     float scale, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
 
+/* Paged decode attention over a shared prefix ([KVC] "意外的收获：prefix
+ * sharing": requests that start with the same prompt share its KV blocks;
+ * [MGMT] section 二, copy_prefix: a new request's table takes the prefix's
+ * physical blocks).  The first prefix_blocks entries of every sequence's
+ * block table must be the same physical blocks; the caller knows this from
+ * the prefix it shared.  The result is that of pkv_attention_decode with the
+ * balanced split (the same definition, up to rounding): each group of
+ * 16 / G sequences (G = num_q_heads / num_kv_heads) runs the shared blocks
+ * once for all its query heads, every sequence's remaining blocks run as
+ * usual, and the pieces are combined.  A sequence may be shorter than the
+ * prefix (positions past its length are masked) or empty.
+ *   prefix_blocks: 0 <= prefix_blocks <= max_blocks_per_seq (0: no sharing)
+ *   workspace: at least pkv_decode_workspace_bytes(num_seqs, num_q_heads,
+ *     head_dim, max_blocks_per_seq, PKV_SPLIT_BALANCED) bytes.
+ * Other arguments and dtypes as for pkv_attention_decode, except that fp32
+ * pools are PKV_ERR_UNSUPPORTED here.  Tables that do not share their first
+ * prefix_blocks entries give unspecified output (never a memory fault). */
+int pkv_attention_prefix(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t prefix_blocks, void* workspace,
+                         size_t workspace_bytes, void* out, int32_t out_dtype, void* stream);
+
 /* pkv_decode_step without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, results and pool update
@@ -275,7 +300,7 @@ int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, co
  * pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
  * max_blocks_per_seq, partition_tokens) exceeds 32 MiB return
  * PKV_ERR_WORKSPACE (the Llama-3-8B shape with 64 sequences of up to 4096
- * tokens and the balanced split needs 18.1 MB).  The call allocates nothing:
+ * tokens and the balanced split needs 20.2 MB).  The call allocates nothing:
  * no hipMalloc, hipFree or allocating library routine.  All calls on one GPU
  * share that GPU's array and nothing in it needs clearing between calls;
  * calls that overlap in time on one GPU (on different streams, or from

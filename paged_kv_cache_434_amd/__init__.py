@@ -71,6 +71,8 @@ def _load():
                                                     ctypes.c_size_t, P, I32, P]),
             "pkv_decode_step": (ctypes.c_int, [C, P, I32, P, P, P, I32, P, I32, I32, F, I32, P,
                                                ctypes.c_size_t, P, I32, P]),
+            "pkv_attention_prefix": (ctypes.c_int, [C, P, I32, P, I32, P, I32, I32, F, I32, P,
+                                                    ctypes.c_size_t, P, I32, P]),
             "pkv_decode_step_noalloc": (ctypes.c_int, [C, P, I32, P, P, P, I32, P, I32, I32, F,
                                                        I32, P, I32, P]),
             "pkv_attention_multi": (ctypes.c_int, [C, P, I32, I32, P, I32, P, I32, I32, F, I32, P,
@@ -100,7 +102,7 @@ EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_m
                     "pkv_slot_mapping_tokens", "pkv_attention_multi", "pkv_attention_window",
                     "pkv_cache_write", "pkv_cache_write_quant", "pkv_decode_workspace_bytes",
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
-                    "pkv_decode_step_noalloc",
+                    "pkv_decode_step_noalloc", "pkv_attention_prefix",
                     "pkv_quantize", "pkv_copy_blocks",
                     "pkv_gather", "pkv_validate_tables")
 
@@ -395,6 +397,33 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, 
                                           partition_tokens, workspace, out, out_dtype, stream,
                                           (k_new, v_new))
     _check(name, fn(*args))
+    return out
+
+
+def prepare_attention_prefix(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                             prefix_blocks: int, workspace=None, out=None, out_dtype=None,
+                             stream=None):
+    """attention_prefix, prepared: returns (PreparedCall, out)."""
+    name, fn, args, out, ws = _decode_call(cache, q, block_tables, context_lens, scale,
+                                           SPLIT_BALANCED, workspace, out, out_dtype, stream,
+                                           None)
+    if int(prefix_blocks) < 0 or int(prefix_blocks) > block_tables.shape[1]:
+        raise ValueError("prefix_blocks must lie in [0, max_blocks_per_seq]")
+    # pkv_attention_decode's arguments with prefix_blocks in place of the split
+    assert len(args) == 15
+    args = args[:9] + (int(prefix_blocks),) + args[10:]
+    keep = (cache, q, block_tables, context_lens, ws, out)
+    return PreparedCall("pkv_attention_prefix", _load().pkv_attention_prefix, args, keep), out
+
+
+def attention_prefix(cache: PagedCache, q, block_tables, context_lens, scale: float,
+                     prefix_blocks: int, workspace=None, out=None, out_dtype=None, stream=None):
+    """Decode attention whose sequences share their first ``prefix_blocks``
+    table entries (a common prompt): the shared blocks run once per group of
+    16 / G sequences.  Same result as attention_decode."""
+    call, out = prepare_attention_prefix(cache, q, block_tables, context_lens, scale,
+                                         prefix_blocks, workspace, out, out_dtype, stream)
+    call()
     return out
 
 

@@ -175,7 +175,8 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
                          int32_t num_seqs, int32_t num_q_heads, float scale,
                          int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                          void* out, int32_t out_dtype, void* stream, bool append,
-                         int32_t ntok = 1, int32_t window = 0, bool use_scratch = false) {
+                         int32_t ntok = 1, int32_t window = 0, bool use_scratch = false,
+                         int32_t prefix_blocks = -1) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   if ((q_dtype != PKV_F32 && q_dtype != PKV_BF16) || (out_dtype != PKV_F32 && out_dtype != PKV_BF16))
@@ -193,6 +194,11 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   if (window < 0) return PKV_ERR_SHAPE;
   if ((ntok > 1 || window > 0) && kv == PKV_F32) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * ntok * num_q_heads > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
+  if (prefix_blocks >= 0) {
+    if (prefix_blocks > max_blocks_per_seq) return PKV_ERR_SHAPE;
+    if (kv == PKV_F32) return PKV_ERR_UNSUPPORTED;
+    partition_tokens = PKV_SPLIT_BALANCED;
+  }
   if (num_seqs == 0) return PKV_OK;
   if (append) {
     if (kv != PKV_F32 && kv != PKV_BF16 && kv != PKV_U8_ZP) return PKV_ERR_UNSUPPORTED;
@@ -229,7 +235,7 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   DecodeArgs a{cache,     q,          q_dtype,   block_tables,     max_blocks_per_seq,
                context_lens, num_seqs, num_q_heads, scale,          partition_tokens,
                workspace, out,        out_dtype, fused ? k_new : nullptr,
-               fused ? v_new : nullptr, ntok, window};
+               fused ? v_new : nullptr, ntok, window, prefix_blocks};
   return launch_decode(a, st);
 }
 
@@ -262,6 +268,18 @@ int pkv_decode_step_noalloc(const pkv_cache_t* cache, const void* q, int32_t q_d
   return decode_common(cache, q, q_dtype, k, v, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, partition_tokens, nullptr, 0, out,
                        out_dtype, stream, true, 1, 0, true);
+}
+
+int pkv_attention_prefix(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t prefix_blocks, void* workspace,
+                         size_t workspace_bytes, void* out, int32_t out_dtype, void* stream) {
+  if (prefix_blocks < 0) return PKV_ERR_SHAPE;
+  return decode_common(cache, q, q_dtype, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, PKV_SPLIT_BALANCED, workspace,
+                       workspace_bytes, out, out_dtype, stream, false, 1, 0, false,
+                       prefix_blocks);
 }
 
 int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype,

@@ -162,6 +162,7 @@ struct DecodeArgs {
   const void* v_new;
   int ntok;            // query tokens per sequence (1: decode)
   int window;          // sliding window in tokens, 0 for none
+  int prefix_blocks;   // >= 0: shared-prefix split over that many common table entries
 };
 int launch_decode(const DecodeArgs& a, hipStream_t st);
 
@@ -171,7 +172,12 @@ int launch_decode(const DecodeArgs& a, hipStream_t st);
 // 16 took that step from 31.7 to 28.9 us; 24 was slower again.
 constexpr int kBalancedMinBlocks = 16;
 
-// Partial slots per (sequence, query head) row for a split setting.
+// Partial slots per (sequence, query head) row for a split setting.  A run of
+// n blocks meets at most ceil((n - 1) / 16) + 1 ranges of 16 or more blocks;
+// the balanced split cuts a sequence into one run, the shared-prefix split
+// into two (its group's P prefix blocks and its own max_blocks - P), so
+// ceil((max_blocks - 2) / 16) + 3 <= ceil(max_blocks / 16) + 3 slots cover
+// both.
 int decode_slots(int max_blocks, int partition_tokens);
 
 // Bytes of the split-context workspace and the offsets of its m, l and count

@@ -117,11 +117,23 @@ __device__ __forceinline__ u32x4 buffer_load16_kv(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
 
-// Query-token modes of the MFMA kernels (template parameter MQ): one token
-// per sequence; several tokens that fit one pass (k * G <= 16 columns); and
-// several passes, whose wavefronts for one (range, KV head) run side by side
-// and share the tiles through L2 (balanced split only).
-enum { kMqOne = 0, kMqPass = 1, kMqPasses = 2 };
+// Column modes of the MFMA kernels (template parameter MQ): one query token
+// per sequence (column n = head n of the group); several tokens that fit one
+// pass (k * G <= 16 columns: column n = head n % G of token n / G); several
+// passes, whose wavefronts for one (range, KV head) run side by side and share
+// the tiles through L2 (balanced split only); and several sequences whose
+// tables share the range's blocks (a common prefix: column n = head n % G of
+// sequence s + n / G), so a shared block is staged once for all of them.
+enum { kMqOne = 0, kMqPass = 1, kMqPasses = 2, kMqSeqs = 3 };
+
+// Columns of a shared-prefix segment (MQ == kMqSeqs): sequences s .. s +
+// nseq - 1 take columns [0, nseq * G); lcol is the context length of this
+// lane's column's sequence and lmin the shortest member's.
+struct SeqCols {
+  int nseq;
+  int lcol;
+  int lmin;
+};
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in an LDS tile of
 // 16-bit rows of D elements, chunks XOR-swizzled by the row index, so the
@@ -254,6 +266,8 @@ struct MfmaArgs {
   int ntok;           // query tokens per sequence (1: decode)
   int tok_per_pass;   // query tokens one wavefront takes (ntok * G columns split in passes)
   int window;         // sliding window in tokens, 0 for none
+  int prefix_blocks;  // shared-prefix split: table entries every sequence shares
+  int seqs_per_group; //                     sequences whose columns share a wavefront
   void* out;
   const uint8_t* kn;  // fused append (decode step): new K/V rows, or null
   const uint8_t* vn;
@@ -317,7 +331,8 @@ __device__ __forceinline__ void zero_rows(const MfmaArgs& a, int s, int g, int t
 template <int D, int KV, int OUT, int NST, int MQ>
 __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, int L, int b0,
                                              int b1, int slot, bool whole, int tok0,
-                                             uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_p) {
+                                             uint8_t* lds_k, uint8_t* lds_v, uint8_t* lds_p,
+                                             SeqCols sc = SeqCols{1, 0, 0}) {
   constexpr int kBits = KV == KV_BF16 ? 16 : KV == KV_FP4 ? 4 : 8;
   constexpr int kRowBytes = D * kBits / 8;       // bytes of one token's row in HBM
   constexpr int kTile = kBlock * kRowBytes;      // bytes of one (block, head) tile in HBM
@@ -331,19 +346,25 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   const int j = lane >> 4;   // token quad (rows 4j..4j+3 of S) / k-slice
   const int n = lane & 15;   // head column
   const int G = a.G, hq = a.hq, hkv = a.hkv, num_blocks = a.num_blocks;
-  // column n of S, P and O: query token ti (several per sequence only with
-  // MQ) and head h of the group
-  const int ti = MQ ? tok0 + n / G : 0;
-  const int h = g * G + (MQ ? n % G : n);
-  const bool has_head = MQ ? (n < G * a.tok_per_pass && ti < a.ntok) : n < G;
-  const size_t out_row = MQ ? ((size_t)s * a.ntok + ti) * hq + h : (size_t)s * hq + h;
-  // last key position + 1 this column may see (causal within the chunk), and
-  // with a window the first one (lo_col), and the lowest first position of
-  // all columns of this pass (lo_seg): V rows below it are zeroed in LDS
-  const int lim = MQ ? L - a.ntok + ti + 1 : L;
+  // column n of S, P and O: query token ti (several per sequence only in the
+  // token modes), sequence s_col (several only for a shared prefix) and head
+  // h of the group
+  constexpr bool kTok = MQ == kMqPass || MQ == kMqPasses;
+  constexpr bool kSeqs = MQ == kMqSeqs;
+  const int ti = kTok ? tok0 + n / G : 0;
+  const int s_col = kSeqs ? s + n / G : s;
+  const int h = g * G + (MQ != kMqOne ? n % G : n);
+  const bool has_head = kTok ? (n < G * a.tok_per_pass && ti < a.ntok)
+                             : kSeqs ? n < G * sc.nseq : n < G;
+  const size_t out_row = kTok ? ((size_t)s * a.ntok + ti) * hq + h : (size_t)s_col * hq + h;
+  // last key position + 1 this column may see (causal within the chunk, or
+  // its own sequence's length), and with a window the first one (lo_col), and
+  // the lowest first position of all columns of this pass (lo_seg): V rows
+  // below it are zeroed in LDS
+  const int lim = kTok ? L - a.ntok + ti + 1 : kSeqs ? sc.lcol : L;
   constexpr int kNoLo = -(1 << 30);
   const int lo_col = a.window > 0 ? lim - a.window : kNoLo;
-  const int lo_seg = a.window > 0 ? (MQ ? L - a.ntok + tok0 + 1 : L) - a.window : kNoLo;
+  const int lo_seg = a.window > 0 ? (kTok ? L - a.ntok + tok0 + 1 : L) - a.window : kNoLo;
 
   f32x4 acc[kNT];
 #pragma unroll
@@ -405,7 +426,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   constexpr int kRowChunks = D * 2 / 16;   // 16-byte chunks of one bf16 row
   int new_b = -1, new_r = 0;
   u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
-  if constexpr (KV == KV_BF16) {
+  if constexpr (KV == KV_BF16 && !kSeqs) {
     if (a.kn != nullptr && (L - 1) / kBlock >= b0 && (L - 1) / kBlock < b1) {
       new_b = (L - 1) / kBlock;
       new_r = (L - 1) % kBlock;
@@ -480,7 +501,9 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const rsrc_t rv = make_rsrc(vbase + off, in ? vrows * kRowBytes : 0);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        constexpr int kCpol = MQ == kMqPasses ? 0 : kCpolNT;
+        // tiles other wavefronts read again (later passes, other sequence
+        // groups of a shared prefix) stay cached
+        constexpr int kCpol = MQ == kMqPasses || MQ == kMqSeqs ? 0 : kCpolNT;
         kr[i] = buffer_load16_kv<kCpol>(rk, i * 1024 + lane * 16);
         vr[i] = buffer_load16_kv<kCpol>(rv, i * 1024 + lane * 16);
       }
@@ -569,7 +592,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           }
         }
       }
-      if constexpr (KV == KV_BF16) {
+      if constexpr (KV == KV_BF16 && !kSeqs) {
         if (b == new_b && lane < kRowChunks) {   // the appended token's row
           *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(new_r, lane)) = knew;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(new_r, lane)) = vnew;
@@ -650,8 +673,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       const int vmin = lo_col - b * kBlock;   // this column's first row in its window
       // one query token per sequence: every row of a block is in range for
       // every column unless the block is the last (or, with a window, the
-      // first) of the sequence, so the per-row selects are skipped
-      const bool full = !MQ && vcol >= kBlock && vmin <= 0;
+      // first) of the sequence, so the per-row selects are skipped; a shared
+      // prefix block likewise when it ends within the shortest member
+      const bool full = kSeqs ? cur_ok && (b + 1) * kBlock <= sc.lmin
+                              : !MQ && vcol >= kBlock && vmin <= 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (KV == KV_U8Z)
@@ -925,6 +950,172 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
         incl = wave_incl_scan(seq_blocks(Lreg, a.ntok, a.window)) + carry;
       }
       Lnext = readlane_i(Lreg, s - base);
+    }
+    if (Lnext == 0) break;
+  }
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Shared-prefix split.  The first P = prefix_blocks entries of every
+// sequence's table are the same physical blocks (a common prompt: page "LLM
+// 推理优化深度解析", section "意外的收获：prefix sharing"; page "大模型推理的KV
+// Cache管理…", section 二, copy_prefix).  The sequences are taken in groups of
+// S = seqs_per_group, whose S * G query heads fill the 16 MFMA columns, and
+// for each KV head the work is laid end to end: first every group's P prefix
+// blocks (each block staged once for the whole group), then every sequence's
+// remaining blocks.  Wavefront v takes the range [v per, v per + per) of that
+// order, per = max(ceil(total / V), min_blocks), as the balanced split does.
+// A sequence's pieces are the Kp pieces of its group's prefix (slots 0 ..
+// Kp - 1) followed by the pieces of its own blocks (slots Kp ...); the
+// wavefront holding a sequence's first suffix piece (or, without suffix, the
+// first prefix piece of its group) records the piece count for the combine.
+// With P = 0 this is the balanced split of one query token per sequence.
+// The 8- and 4-bit formats ask for three wavefronts per SIMD (E4M3 would
+// otherwise need one register more than three allow).
+template <int D, int KV, int OUT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    KV == KV_I8 || KV == KV_FP8 || KV == KV_FP4 ? 3 : kBalWaves))) void
+decode_mfma_prefix_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_p[KV == KV_U8Z ? 160 : 16];
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % a.hkv;
+  const int v = blockIdx.x / a.hkv;
+  const int V = gridDim.x / a.hkv;
+  const int B = a.num_seqs;
+  const int P = a.prefix_blocks;
+  const int S = a.seqs_per_group;
+  const int G = a.G;
+  const int NG = (B + S - 1) / S;
+
+  constexpr int kLenChunks = 4;
+  int lc[kLenChunks];
+#pragma unroll
+  for (int c = 0; c < kLenChunks; ++c) {
+    const int si = c * kWave + lane;
+    lc[c] = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+  }
+  auto len_chunk = [&](int base) -> int {
+    const int c = base / kWave;
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kLenChunks; ++i)
+      if (c == i) r = lc[i];
+    if (c >= kLenChunks) {
+      const int si = base + lane;
+      r = si < B ? clamp_len(a.lens[si], a.max_blocks) : 0;
+    }
+    return r;
+  };
+  // blocks of a sequence of length L after the shared prefix
+  auto suffix_blocks = [&](int L) { return max((L + kBlock - 1) / kBlock - P, 0); };
+
+  // pass 1: suffix blocks in all; zero rows of empty sequences
+  int total = 0, incl0 = 0;
+  for (int base = 0; base < B; base += kWave) {
+    const int si = base + lane;
+    const int Ll = len_chunk(base);
+    const int inc = wave_incl_scan(suffix_blocks(Ll));
+    if (base == 0) incl0 = inc;
+    total += readlane_i(inc, kWave - 1);
+    if (v == 0) {
+      uint64_t empty = __ballot(si < B && Ll == 0);
+      while (empty) {
+        const int e = __ffsll((unsigned long long)empty) - 1;
+        empty &= empty - 1;
+        zero_rows<D, OUT>(a, base + e, g, 0);
+      }
+    }
+  }
+  const int Tp = NG * P;
+  total = __builtin_amdgcn_readfirstlane(total) + Tp;
+  const int per = max((total + V - 1) / V, a.min_blocks);
+  const int x0 = v * per;
+  if (x0 >= total) return;
+  const int x1 = min(x0 + per, total);
+  // prefix pieces of group q: the wavefronts whose ranges meet [q P, q P + P)
+  auto prefix_pieces = [&](int q) { return P > 0 ? ((q + 1) * P - 1) / per - (q * P) / per + 1 : 0; };
+
+  // ---- the shared prefix, one sequence group at a time
+  int x = x0;
+  while (x < x1 && x < Tp) {
+    const int q = x / P;
+    const int e = min(x1, (q + 1) * P);
+    const int Kp = prefix_pieces(q);
+    const int slot = v - (q * P) / per;
+    const int s0 = q * S;
+    const int nseq = min(S, B - s0);
+    const int n = lane & 15;
+    const bool col = n < nseq * G;
+    const int scol = s0 + (col ? n / G : 0);
+    const int lcol = col ? clamp_len(a.lens[scol], a.max_blocks) : 0;
+    const int lmax = __builtin_amdgcn_readfirstlane(wave_max_i(lcol));
+    const int lmin = __builtin_amdgcn_readfirstlane(wave_min_i(col ? lcol : (1 << 30)));
+    const bool has_suffix = suffix_blocks(lcol) > 0;
+    if (g == 0 && slot == 0 && lane < 16 && col && n % G == 0 && !has_suffix)
+      a.ws_count[scol] = Kp;
+    mfma_segment<D, KV, OUT, kBalStages, kMqSeqs>(a, s0, g, lmax, x - q * P, e - q * P, slot,
+                                                  Kp == 1 && !has_suffix, 0, lds_k, lds_v,
+                                                  lds_p, SeqCols{nseq, lcol, lmin});
+    x = e;
+  }
+  if (x >= x1) return;
+
+  // ---- every sequence's own blocks: positions y = x - Tp of the suffix order
+  const int y0 = x - Tp, y1 = x1 - Tp;
+  int base = 0, carry = 0, s = -1, R0 = 0, Lreg = 0, incl = 0;
+  for (; base < B; base += kWave) {
+    Lreg = len_chunk(base);
+    const int nb = suffix_blocks(Lreg);
+    incl = (base == 0 ? incl0 : wave_incl_scan(nb)) + carry;
+    const uint64_t hit = __ballot(nb > 0 && incl - nb <= y0 && y0 < incl);
+    if (hit) {
+      const int hl = __ffsll((unsigned long long)hit) - 1;
+      s = base + hl;
+      R0 = readlane_i(incl - nb, hl);
+      break;
+    }
+    carry = readlane_i(incl, kWave - 1);
+  }
+  if (s < 0) return;   // unreachable while y0 < total suffix blocks
+
+  int y = y0;
+  while (true) {
+    const int L = readlane_i(Lreg, s - base);
+    const int R1 = R0 + suffix_blocks(L);
+    const int e = min(y1, R1);
+    const int vf = (Tp + R0) / per;
+    const int Ks = (Tp + R1 - 1) / per - vf + 1;
+    const int Kp = prefix_pieces(s / S);
+    const int slot = Kp + v - vf;
+    if (g == 0 && slot == Kp && lane == 0) a.ws_count[s] = Kp + Ks;
+    mfma_segment<D, KV, OUT, kBalStages, kMqOne>(a, s, g, L, P + y - R0, P + e - R0, slot,
+                                                 Kp + Ks == 1, 0, lds_k, lds_v, lds_p);
+    if (e >= y1) break;
+    y = e;
+    R0 = R1;
+    int Lnext = 0;
+    while (Lnext == 0 && s + 1 < B) {
+      ++s;
+      if (s - base >= kWave) {
+        carry = readlane_i(incl, kWave - 1);
+        base += kWave;
+        Lreg = len_chunk(base);
+        incl = wave_incl_scan(suffix_blocks(Lreg)) + carry;
+      }
+      Lnext = suffix_blocks(readlane_i(Lreg, s - base)) > 0 ? 1 : 0;
     }
     if (Lnext == 0) break;
   }
@@ -1277,6 +1468,8 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
     m.ntok = a.ntok;
     m.tok_per_pass = pl.tok_per_pass;
     m.window = a.window;
+    m.prefix_blocks = a.prefix_blocks > 0 ? a.prefix_blocks : 0;
+    m.seqs_per_group = G <= 16 ? 16 / G : 1;
     m.out = a.out;
     m.kn = q8 ? nullptr : (const uint8_t*)a.k_new;
     m.vn = q8 ? nullptr : (const uint8_t*)a.v_new;
@@ -1309,6 +1502,15 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
     const int mq = a.ntok <= 1 ? kMqOne : (pl.balanced && pl.passes > 1 ? kMqPasses : kMqPass);
     auto by_kv = [&](auto kv) {
       constexpr int KV = decltype(kv)::value;
+      if (a.prefix_blocks >= 0) {
+        // shared-prefix split: one generation of wavefronts, as the balanced split
+        auto kernel = decode_mfma_prefix_kernel<D, KV, OUT>;
+        const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(kernel));
+        if (per_cu <= 0) return (int)PKV_ERR_HIP;
+        const int64_t waves = (int64_t)pl.cus * per_cu;
+        ranges = (waves + hkv - 1) / hkv;
+        return launch(kernel, dim3((unsigned)(ranges * hkv)), block, st, m);
+      }
       if (mq == kMqOne)
         return go(decode_mfma_kernel<D, KV, OUT, kMqOne>,
                   decode_mfma_balanced_kernel<D, KV, OUT, kMqOne>);
@@ -1340,7 +1542,8 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
                   (const int32_t*)(pl.balanced ? pl.ws_count : nullptr), a.lens, a.max_blocks,
                   a.ntok * hq, pl.part_blocks, pl.kstride, a.ntok, a.window, a.out);
   };
-  const int64_t pieces = pl.balanced ? 1 + ranges / a.num_seqs : 8;
+  // (a shared prefix adds its group's pieces: read 8)
+  const int64_t pieces = a.prefix_blocks > 0 ? 8 : pl.balanced ? 1 + ranges / a.num_seqs : 8;
   if (pieces <= 2) return combine(reduce_kernel<D, OUT, 2>);
   if (pieces <= 4) return combine(reduce_kernel<D, OUT, 4>);
   return combine(reduce_kernel<D, OUT, 8>);
@@ -1380,7 +1583,7 @@ int device_cu_count() {
 
 int decode_slots(int max_blocks, int partition_tokens) {
   if (partition_tokens == PKV_SPLIT_BALANCED)
-    return (max_blocks + kBalancedMinBlocks - 1) / kBalancedMinBlocks + 1;
+    return (max_blocks + kBalancedMinBlocks - 1) / kBalancedMinBlocks + 3;
   const int part_blocks = partition_tokens > 0 ? partition_tokens / kBlock : max_blocks;
   return (max_blocks + part_blocks - 1) / part_blocks;
 }

@@ -18,6 +18,8 @@ a long context; shared-prefix and quantized KV):
   5 quant_prefix     B=128, 2048-token prefix shared by every table (the same
                      128 physical blocks) + U{0..1024} private tokens; bf16
                      source pool that the caller quantizes to INT8 or FP8
+                     (tests shrink it; a sequence shorter than the prefix
+                     still has the prefix ids as its first table entries)
 
 Recipe: ``numpy.random.default_rng(seed)`` (seed = workload number unless
 given); draw order lens -> block permutation -> pool K -> pool V -> new K ->
@@ -159,12 +161,14 @@ def make(cfg: int, seed: Optional[int] = None, quant: Optional[str] = None, **ov
         hi_len = spec["prefix"] + spec["suffix_hi"]
     lens = lens.astype(np.int32)
     max_blocks = max(1, -(-hi_len // bs))
+    if cfg == 5:   # every table holds the shared prefix, however short its sequence
+        max_blocks = max(max_blocks, spec["prefix"] // bs)
     nblk = [-(-int(L) // bs) for L in lens]
 
     # -- pool size and block permutation
     if cfg == 5:
         n_prefix = spec["prefix"] // bs
-        needed = n_prefix + sum(n - n_prefix for n in nblk)
+        needed = n_prefix + sum(max(n - n_prefix, 0) for n in nblk)
     else:
         needed = sum(nblk)
     NB = spec["pool"] if spec.get("pool") else max(1, math.ceil(1.1 * needed))
@@ -177,10 +181,10 @@ def make(cfg: int, seed: Optional[int] = None, quant: Optional[str] = None, **ov
         cur = n_prefix
         for s in range(B):
             tables[s, :n_prefix] = prefix_ids
-            k = nblk[s] - n_prefix
-            tables[s, n_prefix:nblk[s]] = perm[cur:cur + k]
+            k = max(nblk[s] - n_prefix, 0)
+            tables[s, n_prefix:n_prefix + k] = perm[cur:cur + k]
             cur += k
-            used[s, :nblk[s]] = True
+            used[s, :max(nblk[s], n_prefix)] = True
     else:
         cur = 0
         for s in range(B):

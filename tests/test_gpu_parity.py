@@ -1308,3 +1308,96 @@ def test_decode_step_u8z_equals_append_then_attention(part):
                  (qa.v_scale, qb.v_scale), (qa.k_zero, qb.k_zero), (qa.v_zero, qb.v_zero)):
         assert torch.equal(x, y)
     assert torch.equal(fused, sep)
+
+
+# ------------------------------------------------------------- shared prefix
+
+PREFIX_CASES = [
+    # (overrides of the shared-prefix workload, quantized format)
+    (dict(B=10, prefix=256, suffix_hi=300), None),
+    (dict(B=10, prefix=256, suffix_hi=300), "i8"),
+    (dict(B=10, prefix=256, suffix_hi=300), "fp8"),
+    (dict(B=10, prefix=256, suffix_hi=300), "u8z"),
+    (dict(B=10, prefix=256, suffix_hi=300), "fp4"),
+    (dict(B=7, prefix=512, suffix_hi=100), None),                       # B not a multiple of 4
+    (dict(B=9, prefix=256, suffix_hi=300, Hq=64, Hkv=8), None),         # G = 8: 2 per group
+    (dict(B=11, prefix=256, suffix_hi=300, Hq=6, Hkv=2), "i8"),         # G = 3: 5 per group
+    (dict(B=5, prefix=256, suffix_hi=200, Hq=16, Hkv=1), None),         # G = 16: 1 per group
+    (dict(B=9, prefix=256, suffix_hi=300, D=64), "fp8"),                # D = 64
+    (dict(B=8, prefix=512, lens=[512, 0, 100, 513, 700, 16, 1, 530]), None),   # short, empty
+    (dict(B=8, prefix=512, lens=[512, 0, 100, 513, 700, 16, 1, 530]), "u8z"),
+    (dict(B=6, prefix=256, suffix_hi=0), "i8"),                         # no suffix at all
+    (dict(B=150, prefix=64, suffix_hi=100), None),                      # ranges span many
+    (dict(B=300, prefix=32, suffix_hi=60), "fp4"),                      # beyond 256 sequences
+]
+
+
+def _prefix_inputs(wl, quant, d):
+    """Device cache (quantized on the GPU if asked) and the oracle's pool."""
+    cache = _dev_cache(d, wl)
+    k, v, ks, vs, kz, vz = wl.k_pool, wl.v_pool, None, None, None, None
+    if quant:
+        NB, Hkv, bs, D = d["k_pool"].shape
+        qc = _qcache(quant, NB, Hkv, bs, D, blocks="kv" in d)
+        pkv.quantize(cache, qc)
+        cache = qc
+        k, ks, kz = _oracle_quantize(wl.k_pool, wl.kv_dtype, quant)
+        v, vs, vz = _oracle_quantize(wl.v_pool, wl.kv_dtype, quant)
+    return cache, (k, v, ks, vs, kz, vz)
+
+
+@pytest.mark.parametrize("over,quant", PREFIX_CASES)
+def test_attention_prefix(over, quant):
+    """pkv_attention_prefix against the oracle's plain decode (the definition
+    does not change with the split), with prefix_blocks = the shared prefix,
+    half of it, and 0."""
+    wl = W.make(5, quant=quant, **over)
+    P = over["prefix"] // 16
+    _say(f"attention prefix: {over} quant={quant} P={P}")
+    d = W.to_device(wl, layout="blocks")
+    cache, (k, v, ks, vs, kz, vz) = _prefix_inputs(wl, quant, d)
+    ref = oracle.decode(wl.q, wl.q_dtype, k, v, quant or wl.kv_dtype, wl.tables, wl.lens,
+                        wl.scale, k_scale=ks, v_scale=vs, k_zero=kz, v_zero=vz)
+    for pb in (P, P // 2, 0):
+        out = pkv.attention_prefix(cache, d["q"], d["tables"], d["lens"], float(wl.scale), pb,
+                                   out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _cmp(_out_np(out), ref, TOL[quant or wl.kv_dtype], f"prefix P={pb} {over} {quant}")
+
+
+def test_attention_prefix_equal_queries_give_equal_rows():
+    """Sequences with the same query and no private tokens (length = the
+    prefix) see the same keys: their rows agree to rounding, and equal the
+    oracle's."""
+    wl = W.make(5, B=9, prefix=512, suffix_hi=0)
+    wl = dataclasses.replace(wl, q=np.repeat(wl.q[:1], wl.B, axis=0))
+    d = W.to_device(wl, layout="blocks")
+    out = _out_np(pkv.attention_prefix(_dev_cache(d, wl), d["q"], d["tables"], d["lens"],
+                                       float(wl.scale), 32, out_dtype=torch.float32))
+    ref = oracle.decode(wl.q, wl.q_dtype, wl.k_pool, wl.v_pool, wl.kv_dtype, wl.tables, wl.lens,
+                        wl.scale)
+    _cmp(out, ref, TOL["bf16"], "equal queries")
+    assert np.max(np.abs(out - out[:1])) <= 1e-5
+
+
+@pytest.mark.parametrize("quant", [None, "i8", "fp8", "u8z", "fp4"])
+def test_attention_prefix_full_size(quant):
+    """The shared-prefix workload at full size (128 sequences, 2048-token
+    prefix), every row against the oracle; bf16 output as the rounding of
+    the binary32 one."""
+    wl = W.make(5, quant=quant)
+    _say(f"attention prefix full: quant={quant}")
+    d = W.to_device(wl, layout="blocks")
+    cache, (k, v, ks, vs, kz, vz) = _prefix_inputs(wl, quant, d)
+    run = lambda od: pkv.attention_prefix(cache, d["q"], d["tables"], d["lens"],
+                                          float(wl.scale), 128, out_dtype=od)
+    out = run(torch.float32)
+    outb = run(torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.decode(wl.q, wl.q_dtype, k, v, quant or wl.kv_dtype, wl.tables, wl.lens,
+                        wl.scale, k_scale=ks, v_scale=vs, k_zero=kz, v_zero=vz)
+    tol = TOL[quant or wl.kv_dtype]
+    err = _cmp(_out_np(out), ref, tol, f"prefix full {quant}")
+    _record(f"attention prefix/{wl.name}/{quant or wl.kv_dtype}/blocks layout/prefix 128", err,
+            tol)
+    _check_rounded(_out_np(outb), _out_np(out), f"prefix full {quant} bf16 out")

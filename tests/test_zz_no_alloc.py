@@ -66,7 +66,7 @@ def _ref(wl, u8z=False):
 
 @pytest.mark.parametrize("part", [-1, 256])
 def test_noalloc_step_equals_workspace_step_twice(part):
-    """The Llama-3-8B step (18.1 MB of partials with the balanced split), then
+    """The Llama-3-8B step (20.2 MB of partials with the balanced split), then
     a smaller step on the same scratch array."""
     for i, wl in enumerate((W.make(2), W.make(2, B=9, lo=1, hi=700, pool=600))):
         _say(f"noalloc call {i}: {wl.name} B={wl.B} part={part}")
