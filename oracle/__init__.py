@@ -101,6 +101,8 @@ def _load():
         lib.orc_quantize_asym.argtypes = [P, I, P, P, P, I, I, I, I, P, I]
         lib.orc_cache_write_quant.restype = I
         lib.orc_cache_write_quant.argtypes = [P, P, P, P, P, P, I, I, I, P, P, I, P, I]
+        lib.orc_cache_write_sym.restype = I
+        lib.orc_cache_write_sym.argtypes = [P, P, P, P, I, I, I, I, P, P, I, P, I]
         lib.orc_max_threads.restype = I
         lib.orc_max_threads.argtypes = []
         _lib = lib
@@ -413,6 +415,29 @@ def quantize_asym(src, src_dtype, block_ids=None):
     if rc != 0:
         raise ValueError("oracle quantize_asym: unsupported source dtype or allocation failure")
     return codes, scales, zeros
+
+
+def cache_write_sym(k_cache, v_cache, k_scale, v_scale, dtype, k_new, v_new, src_dtype,
+                    slot_mapping):
+    """In-place quantized append into a pool with one symmetric scale per
+    (block, KV head) tile (``i8``, ``fp8``, ``fp4``): a new row that needs a
+    larger scale grows its tile's scale and re-expresses the earlier rows; a
+    row at offset 0 starts a fresh tile (negative slot: skipped).  Pools are
+    [NB][Hkv][16][D] codes ([NB][Hkv][16][D/2] bytes for fp4), scales [NB][Hkv]."""
+    for a in (k_cache, v_cache):
+        assert a.dtype == NP_STORAGE[dtype] and a.flags.c_contiguous
+    for a in (k_scale, v_scale):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    NB, Hkv, bs, Ds = k_cache.shape
+    D = Ds * 2 if dtype == "fp4" else Ds
+    kn = _c(k_new, NP_STORAGE[src_dtype])
+    vn = _c(v_new, NP_STORAGE[src_dtype])
+    sm = _c(slot_mapping, np.int32)
+    rc = _load().orc_cache_write_sym(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                     DTYPES[dtype], Hkv, bs, D, _ptr(kn), _ptr(vn),
+                                     DTYPES[src_dtype], _ptr(sm), sm.shape[0])
+    if rc != 0:
+        raise ValueError("oracle cache_write_sym: unsupported dtype")
 
 
 def cache_write_quant(k_cache, v_cache, k_scale, v_scale, k_zero, v_zero, k_new, v_new,

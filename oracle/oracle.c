@@ -722,6 +722,112 @@ int orc_cache_write_quant(uint8_t* k_cache, uint8_t* v_cache, float* k_scale, fl
 }
 
 /* ------------------------------------------------------------------------ */
+/* Quantized append into a pool with one symmetric scale per (block, KV head)
+ * tile (INT8, E4M3, E2M1: the quantizer above).  Each decode step appends
+ * one token's K and V ([KVC] "KV Cache 的本质"), but the pages quantize whole
+ * token groups and say nothing of a row joining a tile that already has a
+ * scale.  The reading taken: the tile's scale always covers the rows written
+ * so far, so a row that needs a larger scale grows it and the earlier rows
+ * are re-expressed in the new scale; a row at offset 0 starts a fresh tile
+ * (no earlier row of its sequence lives there, so the tile's old contents are
+ * ignored).  Per token i with slot = slot_mapping[i] >= 0 (block b, offset
+ * r), KV head g, K and V separately, every step a binary32 operation with
+ * round-to-nearest-even:
+ *   a = max |x| over the new row,  c = a / Q  (Q = 127, 448 or 6)
+ *   r == 0:      s = c
+ *   r > 0:       s_old = the tile's scale; if c > s_old the scale grows to
+ *                s = c and each earlier row's code becomes
+ *                encode(decode(code) * s_old / s) (the product rounded to
+ *                binary32, then divided); otherwise s = s_old
+ *   new row:     code = encode(x / s); s == 0 gives zero codes
+ * where encode is clamp(rint(.), -127, 127) for INT8 and the nearest code,
+ * ties to even, saturating, for E4M3 and E2M1.  Rows after r are untouched.
+ * Filling a tile in order ends with the scale that quantizing it whole gives
+ * (the maximum of the rows' a / Q).                                         */
+static uint8_t orc_sym_encode(int dtype, float v) {
+  if (dtype == ORC_I8) {
+    float r = rintf(v);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (uint8_t)(int8_t)r;
+  }
+  return dtype == ORC_FP8 ? orc_e4m3_from_float(v) : orc_e2m1_from_float(v);
+}
+
+static float orc_sym_decode(int dtype, uint8_t code) {
+  if (dtype == ORC_I8) return (float)(int8_t)code;
+  return (float)(dtype == ORC_FP8 ? orc_e4m3_to_double(code) : orc_e2m1_to_double(code));
+}
+
+/* code at element index idx of a pool, and its store (E2M1: two per byte,
+ * element 2i in the low nibble of byte i)                                   */
+static uint8_t orc_sym_get(const uint8_t* pool, int dtype, size_t idx) {
+  if (dtype != ORC_FP4) return pool[idx];
+  return (uint8_t)((idx & 1) ? pool[idx / 2] >> 4 : pool[idx / 2] & 15);
+}
+
+static void orc_sym_put(uint8_t* pool, int dtype, size_t idx, uint8_t c) {
+  if (dtype != ORC_FP4) {
+    pool[idx] = c;
+  } else if (idx & 1) {
+    pool[idx / 2] = (uint8_t)((pool[idx / 2] & 0x0F) | (c << 4));
+  } else {
+    pool[idx / 2] = (uint8_t)((pool[idx / 2] & 0xF0) | c);
+  }
+}
+
+static void orc_sym_append_row(uint8_t* pool, float* scales, int dtype, int Hkv, int bs, int D,
+                               size_t b, size_t g, size_t r, const float* x) {
+  const float Q = dtype == ORC_I8 ? 127.0f : dtype == ORC_FP8 ? 448.0f : 6.0f;
+  float a = 0.0f, c, s;
+  size_t tile = orc_pool_offset(b, g, 0, Hkv, bs, D);
+  for (int d = 0; d < D; ++d)
+    if (fabsf(x[d]) > a) a = fabsf(x[d]);
+  c = a / Q;
+  if (r == 0) {
+    s = c;
+  } else {
+    float s_old = scales[b * Hkv + g];
+    s = s_old;
+    if (c > s_old) {
+      s = c;
+      for (size_t e = 0; e < r * (size_t)D; ++e) {
+        float v = orc_sym_decode(dtype, orc_sym_get(pool, dtype, tile + e)) * s_old;
+        orc_sym_put(pool, dtype, tile + e, orc_sym_encode(dtype, v / s));
+      }
+    }
+  }
+  scales[b * Hkv + g] = s;
+  for (int d = 0; d < D; ++d)
+    orc_sym_put(pool, dtype, tile + r * (size_t)D + (size_t)d,
+                s == 0.0f ? 0 : orc_sym_encode(dtype, x[d] / s));
+}
+
+int orc_cache_write_sym(uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
+                        int dtype, int Hkv, int bs, int D, const void* k_new, const void* v_new,
+                        int src_dtype, const int32_t* slot_mapping, int n) {
+  float* row;
+  if (dtype != ORC_I8 && dtype != ORC_FP8 && dtype != ORC_FP4) return -1;
+  if (src_dtype != ORC_F32 && src_dtype != ORC_BF16) return -1;
+  row = (float*)malloc(sizeof(float) * (size_t)D);
+  if (!row) return -1;
+  for (int i = 0; i < n; ++i) {
+    int32_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    for (int g = 0; g < Hkv; ++g) {
+      size_t b = (size_t)(slot / bs), r = (size_t)(slot % bs);
+      size_t src = ((size_t)i * Hkv + g) * (size_t)D;
+      for (int d = 0; d < D; ++d) row[d] = (float)orc_load_elem(k_new, src + d, src_dtype, 1.0, 0.0);
+      orc_sym_append_row(k_cache, k_scale, dtype, Hkv, bs, D, b, (size_t)g, r, row);
+      for (int d = 0; d < D; ++d) row[d] = (float)orc_load_elem(v_new, src + d, src_dtype, 1.0, 0.0);
+      orc_sym_append_row(v_cache, v_scale, dtype, Hkv, bs, D, b, (size_t)g, r, row);
+    }
+  }
+  free(row);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Sliding-window attention ([WIKI] "三个直接推论": keeping only a window of
  * the most recent tokens is one of the ways to cut KV bytes).  As in
  * orc_decode_multi, query token i of sequence s sits at position
