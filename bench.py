@@ -77,10 +77,12 @@ def algorithmic_bytes(wl, ntok=1, window=0):
     if wl.write and ntok == 1 and window == 0:
         # new K/V rows read (in the pool's type, or q's for a quantizing
         # append) and written into the pool, with their row parameters
-        e_new = e_q if wl.quant == "u8z" else e_kv
+        e_new = e_q if wl.quant else e_kv
         write = int(wl.B * wl.Hkv * wl.D * 2 * (e_new + e_kv))
         if wl.quant == "u8z":
             write += wl.B * wl.Hkv * 2 * 5
+        elif wl.quant:          # the tile's scale read and written
+            write += wl.B * wl.Hkv * 2 * 8
     return dict(attention=attention, kv=kv, write=write, step=attention + write,
                 q_out_tables_lens=q_out_tables_lens)
 
@@ -398,6 +400,9 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (>0: attention over each query's most recent "
                          "window only; no append)")
+    ap.add_argument("--append", action="store_true",
+                    help="workload 5: a decode step whose new tokens are appended into the "
+                         "quantized pool before attention")
     ap.add_argument("--prefix-blocks", type=int, default=-1,
                     help="shared-prefix attention over that many common table entries "
                          "(-1: the workload's shared prefix for workload 5, none otherwise; "
@@ -423,7 +428,10 @@ def main():
 
     torch.cuda.set_device(0)
     if args.workload == 5:
-        wl = W.make(5, quant=args.quant or "i8")
+        # --append: a decode step, each sequence's new token appended into its
+        # own blocks (quantized) before attention
+        extra = dict(write=True, suffix_lo=1) if args.append else {}
+        wl = W.make(5, quant=args.quant or "i8", **extra)
     else:
         if args.quant not in (None, "u8z"):
             sys.exit("--quant for workloads 1-4 must be u8z (only that format takes a "
@@ -440,7 +448,7 @@ def main():
     n_rep = args.replicas or max(2, min(8, math.ceil(1.3e9 / pool_bytes) + 1))
     prefix_blocks = args.prefix_blocks
     if prefix_blocks < 0:
-        prefix_blocks = W.SPECS[5]["prefix"] // 16 if args.workload == 5 else 0
+        prefix_blocks = W.SPECS[5]["prefix"] // 16 if args.workload == 5 and not wl.write else 0
     if prefix_blocks > 0 and (wl.write or args.tokens > 1 or args.window > 0):
         sys.exit("--prefix-blocks applies to attention over the shared-prefix workload (5)")
     if prefix_blocks > 0:
@@ -527,7 +535,7 @@ def main():
                            if args.window > 0 else
                            (f"paged attention of {args.tokens} query tokens per sequence + "
                             "partition combine") if args.tokens > 1 else
-                           ("decode step: quantizing append of position L-1 (own launch) + "
+                           ("decode step: quantized append of position L-1 (own launch) + "
                             "paged attention + partition combine") if wl.write and wl.quant else
                            ("decode step: slot of position L-1 + cache write + paged attention "
                             "(one launch) + partition combine") if wl.write else

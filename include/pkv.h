@@ -161,28 +161,41 @@ int pkv_slot_mapping_tokens(const int32_t* block_tables, int32_t max_blocks_per_
  * KV head g, for every g.  Bit-exact copy.
  *   k, v: device [n][num_kv_heads][head_dim] of cache->kv_dtype
  *   slot_mapping: device int32 [n]; negative = skip; slots must be distinct.
- * kv_dtype must be PKV_F32 or PKV_BF16 (for PKV_U8_ZP use
- * pkv_cache_write_quant; appending into a PKV_I8 / PKV_FP8_E4M3 pool is
- * PKV_ERR_UNSUPPORTED, since one new row would change its block's scale:
- * quantize whole blocks with pkv_quantize instead). */
+ * kv_dtype must be PKV_F32 or PKV_BF16 (quantized pools take
+ * pkv_cache_write_quant, which quantizes the new rows). */
 int pkv_cache_write(const pkv_cache_t* cache, const void* k, const void* v,
                     const int32_t* slot_mapping, int32_t n, void* stream);
 
 /* Quantized append ([KVC] "KV Cache 的本质": each step appends the new token's
- * K and V; [MGMT] section 四, KVQuantizationCache.quantize_key with per-channel
- * parameters, restored as (code - zero) * scale): for i < n with slot =
- * slot_mapping[i] in range, each KV head's row k[i][g][:] (and v[i][g][:]) is
- * quantized on its own over its range widened to hold 0,
- *   lo = min(min x, 0), hi = max(max x, 0), scale = (hi - lo) / 255,
- *   zero = clamp(rint(-lo / scale), 0, 255),
- *   code = clamp(rint(x / scale) + zero, 0, 255),
- * every step a binary32 operation rounding to nearest even, so every value
- * restores within half a step; an all-zero row is stored as scale 0, zero 0,
- * codes 0.  The codes go to row
- * slot % 16 of block slot / 16 and the scale and zero point to the same row
- * of k_scale / k_zero (v_scale / v_zero); no other row changes.  Bit-exact
- * with pkv_quantize of the same values.
- *   cache: kv_dtype PKV_U8_ZP
+ * K and V) into a quantized pool.  For i < n with slot = slot_mapping[i] in
+ * range, each KV head's row k[i][g][:] (and v[i][g][:]) goes to row
+ * r = slot % 16 of block slot / 16:
+ *   PKV_U8_ZP ([MGMT] section 四, KVQuantizationCache with per-channel
+ *     parameters, restored as (code - zero) * scale): the row is quantized on
+ *     its own over its range widened to hold 0,
+ *       lo = min(min x, 0), hi = max(max x, 0), scale = (hi - lo) / 255,
+ *       zero = clamp(rint(-lo / scale), 0, 255),
+ *       code = clamp(rint(x / scale) + zero, 0, 255),
+ *     so every value restores within half a step; an all-zero row is stored
+ *     as scale 0, zero 0, codes 0.  Its scale and zero point go to the same
+ *     row of k_scale / k_zero (v_scale / v_zero); no other row changes.
+ *     Bit-exact with pkv_quantize of the same values.
+ *   PKV_I8, PKV_FP8_E4M3, PKV_FP4_E2M1 ([MGMT] section 四, codes restored as
+ *     code * scale with one scale per (block, KV head) tile): the tile's
+ *     scale covers the rows written so far.  With a = max |x| of the new row
+ *     and c = a / Q (Q = 127, 448, 6): at r == 0 the tile starts afresh,
+ *     scale = c (its old contents are ignored); at r > 0, if c exceeds the
+ *     tile's scale s_old the scale grows to c and every earlier row's code
+ *     becomes encode(decode(code) * s_old / c), otherwise it stays; the new
+ *     row's codes are encode(x / scale) (zero codes when the scale is 0).
+ *     encode is clamp(rint(.), -127, 127) for INT8 and the nearest code
+ *     (ties to even, saturating) for E4M3 and E2M1.  Rows after r are left
+ *     alone.  Filling a tile in position order ends with the scale
+ *     pkv_quantize gives the whole tile.  The slots of one call must lie in
+ *     distinct blocks (rows of one tile share its scale): append several
+ *     rows of one block in successive calls, in position order.
+ * Every step is a binary32 operation rounding to nearest even.
+ *   cache: kv_dtype PKV_U8_ZP, PKV_I8, PKV_FP8_E4M3 or PKV_FP4_E2M1
  *   k, v: device [n][num_kv_heads][head_dim] of src_dtype (PKV_F32 or PKV_BF16)
  *   slot_mapping: device int32 [n]; negative = skip; slots must be distinct. */
 int pkv_cache_write_quant(const pkv_cache_t* cache, const void* k, const void* v,
@@ -257,11 +270,12 @@ int pkv_attention_decode(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
  * pkv_attention_decode, and leaves the pool in the same state.
  *   k, v: device [num_seqs][num_kv_heads][head_dim] of cache->kv_dtype (the
  *     new token of each sequence; ignored for sequences with length 0)
- * kv_dtype must be PKV_F32, PKV_BF16 or PKV_U8_ZP; for PKV_U8_ZP, k and v are
- * of q_dtype and are quantized as pkv_cache_write_quant does, by a launch of
- * its own before the attention.  Other arguments as for
+ * For quantized pools (PKV_U8_ZP, PKV_I8, PKV_FP8_E4M3, PKV_FP4_E2M1), k and
+ * v are of q_dtype and are quantized as pkv_cache_write_quant does, by a
+ * launch of its own before the attention.  Other arguments as for
  * pkv_attention_decode.  Tables must not map the new token's slot of two
- * sequences to the same physical row. */
+ * sequences to the same physical row (for the per-tile formats, to the same
+ * block). */
 int pkv_decode_step(const pkv_cache_t* cache, const void* q, int32_t q_dtype, const void* k,
                     const void* v, const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,

@@ -20,6 +20,7 @@ PKV_OK = 0
 SPLIT_BALANCED = -1     # partition_tokens value: balanced split (PKV_SPLIT_BALANCED)
 DTYPE_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "u8z": 4, "fp4": 5}
 BLOCK_SIZE = 16
+QUANTIZED = ("i8", "fp8", "u8z", "fp4")
 
 _lib = None
 
@@ -265,9 +266,12 @@ def cache_write(cache: PagedCache, k, v, slot_mapping, stream=None):
 
 
 def cache_write_quant(cache: PagedCache, k, v, slot_mapping, stream=None):
-    """Quantized append into a ``u8z`` pool: every new (token, head) row of k
-    and v (float32 or bfloat16 [n][Hkv][D]) is quantized on its own and stored
-    with its scale and zero point at its slot."""
+    """Quantized append into a quantized pool: the new (token, head) rows of k
+    and v (float32 or bfloat16 [n][Hkv][D]) are quantized and stored at their
+    slots.  ``u8z``: each row gets its own scale and zero point.  ``i8`` /
+    ``fp8`` / ``fp4``: the row joins its tile, whose scale grows (and whose
+    earlier rows are re-encoded) when the row needs it; the slots of one call
+    must lie in distinct blocks."""
     torch = _torch()
     sd = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(k.dtype)
     if sd is None:
@@ -347,8 +351,8 @@ def _decode_call(cache: PagedCache, q, block_tables, context_lens, scale: float,
     if context_lens.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("q, block_tables and context_lens disagree on the batch size")
     if append is not None:
-        # new rows for a u8z pool come in q's dtype and are quantized on append
-        sd = q.dtype if cache.kv_dtype == "u8z" else _storage_dtype(cache.kv_dtype)
+        # new rows for a quantized pool come in q's dtype and are quantized on append
+        sd = q.dtype if cache.kv_dtype in QUANTIZED else _storage_dtype(cache.kv_dtype)
         k_new, v_new = append
         _need(k_new, "k_new", sd, 3)
         _need(v_new, "v_new", sd, 3)

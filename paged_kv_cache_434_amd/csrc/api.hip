@@ -141,7 +141,7 @@ int pkv_cache_write_quant(const pkv_cache_t* cache, const void* k, const void* v
                           void* stream) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
-  if (cache->kv_dtype != PKV_U8_ZP || (src_dtype != PKV_F32 && src_dtype != PKV_BF16))
+  if (!is_quantized(cache->kv_dtype) || (src_dtype != PKV_F32 && src_dtype != PKV_BF16))
     return PKV_ERR_DTYPE;
   if (n < 0) return PKV_ERR_SHAPE;
   if (n == 0) return PKV_OK;
@@ -201,7 +201,6 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
   }
   if (num_seqs == 0) return PKV_OK;
   if (append) {
-    if (kv != PKV_F32 && kv != PKV_BF16 && kv != PKV_U8_ZP) return PKV_ERR_UNSUPPORTED;
     if (!k_new || !v_new) return PKV_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_UNSUPPORTED;
   }
@@ -224,9 +223,9 @@ static int decode_common(const pkv_cache_t* cache, const void* q, int32_t q_dtyp
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // asymmetric per-row pools: the new rows are quantized and stored by a
-  // launch of their own, then the attention reads them from the pool
-  const bool fused = append && kv != PKV_U8_ZP;
+  // quantized pools: the new rows are quantized and stored by a launch of
+  // their own, then the attention reads them from the pool
+  const bool fused = append && !is_quantized(kv);
   if (append && !fused) {
     rc = launch_cache_write_quant(*cache, k_new, v_new, q_dtype, nullptr, block_tables,
                                   max_blocks_per_seq, context_lens, num_seqs, st);

@@ -366,6 +366,167 @@ int launch_cwq(const pkv_cache_t& c, const void* k, const void* v, const int32_t
                 c.num_blocks, block_stride_bytes(c));
 }
 
+// Quantized append into a pool with one symmetric scale per (block, KV head)
+// tile (INT8, E4M3, E2M1).  Each decode step appends one token's K and V
+// (page "LLM 推理优化深度解析", section "KV Cache 的本质"); the tile's scale
+// covers the rows written so far, so a row whose a / Q exceeds it grows the
+// scale and the earlier rows are re-expressed:
+//   a = max |x| of the new row, c = a / Q (Q = 127, 448 or 6)
+//   row offset r == 0: a fresh tile, s = c (its old contents are ignored)
+//   r > 0: s_old = the tile's scale; if c > s_old, s = c and every earlier
+//          code becomes encode(decode(code) * s_old / s), else s = s_old
+//   new row: code = encode(x / s), zero codes when s == 0
+// every step binary32 with ties to even; rows after r are left alone.
+// One wavefront per (token, KV head, K-or-V); lane l holds the new row's
+// values 2l and 2l + 1 (lanes 32-63 hold none at D = 64), and re-encodes the
+// earlier rows 16 code bytes at a time.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two codes of a 32-bit word to binary32, exact: E4M3 bytes 2K and 2K + 1
+// (K = 0, 1), or the two E2M1 codes of byte K (low nibble first).
+template <int MODE, int K>
+__device__ __forceinline__ f32x2 sym_decode_pair(uint32_t w) {
+  if constexpr (MODE == Q_FP8)
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, K == 1);
+  else
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, K);
+}
+
+template <typename SrcT, int D, int MODE>
+__global__ __launch_bounds__(64) void cache_write_sym_kernel(
+    const SrcT* __restrict__ kn, const SrcT* __restrict__ vn, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, float* __restrict__ kscale, float* __restrict__ vscale,
+    const int32_t* __restrict__ slots, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ lens, int hkv, int num_blocks, size_t blk_bytes) {
+  constexpr float kQ = MODE == Q_I8 ? 127.0f : MODE == Q_FP8 ? 448.0f : 6.0f;
+  constexpr int kRowBytes = MODE == Q_FP4 ? D / 2 : D;
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  int64_t slot = -1;
+  if (slots != nullptr) {
+    slot = slots[i];
+  } else {
+    const int L = lens[i];
+    if (L > 0 && L <= max_blocks * kBlock)
+      slot = (int64_t)tables[(size_t)i * max_blocks + (L - 1) / kBlock] * kBlock + (L - 1) % kBlock;
+  }
+  if (slot < 0 || slot >= (int64_t)num_blocks * kBlock) return;
+  const bool is_v = blockIdx.y != 0;
+  const int64_t blk = slot / kBlock;
+  const int r = (int)(slot % kBlock);
+  uint8_t* tile = (is_v ? vc : kc) + (size_t)blk * blk_bytes + (size_t)g * kBlock * kRowBytes;
+  float* scp = (is_v ? vscale : kscale) + (size_t)blk * hkv + g;
+
+  // the new row: values 2 lane and 2 lane + 1
+  const bool has = 2 * lane < D;
+  float x0 = 0.f, x1 = 0.f;
+  if (has) {
+    const SrcT* src = (is_v ? vn : kn) + ((size_t)i * hkv + g) * D + 2 * lane;
+    if constexpr (sizeof(SrcT) == 4) {
+      x0 = src[0];
+      x1 = src[1];
+    } else {
+      x0 = bf16_bits_to_f32(src[0]);
+      x1 = bf16_bits_to_f32(src[1]);
+    }
+  }
+  const float a = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const float c = a / kQ;
+  float s = c;
+  if (r > 0) {
+    const float s_old = *scp;
+    s = s_old;
+    if (c > s_old) {
+      s = c;
+      // re-encode rows 0 .. r-1, 16 code bytes per lane and pass
+      const int chunks = r * kRowBytes / 16;
+      for (int ch = lane; ch < chunks; ch += kWave) {
+        uint4* p = reinterpret_cast<uint4*>(tile + ch * 16);
+        const uint4 in = *p;
+        const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (MODE == Q_I8) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = (float)(int8_t)((w[q] >> (8 * e)) & 0xFFu) * s_old;
+              const float rr = fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
+              acc |= (uint32_t)(uint8_t)(int8_t)(int)rr << (8 * e);
+            }
+            o[q] = acc;
+          } else if constexpr (MODE == Q_FP8) {
+            const f32x2 lo = sym_decode_pair<MODE, 0>(w[q]), hi = sym_decode_pair<MODE, 1>(w[q]);
+            const float v0 = lo[0] * s_old, v1 = lo[1] * s_old;
+            const float v2 = hi[0] * s_old, v3 = hi[1] * s_old;
+            o[q] = e4m3_word(v0 / s, v1 / s, v2 / s, v3 / s);
+          } else {
+            const f32x2 c0 = sym_decode_pair<MODE, 0>(w[q]), c1 = sym_decode_pair<MODE, 1>(w[q]);
+            const f32x2 c2 = sym_decode_pair<MODE, 2>(w[q]), c3 = sym_decode_pair<MODE, 3>(w[q]);
+            auto rq = [&](float d) {
+              const float v = d * s_old;
+              return v / s;
+            };
+            uint32_t acc = 0;
+            acc = e2m1_pair<0>(acc, rq(c0[0]), rq(c0[1]));
+            acc = e2m1_pair<1>(acc, rq(c1[0]), rq(c1[1]));
+            acc = e2m1_pair<2>(acc, rq(c2[0]), rq(c2[1]));
+            acc = e2m1_pair<3>(acc, rq(c3[0]), rq(c3[1]));
+            o[q] = acc;
+          }
+        }
+        *p = uint4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  }
+  // the new row's codes
+  if (has) {
+    uint8_t* dst = tile + (size_t)r * kRowBytes;
+    const bool zero = s == 0.0f;
+    if constexpr (MODE == Q_I8) {
+      const float r0 = fminf(fmaxf(rintf(x0 / s), -127.0f), 127.0f);
+      const float r1 = fminf(fmaxf(rintf(x1 / s), -127.0f), 127.0f);
+      const uint16_t v = zero ? 0 : (uint16_t)((uint8_t)(int8_t)(int)r0 |
+                                               ((uint16_t)(uint8_t)(int8_t)(int)r1 << 8));
+      *reinterpret_cast<uint16_t*>(dst + 2 * lane) = v;
+    } else if constexpr (MODE == Q_FP8) {
+      const uint32_t w = zero ? 0u : e4m3_word(x0 / s, x1 / s, 0.f, 0.f);
+      *reinterpret_cast<uint16_t*>(dst + 2 * lane) = (uint16_t)(w & 0xFFFFu);
+    } else {
+      const uint32_t w = zero ? 0u : e2m1_pair<0>(0u, x0 / s, x1 / s);
+      dst[lane] = (uint8_t)(w & 0xFFu);
+    }
+  }
+  if (lane == 0) *scp = s;
+}
+
+template <typename SrcT, int D, int MODE>
+int launch_cws(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,
+               const int32_t* tables, int max_blocks, const int32_t* lens, int n,
+               hipStream_t st) {
+  dim3 grid((unsigned)((int64_t)n * c.num_kv_heads), 2), block(kWave);
+  return launch(cache_write_sym_kernel<SrcT, D, MODE>, grid, block, st, (const SrcT*)k,
+                (const SrcT*)v, (uint8_t*)c.k_cache, (uint8_t*)c.v_cache, c.k_scale, c.v_scale,
+                slots, tables, max_blocks, lens, c.num_kv_heads, c.num_blocks,
+                block_stride_bytes(c));
+}
+
+template <typename SrcT, int D>
+int launch_cwq_any(const pkv_cache_t& c, const void* k, const void* v, const int32_t* slots,
+                   const int32_t* tables, int max_blocks, const int32_t* lens, int n,
+                   hipStream_t st) {
+  switch (c.kv_dtype) {
+    case PKV_U8_ZP: return launch_cwq<SrcT, D>(c, k, v, slots, tables, max_blocks, lens, n, st);
+    case PKV_I8: return launch_cws<SrcT, D, Q_I8>(c, k, v, slots, tables, max_blocks, lens, n, st);
+    case PKV_FP8_E4M3:
+      return launch_cws<SrcT, D, Q_FP8>(c, k, v, slots, tables, max_blocks, lens, n, st);
+    case PKV_FP4_E2M1:
+      return launch_cws<SrcT, D, Q_FP4>(c, k, v, slots, tables, max_blocks, lens, n, st);
+    default: return PKV_ERR_UNSUPPORTED;
+  }
+}
+
 template <typename SrcT, int D>
 int launch_qd(const pkv_cache_t& src, const pkv_cache_t& dst, const int32_t* ids, int n,
               hipStream_t st) {
@@ -397,10 +558,10 @@ int launch_cache_write_quant(const pkv_cache_t& c, const void* k, const void* v,
   if (n == 0) return PKV_OK;
   const bool f32 = src_dtype == PKV_F32;
   if (c.head_dim == 128)
-    return f32 ? launch_cwq<float, 128>(c, k, v, slots, tables, max_blocks, lens, n, st)
-               : launch_cwq<uint16_t, 128>(c, k, v, slots, tables, max_blocks, lens, n, st);
-  return f32 ? launch_cwq<float, 64>(c, k, v, slots, tables, max_blocks, lens, n, st)
-             : launch_cwq<uint16_t, 64>(c, k, v, slots, tables, max_blocks, lens, n, st);
+    return f32 ? launch_cwq_any<float, 128>(c, k, v, slots, tables, max_blocks, lens, n, st)
+               : launch_cwq_any<uint16_t, 128>(c, k, v, slots, tables, max_blocks, lens, n, st);
+  return f32 ? launch_cwq_any<float, 64>(c, k, v, slots, tables, max_blocks, lens, n, st)
+             : launch_cwq_any<uint16_t, 64>(c, k, v, slots, tables, max_blocks, lens, n, st);
 }
 
 }  // namespace pkv

@@ -19,7 +19,9 @@ a long context; shared-prefix and quantized KV):
                      128 physical blocks) + U{0..1024} private tokens; bf16
                      source pool that the caller quantizes to INT8 or FP8
                      (tests shrink it; a sequence shorter than the prefix
-                     still has the prefix ids as its first table entries)
+                     still has the prefix ids as its first table entries;
+                     with write=True and suffix_lo=1 each sequence also
+                     gets a new token in a private block)
 
 Recipe: ``numpy.random.default_rng(seed)`` (seed = workload number unless
 given); draw order lens -> block permutation -> pool K -> pool V -> new K ->
@@ -156,7 +158,7 @@ def make(cfg: int, seed: Optional[int] = None, quant: Optional[str] = None, **ov
         lens = np.full(B, spec["L"], dtype=np.int64)
         hi_len = spec["L"]
     else:
-        suffix = rng.integers(0, spec["suffix_hi"], size=B, endpoint=True)
+        suffix = rng.integers(spec.get("suffix_lo", 0), spec["suffix_hi"], size=B, endpoint=True)
         lens = spec["prefix"] + suffix
         hi_len = spec["prefix"] + spec["suffix_hi"]
     lens = lens.astype(np.int32)

@@ -209,7 +209,8 @@ def test_asymmetric_pool_validation():
     assert lib.pkv_cache_write(ctypes.byref(_u8z()), FAKE, FAKE, FAKE, 3, None) == 6
     wq = lambda cc, k=FAKE, v=FAKE, sd=1, s=FAKE, n=3: lib.pkv_cache_write_quant(
         ctypes.byref(cc), k, v, sd, s, n, None)
-    assert wq(_cache()) == 3                            # not a u8z pool
+    assert wq(_cache()) == 3                            # not a quantized pool
+    assert wq(_cache(kv_dtype=2, k_scale=FAKE, v_scale=FAKE), sd=2) == 3   # INT8 from INT8
     assert wq(_u8z(), sd=2) == 3                        # source must be f32 or bf16
     assert wq(_u8z(), n=-1) == 2
     assert wq(_u8z(), n=0) == 0
