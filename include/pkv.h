@@ -432,6 +432,25 @@ int pkv_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
                         int32_t* bad_seq, void* stream);
 
+/* Debug check of a slot list before a cache write ([MGMT] section 二: a
+ * failed append is reported as a return value, not a crash).  Writes skip a
+ * negative slot and one outside [0, num_blocks * 16); two entries with the
+ * same slot would race (the result depends on their order), and for the
+ * per-tile formats (PKV_I8, PKV_FP8_E4M3, PKV_FP4_E2M1) two entries in the
+ * same block would race on the tile's scale.  Returns PKV_ERR_RANGE if an
+ * entry is at or past num_blocks * 16, or repeats the slot (with
+ * one_per_block != 0: the block, slot / 16) of an earlier entry; negative
+ * entries are padding and pass.  *bad_index (if not NULL) receives the first
+ * offending index, or -1.
+ *   pkv_validate_slots: slot_mapping is device memory; the call copies it to
+ *     the host and synchronises `stream`.
+ *   pkv_validate_slots_host: slot_mapping is host memory (a scheduler's own
+ *     copy); no HIP call. */
+int pkv_validate_slots(const int32_t* slot_mapping, int32_t n, int32_t num_blocks,
+                       int32_t one_per_block, int32_t* bad_index, void* stream);
+int pkv_validate_slots_host(const int32_t* slot_mapping, int32_t n, int32_t num_blocks,
+                            int32_t one_per_block, int32_t* bad_index);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIBRARY names another build of the same library (e.g. one whose host
+# code is compiled with sanitizers)
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 SPLIT_BALANCED = -1     # partition_tokens value: balanced split (PKV_SPLIT_BALANCED)
@@ -85,6 +87,8 @@ def _load():
             "pkv_copy_blocks": (ctypes.c_int, [C, P, I32, P]),
             "pkv_validate_tables": (ctypes.c_int, [P, I32, P, I32, I32,
                                                    ctypes.POINTER(I32), P]),
+            "pkv_validate_slots": (ctypes.c_int, [P, I32, I32, I32, ctypes.POINTER(I32), P]),
+            "pkv_validate_slots_host": (ctypes.c_int, [P, I32, I32, I32, ctypes.POINTER(I32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -105,7 +109,8 @@ EXPORTED_SYMBOLS = ("pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_slot_m
                     "pkv_decode_default_partition", "pkv_attention_decode", "pkv_decode_step",
                     "pkv_decode_step_noalloc", "pkv_attention_prefix",
                     "pkv_quantize", "pkv_copy_blocks",
-                    "pkv_gather", "pkv_validate_tables")
+                    "pkv_gather", "pkv_validate_tables", "pkv_validate_slots",
+                    "pkv_validate_slots_host")
 
 
 def _check(fn: str, status: int):
@@ -588,4 +593,21 @@ def validate_tables(block_tables, context_lens, num_blocks, stream=None):
     rc = _load().pkv_validate_tables(_ptr(block_tables), block_tables.shape[1],
                                      _ptr(context_lens), context_lens.shape[0], num_blocks,
                                      ctypes.byref(bad), _stream(stream))
+    return rc, bad.value
+
+
+def validate_slots(slot_mapping, num_blocks, one_per_block=False, stream=None):
+    """Debug check of a slot list (device tensor: synchronises; numpy array
+    or list: checked on the host): returns (status, first bad index or -1)."""
+    bad = ctypes.c_int32(-1)
+    torch = _torch()
+    if isinstance(slot_mapping, torch.Tensor) and slot_mapping.is_cuda:
+        _need(slot_mapping, "slot_mapping", torch.int32, 1)
+        rc = _load().pkv_validate_slots(_ptr(slot_mapping), slot_mapping.shape[0], num_blocks,
+                                        int(one_per_block), ctypes.byref(bad), _stream(stream))
+    else:
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int32))
+        rc = _load().pkv_validate_slots_host(a.ctypes.data_as(ctypes.c_void_p), a.shape[0],
+                                             num_blocks, int(one_per_block), ctypes.byref(bad))
     return rc, bad.value

@@ -58,6 +58,68 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(ROOT, "_build", "asan", "libpkv.so")
+# the argument checks (csrc/api.hip) with AddressSanitizer and
+# UndefinedBehaviorSanitizer on their host code; device code is not
+# instrumented
+SAN_SOURCE = "api.hip"
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libpkv.so whose argument checks (csrc/api.hip) are built with host
+    ASan and UBSan, linked with the kernel sources' regular objects (reused
+    from the last build when newer than their sources).  Returns its path."""
+    outdir = os.path.dirname(SAN_LIB)
+    os.makedirs(outdir, exist_ok=True)
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    headers = glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+    newest_header = max(os.path.getmtime(h) for h in headers)
+
+    def comp(src):
+        if os.path.basename(src) == SAN_SOURCE:
+            obj = os.path.join(outdir, SAN_SOURCE + ".o")
+            cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-c", src, "-o", obj]
+        else:
+            obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+            if (os.path.exists(obj) and os.path.getmtime(obj) >= os.path.getmtime(src)
+                    and os.path.getmtime(obj) >= newest_header):
+                return obj
+            cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+                        "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-shared-libsan", *objs, "-o", SAN_LIB], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (preloaded into a Python
+    process that loads the sanitized library)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        found = glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        path = found[0] if found else ""
+    return path
+
+
 def clean() -> None:
     shutil.rmtree(OBJDIR, ignore_errors=True)
 

@@ -4,8 +4,11 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "common.hpp"
 
@@ -66,6 +69,28 @@ int check_cache(const pkv_cache_t* c) {
       return PKV_ERR_UNSUPPORTED;
   }
   return PKV_OK;
+}
+
+// First offending index of a slot list held on the host (see
+// pkv_validate_slots), or -1: an entry outside [0, num_slots), or one whose
+// slot (block, with one_per_block) an earlier entry already holds.
+int first_bad_slot(const int32_t* sl, int32_t n, int64_t num_slots, bool one_per_block) {
+  int best = INT_MAX;
+  std::vector<std::pair<int64_t, int>> keys;
+  keys.reserve((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const int32_t v = sl[i];
+    if (v < 0) continue;   // padding, skipped by the writes
+    if ((int64_t)v >= num_slots) {
+      best = std::min(best, i);
+      continue;
+    }
+    keys.emplace_back(one_per_block ? v / PKV_BLOCK_SIZE : v, i);
+  }
+  std::sort(keys.begin(), keys.end());
+  for (size_t k = 1; k < keys.size(); ++k)
+    if (keys[k].first == keys[k - 1].first) best = std::min(best, keys[k].second);
+  return best == INT_MAX ? -1 : best;
 }
 
 bool split_ok(int32_t partition_tokens) {
@@ -344,6 +369,38 @@ int pkv_gather(const pkv_cache_t* cache, const int32_t* block_tables, int32_t ma
   if ((int64_t)num_seqs * max_blocks_per_seq > (int64_t)INT_MAX) return PKV_ERR_SHAPE;
   return launch_gather(*cache, block_tables, max_blocks_per_seq, context_lens, cu_seqlens,
                        num_seqs, k_out, v_out, static_cast<hipStream_t>(stream));
+}
+
+int pkv_validate_slots_host(const int32_t* slot_mapping, int32_t n, int32_t num_blocks,
+                            int32_t one_per_block, int32_t* bad_index) {
+  if (bad_index) *bad_index = -1;
+  if (n < 0 || num_blocks < 0) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!slot_mapping) return PKV_ERR_NULL;
+  const int bad = first_bad_slot(slot_mapping, n, (int64_t)num_blocks * PKV_BLOCK_SIZE,
+                                 one_per_block != 0);
+  if (bad_index) *bad_index = bad;
+  return bad < 0 ? PKV_OK : PKV_ERR_RANGE;
+}
+
+int pkv_validate_slots(const int32_t* slot_mapping, int32_t n, int32_t num_blocks,
+                       int32_t one_per_block, int32_t* bad_index, void* stream) {
+  if (bad_index) *bad_index = -1;
+  if (n < 0 || num_blocks < 0) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!slot_mapping) return PKV_ERR_NULL;
+  int32_t* hs = static_cast<int32_t*>(malloc((size_t)n * sizeof(int32_t)));
+  if (!hs) return PKV_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int rc;
+  if (hipMemcpyAsync(hs, slot_mapping, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    rc = PKV_ERR_HIP;
+  else
+    rc = pkv_validate_slots_host(hs, n, num_blocks, one_per_block, bad_index);
+  free(hs);
+  return rc;
 }
 
 int pkv_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -319,3 +319,37 @@ def test_decode_step_noalloc_rejects_bad_arguments():
     # the Llama-3-8B shape fits
     assert lib.pkv_decode_workspace_bytes(64, 32, 128, 256, pkv.SPLIT_BALANCED) <= \
         pkv.NOALLOC_MAX_WORKSPACE
+
+
+def test_validate_slots_host():
+    """Out-of-range and repeated slots are reported with the first offending
+    index; negative slots are padding; one_per_block also rejects two rows of
+    one block (the per-tile formats' tiles share a scale)."""
+    NB = 4                                         # slots 0 .. 63
+    assert pkv.validate_slots([0, 5, 63, -1, -7, 16], NB) == (0, -1)
+    assert pkv.validate_slots([], NB) == (0, -1)
+    assert pkv.validate_slots([3, 64, 2], NB) == (4, 1)          # past the pool
+    assert pkv.validate_slots([3, 9, 2, 9, 3], NB) == (4, 3)     # 9 repeats first at 3
+    assert pkv.validate_slots([-1, -1, 10], NB) == (0, -1)       # padding may repeat
+    assert pkv.validate_slots([0, 17, 33, 49], NB, one_per_block=True) == (0, -1)
+    assert pkv.validate_slots([0, 17, 18, 49], NB, one_per_block=True) == (4, 2)
+    assert pkv.validate_slots([70, 1, 1], NB, one_per_block=True) == (4, 0)
+    lib = pkv.lib()
+    bad = ctypes.c_int32(5)
+    assert lib.pkv_validate_slots_host(None, 3, NB, 0, ctypes.byref(bad)) == 1
+    assert lib.pkv_validate_slots_host(None, -1, NB, 0, None) == 2
+    assert lib.pkv_validate_slots(None, -1, NB, 0, None, None) == 2
+    assert lib.pkv_validate_slots(None, 2, NB, 0, None, None) == 1
+    rng = __import__("numpy").random.default_rng(3)
+    for _ in range(200):
+        s = rng.integers(-3, 70, int(rng.integers(0, 40)))
+        want = -1
+        seen = set()
+        for i, v in enumerate(s):
+            if v < 0:
+                continue
+            if v >= NB * 16 or v in seen:
+                want = i
+                break
+            seen.add(v)
+        assert pkv.validate_slots(s, NB) == ((0, -1) if want < 0 else (4, want))
