@@ -80,6 +80,9 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 // native clang vector (HIP's u32x4 is a wrapper struct that can keep arrays of
 // it out of registers)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxDevices = 64;
@@ -342,6 +345,20 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   constexpr bool kBlockScale = KV == KV_I8 || KV == KV_FP8 || KV == KV_FP4;
   constexpr int kNKK = D / 32;              // QK^T instructions per block
   constexpr int kNT = D / 16;               // PV instructions per block
+  // E4M3 and E2M1 K codes enter v_mfma_scale_f32_16x16x128_f8f6f4 as they
+  // are stored (A = K rows, 128 codes per row), with the queries as two
+  // E4M3 operands (hi + lo): no widening.  Lane (j, n) holds 32 codes of row
+  // n; past head_dim they are zero.  E2M1: codes 32 j .. 32 j + 31, one
+  // 16-byte load straight into the operand (the four lanes of a row read
+  // its 64 bytes, so a load stays contiguous).  E4M3: the tile is loaded
+  // linearly and staged in LDS as raw codes (16-byte chunks XOR-swizzled by
+  // row), and lane (j, n) reads back chunks 2 j and 2 j + 1 of row n; loading
+  // those 32 bytes directly would touch every cache line twice.
+  // INT8 K codes take the same raw staging into v_mfma_i32_16x16x64_i8 (two
+  // 64-code halves per row), with the queries as two int8 operands (hi, lo):
+  // the products are exact integers.
+  constexpr bool kDirectK = KV == KV_FP8 || KV == KV_FP4 || KV == KV_I8;
+  constexpr int kKLoads = KV == KV_FP4 ? 1 : kLoads;
   const int lane = threadIdx.x;
   const int j = lane >> 4;   // token quad (rows 4j..4j+3 of S) / k-slice
   const int n = lane & 15;   // head column
@@ -372,13 +389,81 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
   // queries of this group as the B operand of S = K q^T: lane (j, n) holds
   // q[h][32 kk + 8 j .. + 8] for each kk
-  bf16x8 qop[kNKK];
+  // queries as the B operand: 8 values per MFMA k-slice, or (direct K) the
+  // 32 values that pair with this lane group's K codes in the k order of
+  // v_mfma_scale_f32_16x16x128_f8f6f4.  With an E4M3 A operand lane group j
+  // holds k = 32 j .. 32 j + 31; with an E2M1 A operand its 32 codes pair
+  // with the B bytes of k = 16 j .. 16 j + 15 and 64 + 16 j .. 64 + 16 j + 15
+  // (taken from an in-bounds probe of the instruction), so B lane group j
+  // holds q[16 j ..] and q[64 + 16 j ..]; past head_dim the values are 0.
+  constexpr int kQV = kDirectK ? 4 : kNKK;
+  bf16x8 qop[kQV];
   {
     const uint16_t* qrow = a.q + (has_head ? out_row : (size_t)s * a.ntok * hq) * D;
 #pragma unroll
-    for (int kk = 0; kk < kNKK; ++kk) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * j);
+    for (int kk = 0; kk < kQV; ++kk) {
+      int off = 32 * kk + 8 * j;
+      if constexpr (KV == KV_FP8 || KV == KV_I8) off = 32 * j + 8 * kk;
+      if constexpr (KV == KV_FP4) off = kk < 2 ? 16 * j + 8 * kk : 64 + 16 * j + 8 * (kk - 2);
+      bf16x8 v = {};
+      if (!kDirectK || off < D) v = *reinterpret_cast<const bf16x8*>(qrow + off);
       qop[kk] = has_head ? v : bf16x8{};
+    }
+  }
+  // Direct K: the queries, scaled per head by 2^qe, split into two operands
+  // whose sum holds them to a few ulp of bf16 or better.  E4M3: the largest
+  // |q| 2^qe lies in [128, 256); hi = nearest E4M3 of q 2^qe and lo = nearest
+  // E4M3 of the (exact) remainder, about 8 significant bits together.  INT8:
+  // the largest |q| 2^qe lies in [2^12, 2^13); q 2^qe is rounded to an
+  // integer u = 128 hi + lo with hi = (u + 64) >> 7 and lo in [-64, 63], both
+  // int8, 13 bits in all, and the two integer products are exact.  The logit
+  // multiplies by 2^-qe.
+  i32x8 qhi8 = {}, qlo8 = {};
+  float qinv_d = 1.f;
+  if constexpr (kDirectK) {
+    float mq = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kQV; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(static_cast<float>(qop[kk][e])));
+    mq = rows_max(mq);
+    constexpr int kTop = KV == KV_I8 ? 13 : 8;
+    const int qe = mq > 0.f ? kTop - __builtin_amdgcn_frexp_expf(mq) : 0;
+    qinv_d = __builtin_ldexpf(1.f, -qe);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * w + e;   // byte v of the operand
+        y[e] = __builtin_ldexpf(static_cast<float>(qop[v / 8][v % 8]), qe);
+      }
+      if constexpr (KV == KV_I8) {
+        uint32_t hw = 0, lw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int u = (int)rintf(y[e]);
+          const int hi = (u + 64) >> 7;
+          const int lo = u - (hi << 7);
+          hw |= (uint32_t)(uint8_t)(int8_t)hi << (8 * e);
+          lw |= (uint32_t)(uint8_t)(int8_t)lo << (8 * e);
+        }
+        qhi8[w] = (int)hw;
+        qlo8[w] = (int)lw;
+      } else {
+        s16x2 h = {0, 0};
+        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, y[0], y[1], 1.0f, false);
+        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, y[2], y[3], 1.0f, true);
+        const uint32_t hw = __builtin_bit_cast(uint32_t, h);
+        const f32x2 d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, 1.0f, false);
+        const f32x2 d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, 1.0f, true);
+        s16x2 l = {0, 0};
+        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, y[0] - d01[0], y[1] - d01[1], 1.0f,
+                                                      false);
+        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, y[2] - d23[0], y[3] - d23[1], 1.0f, true);
+        qhi8[w] = (int)hw;
+        qlo8[w] = __builtin_bit_cast(int, l);
+      }
     }
   }
   float qsum = 0.f;   // sum of the scaled fp16 queries of this lane's head
@@ -387,7 +472,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // |q| in [2^14, 2^15) and keeps every value finite in fp16 (bf16 values
   // within 2^29 of that largest one convert exactly).  The logit then takes
   // (1024 + offset) * sum(q) off and multiplies by 2^-qe.
-  constexpr bool kK16 = KV == KV_I8 || KV == KV_U8Z;
+  constexpr bool kK16 = KV == KV_U8Z;
   f16x8 qoh[kNKK];
   float qinv = 1.f;
   if constexpr (kK16) {
@@ -408,9 +493,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
     qsum = rows_sum(qsum);
   }
-  // INT8: each logit holds (1024 + 128) * sum(q) on top; uint8 subtracts
-  // (1024 + zero point) * sum(q) per row
-  const float qoff = (KV == KV_I8 ? 1152.f : 1024.f) * qsum;
+  // uint8 subtracts (1024 + zero point) * sum(q) per row
+  const float qoff = 1024.f * qsum;
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = a.blk_stride;
@@ -490,7 +574,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     // scales in lanes 16-31, its K zero points (4 per dword) in lanes 32-35
     // and its V zero points in lanes 36-39; every other lane's offset lies
     // outside the descriptor's range and reads zero.
-    auto load_tile = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], u32x4& pr, int ph, int bl) {
+    auto load_tile = [&](u32x4 (&kr)[kKLoads], u32x4 (&vr)[kLoads], u32x4& pr, int ph, int bl) {
       const bool in = ph >= 0 && ph < num_blocks;
       const size_t off = in ? (size_t)ph * blk_stride : 0;
       const rsrc_t rk = make_rsrc(kbase + off, in ? kTile : 0);
@@ -499,14 +583,22 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       // zero weight would not cancel
       const int vrows = __builtin_amdgcn_readfirstlane(min(max(L - bl * kBlock, 0), kBlock));
       const rsrc_t rv = make_rsrc(vbase + off, in ? vrows * kRowBytes : 0);
+      // tiles other wavefronts read again (later passes, other sequence
+      // groups of a shared prefix) stay cached
+      constexpr int kCpol = MQ == kMqPasses || MQ == kMqSeqs ? 0 : kCpolNT;
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        // tiles other wavefronts read again (later passes, other sequence
-        // groups of a shared prefix) stay cached
-        constexpr int kCpol = MQ == kMqPasses || MQ == kMqSeqs ? 0 : kCpolNT;
-        kr[i] = buffer_load16_kv<kCpol>(rk, i * 1024 + lane * 16);
-        vr[i] = buffer_load16_kv<kCpol>(rv, i * 1024 + lane * 16);
+      for (int i = 0; i < kKLoads; ++i) {
+        if constexpr (KV == KV_FP4) {
+          // row n, bytes 16 j .. 16 j + 15 (codes 32 j ..); past head_dim the
+          // offset leaves the descriptor and loads zeros
+          const int off = 16 * j < kRowBytes ? n * kRowBytes + 16 * j : kTile;
+          kr[i] = buffer_load16_kv<kCpol>(rk, off);
+        } else {
+          kr[i] = buffer_load16_kv<kCpol>(rk, i * 1024 + lane * 16);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) vr[i] = buffer_load16_kv<kCpol>(rv, i * 1024 + lane * 16);
       if constexpr (KV == KV_U8Z) {
         const size_t row0 = in ? ((size_t)ph * hkv + g) * kBlock : 0;
         const rsrc_t rks = make_rsrc(a.ksc + row0, in ? kBlock * 4 : 0);
@@ -522,7 +614,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
     // Stage block b from (kr, vr) into LDS, refill the buffer with block
     // b+2, then run QK^T, the softmax update and PV for block b.
-    auto process = [&](u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], u32x4& pr, int& ph, int b) {
+    auto process = [&](u32x4 (&kr)[kKLoads], u32x4 (&vr)[kLoads], u32x4& pr, int& ph, int b) {
       const int cur = ph;
       const bool cur_ok = cur >= 0 && cur < num_blocks;
       const int valid = cur_ok ? min(kBlock, L - b * kBlock) : 0;  // valid rows
@@ -549,31 +641,42 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           const int e0 = (i * 1024 + lane * 16) * 2;   // first of this lane's 32 codes
           const int row = e0 / D, col = e0 % D;
           if (row < kBlock) {
-            u32x4 kw[4], vw[4];
-            widen32_fp4(kr[i], kw);
+            u32x4 vw[4];
             widen32_fp4(vr[i], vw);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8 + c)) = kw[c];
+            for (int c = 0; c < 4; ++c)
               *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8 + c)) = vw[c];
-            }
           }
+        } else if constexpr (KV == KV_FP8) {
+          const int byte = (i * 64 + lane) * 16;    // first code of this chunk
+          const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
+          u32x4 vlo4, vhi;
+          widen16<KV>(vr[i], vlo4, vhi);
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8)) = vlo4;
+          *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8 + 1)) = vhi;
+          // raw K codes: chunk c of row r at r * D + 16 (c ^ (r mod D / 16))
+          constexpr int kC = D / 16;
+          *reinterpret_cast<u32x4*>(lds_k + row * D + 16 * ((col / 16) ^ (row % kC))) = kr[i];
         } else {
           const int byte = (i * 64 + lane) * 16;    // first code of this chunk
           const int row = byte / D, col = byte % D; // 16 codes = 2 bf16 chunks
-          u32x4 klo, khi, vlo4, vhi;
-          if constexpr (kK16)
-            widen16_k16<KV>(kr[i], klo, khi);
-          else
-            widen16<KV>(kr[i], klo, khi);
+          u32x4 vlo4, vhi;
           if constexpr (kV16)
             widen16_k16<KV>(vr[i], vlo4, vhi);
           else
             widen16<KV>(vr[i], vlo4, vhi);
-          *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8)) = klo;
-          *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8 + 1)) = khi;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8)) = vlo4;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8 + 1)) = vhi;
+          if constexpr (KV == KV_I8) {
+            // raw K codes, as for E4M3
+            constexpr int kC = D / 16;
+            *reinterpret_cast<u32x4*>(lds_k + row * D + 16 * ((col / 16) ^ (row % kC))) = kr[i];
+          } else {
+            u32x4 klo, khi;
+            widen16_k16<KV>(kr[i], klo, khi);
+            *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8)) = klo;
+            *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8 + 1)) = khi;
+          }
         }
       }
       if constexpr (kZeroLow) {
@@ -628,14 +731,54 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         vzw = *reinterpret_cast<const uint32_t*>(lds_p + 144 + 4 * j);
       }
 
+      // direct K: E2M1 codes leave the buffer before its refill; E4M3 codes
+      // come back from LDS (chunks 2 j and 2 j + 1 of row n)
+      i32x8 ka = {};
+      if constexpr (KV == KV_FP4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ka[e] = (int)kr[0][e];
+      } else if constexpr (KV == KV_FP8 || KV == KV_I8) {
+        constexpr int kC = D / 16;
+        if (2 * j < kC) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const u32x4 c = *reinterpret_cast<const u32x4*>(
+                lds_k + n * D + 16 * ((2 * j + h) ^ (n % kC)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ka[4 * h + e] = (int)c[e];
+          }
+        }
+      }
+
       // ---- refill this buffer with block b+NST (zero-length if absent)
       ph = phys_of(b + NST);
       load_tile(kr, vr, pr, ph, b + NST);
 
       // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
       f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (KV == KV_I8) {
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4 a0 = {ka[0], ka[1], ka[2], ka[3]}, a1 = {ka[4], ka[5], ka[6], ka[7]};
+        const i32x4 h0 = {qhi8[0], qhi8[1], qhi8[2], qhi8[3]};
+        const i32x4 h1 = {qhi8[4], qhi8[5], qhi8[6], qhi8[7]};
+        const i32x4 l0 = {qlo8[0], qlo8[1], qlo8[2], qlo8[3]};
+        const i32x4 l1 = {qlo8[4], qlo8[5], qlo8[6], qlo8[7]};
+        i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
+        ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, h0, ah, 0, 0, 0);
+        ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, h1, ah, 0, 0, 0);
+        al = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, l0, al, 0, 0, 0);
+        al = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, l1, al, 0, 0, 0);
 #pragma unroll
-      for (int kk = 0; kk < kNKK; ++kk) {
+        for (int i = 0; i < 4; ++i) sv[i] = (float)(ah[i] * 128 + al[i]);
+      } else if constexpr (kDirectK) {
+        constexpr int kFmtA = KV == KV_FP8 ? 0 : 4;   // A operand: E4M3 or E2M1 codes
+        sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi8, sv, kFmtA, 0, 0, 127, 0,
+                                                              127);
+        sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo8, sv, kFmtA, 0, 0, 127, 0,
+                                                              127);
+      }
+#pragma unroll
+      for (int kk = 0; kk < (kDirectK ? 0 : kNKK); ++kk) {
         if constexpr (kK16) {
           const f16x8 kop = *reinterpret_cast<const f16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
           sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qoh[kk], sv, 0, 0, 0);
@@ -666,7 +809,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
 
       // ---- online softmax (base 2)
-      const float cb = a.scale_log2 * kscale * qinv;
+      const float cb = a.scale_log2 * kscale * (kDirectK ? qinv_d : qinv);
       float x[4];
       float mx = -INFINITY;
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
@@ -683,7 +826,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
           x[i] = (sv[i] - __builtin_fmaf((float)((kzw >> (8 * i)) & 0xFFu), qsum, qoff)) *
                  (cb * ks4[i]);
         else
-          x[i] = ((KV == KV_I8) ? sv[i] - qoff : sv[i]) * cb;
+          x[i] = sv[i] * cb;
       }
       if (!full) {
 #pragma unroll
@@ -742,7 +885,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     };
 
     // NST register buffers in a ring: buffer i holds block b with b % NST == i
-    u32x4 kr[NST][kLoads], vr[NST][kLoads], pr[NST];
+    u32x4 kr[NST][kKLoads], vr[NST][kLoads], pr[NST];
     int ph[NST];
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
