@@ -356,8 +356,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // those 32 bytes directly would touch every cache line twice.
   // INT8 K codes take the same raw staging into v_mfma_i32_16x16x64_i8 (two
   // 64-code halves per row), with the queries as two int8 operands (hi, lo):
-  // the products are exact integers.
-  constexpr bool kDirectK = KV == KV_FP8 || KV == KV_FP4 || KV == KV_I8;
+  // the products are exact integers.  Per-row uint8 codes c are staged as
+  // the int8 c - 128 and the row's logit takes (128 - zero) sum(q) back on.
+  constexpr bool kIntK = KV == KV_I8 || KV == KV_U8Z;
+  constexpr bool kDirectK = KV == KV_FP8 || KV == KV_FP4 || kIntK;
   constexpr int kKLoads = KV == KV_FP4 ? 1 : kLoads;
   const int lane = threadIdx.x;
   const int j = lane >> 4;   // token quad (rows 4j..4j+3 of S) / k-slice
@@ -403,7 +405,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
     for (int kk = 0; kk < kQV; ++kk) {
       int off = 32 * kk + 8 * j;
-      if constexpr (KV == KV_FP8 || KV == KV_I8) off = 32 * j + 8 * kk;
+      if constexpr (KV == KV_FP8 || kIntK) off = 32 * j + 8 * kk;
       if constexpr (KV == KV_FP4) off = kk < 2 ? 16 * j + 8 * kk : 64 + 16 * j + 8 * (kk - 2);
       bf16x8 v = {};
       if (!kDirectK || off < D) v = *reinterpret_cast<const bf16x8*>(qrow + off);
@@ -420,6 +422,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // multiplies by 2^-qe.
   i32x8 qhi8 = {}, qlo8 = {};
   float qinv_d = 1.f;
+  int qsum_i = 0;   // per-row uint8: sum of this lane's integer queries u
   if constexpr (kDirectK) {
     float mq = 0.f;
 #pragma unroll
@@ -427,7 +430,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
       for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(static_cast<float>(qop[kk][e])));
     mq = rows_max(mq);
-    constexpr int kTop = KV == KV_I8 ? 13 : 8;
+    constexpr int kTop = kIntK ? 13 : 8;
     const int qe = mq > 0.f ? kTop - __builtin_amdgcn_frexp_expf(mq) : 0;
     qinv_d = __builtin_ldexpf(1.f, -qe);
 #pragma unroll
@@ -438,11 +441,12 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         const int v = 4 * w + e;   // byte v of the operand
         y[e] = __builtin_ldexpf(static_cast<float>(qop[v / 8][v % 8]), qe);
       }
-      if constexpr (KV == KV_I8) {
+      if constexpr (kIntK) {
         uint32_t hw = 0, lw = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int u = (int)rintf(y[e]);
+          qsum_i += u;
           const int hi = (u + 64) >> 7;
           const int lo = u - (hi << 7);
           hw |= (uint32_t)(uint8_t)(int8_t)hi << (8 * e);
@@ -466,35 +470,9 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
     }
   }
-  float qsum = 0.f;   // sum of the scaled fp16 queries of this lane's head
-  // INT8 and uint8 K codes enter QK^T as fp16 1024 + u (see widen16_k16), so
-  // the queries do too: scaled per head by 2^qe, which puts the head's largest
-  // |q| in [2^14, 2^15) and keeps every value finite in fp16 (bf16 values
-  // within 2^29 of that largest one convert exactly).  The logit then takes
-  // (1024 + offset) * sum(q) off and multiplies by 2^-qe.
-  constexpr bool kK16 = KV == KV_U8Z;
-  f16x8 qoh[kNKK];
-  float qinv = 1.f;
-  if constexpr (kK16) {
-    float mq = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < kNKK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(static_cast<float>(qop[kk][e])));
-    mq = rows_max(mq);
-    const int qe = mq > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mq) : 0;
-    qinv = __builtin_ldexpf(1.f, -qe);
-#pragma unroll
-    for (int kk = 0; kk < kNKK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qoh[kk][e] = static_cast<_Float16>(__builtin_ldexpf(static_cast<float>(qop[kk][e]), qe));
-        qsum += static_cast<float>(qoh[kk][e]);
-      }
-    qsum = rows_sum(qsum);
-  }
-  // uint8 subtracts (1024 + zero point) * sum(q) per row
-  const float qoff = 1024.f * qsum;
+  // per-row uint8: the integer queries' sum over the head (exact: at most
+  // 128 * 2^13 in magnitude)
+  if constexpr (KV == KV_U8Z) qsum_i = (int)rows_sum((float)qsum_i);
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = a.blk_stride;
@@ -667,16 +645,11 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             widen16<KV>(vr[i], vlo4, vhi);
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8)) = vlo4;
           *reinterpret_cast<u32x4*>(lds_v + lds_off<D, KV>(row, col / 8 + 1)) = vhi;
-          if constexpr (KV == KV_I8) {
-            // raw K codes, as for E4M3
-            constexpr int kC = D / 16;
-            *reinterpret_cast<u32x4*>(lds_k + row * D + 16 * ((col / 16) ^ (row % kC))) = kr[i];
-          } else {
-            u32x4 klo, khi;
-            widen16_k16<KV>(kr[i], klo, khi);
-            *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8)) = klo;
-            *reinterpret_cast<u32x4*>(lds_k + lds_off<D, KV>(row, col / 8 + 1)) = khi;
-          }
+          // raw K codes, as for E4M3 (uint8: as the int8 c - 128)
+          constexpr int kC = D / 16;
+          u32x4 kw = kr[i];
+          if constexpr (KV == KV_U8Z) kw ^= u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+          *reinterpret_cast<u32x4*>(lds_k + row * D + 16 * ((col / 16) ^ (row % kC))) = kw;
         }
       }
       if constexpr (kZeroLow) {
@@ -737,7 +710,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       if constexpr (KV == KV_FP4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) ka[e] = (int)kr[0][e];
-      } else if constexpr (KV == KV_FP8 || KV == KV_I8) {
+      } else if constexpr (KV == KV_FP8 || kIntK) {
         constexpr int kC = D / 16;
         if (2 * j < kC) {
 #pragma unroll
@@ -756,7 +729,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 
       // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
       f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KV == KV_I8) {
+      int sk[4] = {0, 0, 0, 0};   // integer products (INT8, uint8)
+      if constexpr (kIntK) {
         typedef int i32x4 __attribute__((ext_vector_type(4)));
         const i32x4 a0 = {ka[0], ka[1], ka[2], ka[3]}, a1 = {ka[4], ka[5], ka[6], ka[7]};
         const i32x4 h0 = {qhi8[0], qhi8[1], qhi8[2], qhi8[3]};
@@ -769,7 +743,11 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         al = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, l0, al, 0, 0, 0);
         al = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, l1, al, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = (float)(ah[i] * 128 + al[i]);
+        for (int i = 0; i < 4; ++i) sk[i] = ah[i] * 128 + al[i];
+        if constexpr (KV == KV_I8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[i] = (float)sk[i];
+        }
       } else if constexpr (kDirectK) {
         constexpr int kFmtA = KV == KV_FP8 ? 0 : 4;   // A operand: E4M3 or E2M1 codes
         sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi8, sv, kFmtA, 0, 0, 127, 0,
@@ -779,13 +757,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
 #pragma unroll
       for (int kk = 0; kk < (kDirectK ? 0 : kNKK); ++kk) {
-        if constexpr (kK16) {
-          const f16x8 kop = *reinterpret_cast<const f16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
-          sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qoh[kk], sv, 0, 0, 0);
-        } else {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
-          sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
-        }
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
       }
 
       // ---- V^T operands of O^T += V^T P, read now so that their LDS latency
@@ -809,7 +782,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
 
       // ---- online softmax (base 2)
-      const float cb = a.scale_log2 * kscale * (kDirectK ? qinv_d : qinv);
+      const float cb = a.scale_log2 * kscale * qinv_d;
       float x[4];
       float mx = -INFINITY;
       const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
@@ -823,7 +796,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (KV == KV_U8Z)
-          x[i] = (sv[i] - __builtin_fmaf((float)((kzw >> (8 * i)) & 0xFFu), qsum, qoff)) *
+          // sum u (c - z) = sum u (c - 128) + (128 - z) sum u, all in int32
+          x[i] = (float)(sk[i] + (128 - (int)((kzw >> (8 * i)) & 0xFFu)) * qsum_i) *
                  (cb * ks4[i]);
         else
           x[i] = sv[i] * cb;
