@@ -32,6 +32,7 @@ from __future__ import annotations
 import argparse
 import dataclasses
 import hashlib
+import re
 import json
 import math
 import os
@@ -124,11 +125,24 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def kernel_source_hash() -> str:
+def code_only(text: str) -> str:
+    """C++ source without comments and blank lines: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the attention kernels' code (comments left out, so counters
+    recorded on a source stay valid across edits of its comments)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel)) as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -19,13 +19,17 @@
 //      the partition's block-table entries are loaded once, 64 per vector
 //      load, and broadcast from a lane, so no table read sits in front of a
 //      tile load;
-//   2. 8-bit codes are widened to bf16 (exact; INT8 and uint8 K codes to fp16
-//      1024 + u, also exact, for an fp16 QK^T), then both tiles are written to
-//      LDS with the 16-byte chunks of row t XOR-swizzled by t, so the
-//      row-per-lane and column-per-lane reads below are free of bank conflicts;
+//   2. V codes are widened to bf16 (exact; INT8 V codes to fp16 1024 + u, also
+//      exact), then the tiles are written to LDS with the 16-byte chunks of
+//      row t XOR-swizzled by t, so the row-per-lane and column-per-lane reads
+//      below are free of bank conflicts; 8- and 4-bit K codes are not widened
+//      (step 3);
 //   3. S = K q^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = K rows
 //      (token m = lane % 16) and B = the group's queries (head n = lane % 16,
-//      zero for n >= G), D/32 instructions;
+//      zero for n >= G), D/32 instructions; E4M3 and E2M1 K codes go straight
+//      into v_mfma_scale_f32_16x16x128_f8f6f4, INT8 and uint8 K codes into
+//      v_mfma_i32_16x16x64_i8, against the query split into a high and a low
+//      part in the same format (two or four instructions for D = 128);
 //   4. online softmax in base 2: S is scaled by scale*log2(e) (times the
 //      block's K scale for 8-bit KV), masked past L by selection, the block
 //      maximum per head is shuffled across the four lanes holding that head,
@@ -36,10 +40,9 @@
 //      (4 consecutive tokens per lane, head = lane % 16); V^T comes from the
 //      row-major LDS tile through gfx950's transposing LDS read (one 8-byte
 //      read per instruction instead of four 2-byte ones); for 8-bit KV, P is
-//      multiplied by the block's V scale first.  INT8 K and V codes (and
-//      uint8 K codes) take an fp16 route instead: a byte permute makes two fp16
-//      values 1024 + u at a time, and the products run on the fp16 MFMAs (see
-//      widen16_k16).
+//      multiplied by the block's V scale first.  INT8 V codes take an fp16
+//      route instead: a byte permute makes two fp16 values 1024 + u at a time,
+//      and P V runs on the fp16 MFMA (see widen16_k16).
 // Asymmetric per-row pools (value = (code - zero) * scale for each row) run
 // the matrix cores on the raw codes: row t's logit is
 // scale_t * (q . code_t - zero_t * sum(q)) and the output is
@@ -164,9 +167,8 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // most 8 significant bits, so its binary32 upper half is u in bf16 exactly.
 // The kernel subtracts the offset afterwards: 128 * sum(p) from each output
 // column.  Asymmetric uint8 codes are widened the same way without the flip.
-// (This widening serves V; INT8 and uint8 K codes take the cheaper fp16 route
-// of widen16_k16, because QK^T may run in fp16 where P V may not: P carries
-// the block's V scale, which fp16's range cannot hold in general.)
+// (This widening serves the V codes of E4M3 and uint8 pools; INT8 V codes take
+// the cheaper fp16 route of widen16_k16, and K codes are not widened.)
 template <int KV>
 __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
   const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
@@ -193,11 +195,10 @@ __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
   hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
-// 16 INT8 or uint8 K codes -> 16 fp16 values 1024 + u, exact (u = c + 128
-// for INT8, the raw code for uint8): fp16 1024 has the bits 0x6400 and a unit
-// in the last place of 1, so a byte permute that puts code u under the byte
-// 0x64 makes 1024 + u, two codes per permute.  The logit takes the
-// (1024 + offset) * sum(q) back off.
+// 16 INT8 V codes -> 16 fp16 values 1024 + u with u = c + 128, exact: fp16
+// 1024 has the bits 0x6400 and a unit in the last place of 1, so a byte
+// permute that puts code u under the byte 0x64 makes 1024 + u, two codes per
+// permute.  The output takes (1024 + 128) * sum(P) back off.
 template <int KV>
 __device__ __forceinline__ void widen16_k16(u32x4 c, u32x4& lo, u32x4& hi) {
   constexpr uint32_t kExp = 0x64646464u;

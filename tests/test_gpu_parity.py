@@ -1526,3 +1526,43 @@ def test_decode_step_per_tile_quant_full_size(dtype):
                         k_scale=ks, v_scale=vs)
     err = _cmp(_out_np(out), ref, TOL[dtype], f"{dtype} full step")
     _record(f"decode step/{wl.name}/{dtype} append/blocks layout/split -1", err, TOL[dtype])
+
+
+def test_shared_prefix_partials_bit_identical_on_gpu():
+    """Sequences whose tables share a 2048-token prefix and whose queries are
+    equal: with 512-token partitions the four prefix partitions' partials
+    (maximum, sum, output row) in the workspace are bit-identical across all
+    sequences, and a sequence with no private token equals the prefix-only
+    result.  Checked on the GPU's own workspace."""
+    wl = W.make(5, B=12, suffix_hi=600)
+    lens = wl.lens.copy()
+    lens[3] = 2048                                          # prefix only
+    wl = dataclasses.replace(wl, lens=lens, q=np.repeat(wl.q[:1], wl.B, axis=0))
+    d = W.to_device(wl, layout="blocks")
+    part = 512
+    ws = pkv.alloc_workspace(wl.B, wl.Hq, wl.D, wl.max_blocks, part)
+    out = pkv.attention_decode(_dev_cache(d, wl), d["q"], d["tables"], d["lens"], float(wl.scale),
+                               partition_tokens=part, workspace=ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    R, K = wl.B * wl.Hq, -(-wl.max_blocks * 16 // part)
+    o_bytes = -(-R * K * wl.D * 4 // 256) * 256
+    m_bytes = -(-R * K * 4 // 256) * 256
+    raw = ws.cpu().numpy()
+    o = raw[:R * K * wl.D * 4].view(np.float32).reshape(wl.B, wl.Hq, K, wl.D)
+    m = raw[o_bytes:o_bytes + R * K * 4].view(np.float32).reshape(wl.B, wl.Hq, K)
+    l = raw[o_bytes + m_bytes:o_bytes + m_bytes + R * K * 4].view(np.float32).reshape(wl.B, wl.Hq, K)
+    for s in range(wl.B):
+        if s == 3:
+            continue
+        for p in range(4):                                  # the 2048-token prefix
+            assert np.array_equal(o[s, :, p].view(np.uint32), o[0, :, p].view(np.uint32))
+            assert np.array_equal(m[s, :, p].view(np.uint32), m[0, :, p].view(np.uint32))
+            assert np.array_equal(l[s, :, p].view(np.uint32), l[0, :, p].view(np.uint32))
+    ref = oracle.decode(wl.q, wl.q_dtype, wl.k_pool, wl.v_pool, wl.kv_dtype, wl.tables, wl.lens,
+                        wl.scale)
+    _cmp(_out_np(out), ref, TOL["bf16"], "shared prefix, 512-token partitions")
+    # the prefix-only sequence combines exactly the four shared partials
+    # (the workspace holds maxima in log2 units, the oracle's combine natural ones)
+    mp = oracle.combine_partials(m[:1, :, :4].astype(np.float64) / np.log2(np.e),
+                                 l[:1, :, :4].astype(np.float64), o[:1, :, :4].astype(np.float64))
+    assert np.max(np.abs(_out_np(out)[3] - mp[0])) <= 1e-5
