@@ -518,7 +518,8 @@ def main():
     key = (f"{wl.name}{'_' + wl.quant if wl.quant else ''}/{args.layout}/"
            + (f"prefix{prefix_blocks}" if prefix_blocks > 0 else f"{part}")
            + (f"/tokens{args.tokens}" if args.tokens > 1 else "")
-           + (f"/window{args.window}" if args.window > 0 else ""))
+           + (f"/window{args.window}" if args.window > 0 else "")
+           + ("/append" if wl.write and args.workload == 5 else ""))
     traffic = recorded_traffic(key)
     e_q = {"f32": "f32", "bf16": "bf16"}[wl.q_dtype]
     line = {
