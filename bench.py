@@ -258,6 +258,9 @@ def cpu_baseline(wl, budget_s=10.0):
             if wl.quant == "u8z":
                 oracle.cache_write_quant(k, v, ks, vs, kz, vz, wl.k_new, wl.v_new,
                                          wl.kv_dtype, slots)
+            elif wl.quant:
+                oracle.cache_write_sym(k, v, ks, vs, wl.quant, wl.k_new, wl.v_new,
+                                       wl.kv_dtype, slots)
             else:
                 oracle.cache_write(k, v, wl.kv_dtype, wl.k_new, wl.v_new, slots)
         oracle.decode(wl.q, wl.q_dtype, k, v, kvd, wl.tables, wl.lens, wl.scale,
@@ -394,10 +397,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=(1, 2, 3, 4, 5))
     ap.add_argument("--quant", choices=("i8", "fp8", "u8z", "fp4"), default=None,
-                    help="quantized pool format: for the quantized-prefix workload (5; default "
-                         "i8) i8, fp8, u8z (asymmetric per-row uint8) or fp4 (E2M1); for the "
-                         "decode-step workloads (2-4) u8z, whose step then appends the new "
-                         "token quantized")
+                    help="quantized pool format: i8, fp8 (E4M3), fp4 (E2M1), each with a "
+                         "scale per (block, KV head), or u8z (asymmetric per-row uint8); the "
+                         "quantized-prefix workload (5) defaults to i8, and on the decode-step "
+                         "workloads (2-4) the pool is quantized once and the step appends the "
+                         "new token quantized")
     ap.add_argument("--replicas", type=int, default=0,
                     help="input copies cycled through (0: enough for 1.3 GB of pools)")
     ap.add_argument("--partition", type=int, default=None,
@@ -447,13 +451,10 @@ def main():
         extra = dict(write=True, suffix_lo=1) if args.append else {}
         wl = W.make(5, quant=args.quant or "i8", **extra)
     else:
-        if args.quant not in (None, "u8z"):
-            sys.exit("--quant for workloads 1-4 must be u8z (only that format takes a "
-                     "quantized append)")
         wl = W.make(args.workload)
         if args.quant:
             if wl.kv_dtype != "bf16":
-                sys.exit("--quant u8z needs a bf16 workload (2-4)")
+                sys.exit("--quant needs a bf16 workload (2-4)")
             wl = dataclasses.replace(wl, quant=args.quant)
     part = args.partition if args.partition is not None else pkv.default_partition(
         wl.B, wl.Hkv, wl.max_blocks)

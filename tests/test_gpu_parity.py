@@ -1528,6 +1528,34 @@ def test_decode_step_per_tile_quant_full_size(dtype):
     _record(f"decode step/{wl.name}/{dtype} append/blocks layout/split -1", err, TOL[dtype])
 
 
+@pytest.mark.parametrize("cfg,dtype", [(2, "i8"), (2, "fp8"), (2, "fp4"), (3, "fp8")])
+def test_decode_step_per_tile_quant_llama_shapes(cfg, dtype):
+    """Full-size decode step on the Llama-3-8B / 70B shapes over an INT8 /
+    E4M3 / E2M1 pool quantized once: the new token of every sequence is
+    appended into its tile (scale growth where needed), pool bytes and scales
+    bit-exact, every output row within 2e-2 of the oracle."""
+    wl = W.make(cfg)
+    _say(f"decode step {dtype} full: {wl.name} B={wl.B} NB={wl.num_blocks}")
+    d = W.to_device(wl, layout="blocks")
+    qc = _qcache(dtype, wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
+    pkv.quantize(_dev_cache(d, wl), qc)
+    out = pkv.decode_step(qc, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"],
+                          float(wl.scale), partition_tokens=-1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kc, ks = oracle.quantize(wl.k_pool, wl.kv_dtype, dtype)
+    vc, vs = oracle.quantize(wl.v_pool, wl.kv_dtype, dtype)
+    oracle.cache_write_sym(kc, vc, ks, vs, dtype, wl.k_new, wl.v_new, wl.kv_dtype,
+                           oracle.slot_mapping(wl.tables, wl.lens))
+    assert np.array_equal(W.from_device(qc.k_cache), kc)
+    assert np.array_equal(W.from_device(qc.v_cache), vc)
+    assert np.array_equal(qc.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(qc.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    ref = oracle.decode(wl.q, wl.q_dtype, kc, vc, dtype, wl.tables, wl.lens, wl.scale,
+                        k_scale=ks, v_scale=vs)
+    err = _cmp(_out_np(out), ref, TOL[dtype], f"{dtype} full step {wl.name}")
+    _record(f"decode step/{wl.name}/{dtype} append/blocks layout/split -1", err, TOL[dtype])
+
+
 def test_shared_prefix_partials_bit_identical_on_gpu():
     """Sequences whose tables share a 2048-token prefix and whose queries are
     equal: with 512-token partitions the four prefix partitions' partials
