@@ -127,10 +127,12 @@ __device__ __forceinline__ u32x4 buffer_load16_kv(rsrc_t r, int off) {
 // per sequence (column n = head n of the group); several tokens that fit one
 // pass (k * G <= 16 columns: column n = head n % G of token n / G); several
 // passes, whose wavefronts for one (range, KV head) run side by side and share
-// the tiles through L2 (balanced split only); and several sequences whose
+// the tiles through L2 (balanced split only); several sequences whose
 // tables share the range's blocks (a common prefix: column n = head n % G of
-// sequence s + n / G), so a shared block is staged once for all of them.
-enum { kMqOne = 0, kMqPass = 1, kMqPasses = 2, kMqSeqs = 3 };
+// sequence s + n / G), so a shared block is staged once for all of them; and
+// two 16-column groups in one wavefront (k * G <= 32, balanced split), whose
+// tiles are loaded, staged and read from LDS once for both groups.
+enum { kMqOne = 0, kMqPass = 1, kMqPasses = 2, kMqSeqs = 3, kMqPair = 4 };
 
 // Columns of a shared-prefix segment (MQ == kMqSeqs): sequences s .. s +
 // nseq - 1 take columns [0, nseq * G); lcol is the context length of this
@@ -369,26 +371,41 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // column n of S, P and O: query token ti (several per sequence only in the
   // token modes), sequence s_col (several only for a shared prefix) and head
   // h of the group
-  constexpr bool kTok = MQ == kMqPass || MQ == kMqPasses;
+  constexpr bool kTok = MQ == kMqPass || MQ == kMqPasses || MQ == kMqPair;
   constexpr bool kSeqs = MQ == kMqSeqs;
-  const int ti = kTok ? tok0 + n / G : 0;
+  // 16-column groups of this wavefront: group c takes the query tokens
+  // tok0 + c * tok_per_pass ..; the tiles are shared by the groups
+  constexpr int CG = MQ == kMqPair ? 2 : 1;
   const int s_col = kSeqs ? s + n / G : s;
   const int h = g * G + (MQ != kMqOne ? n % G : n);
-  const bool has_head = kTok ? (n < G * a.tok_per_pass && ti < a.ntok)
-                             : kSeqs ? n < G * sc.nseq : n < G;
-  const size_t out_row = kTok ? ((size_t)s * a.ntok + ti) * hq + h : (size_t)s_col * hq + h;
+  int ti[CG];
+  bool has_head[CG];
+  size_t out_row[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    ti[c] = kTok ? tok0 + c * a.tok_per_pass + n / G : 0;
+    has_head[c] = kTok ? (n < G * a.tok_per_pass && ti[c] < a.ntok)
+                       : kSeqs ? n < G * sc.nseq : n < G;
+    out_row[c] = kTok ? ((size_t)s * a.ntok + ti[c]) * hq + h : (size_t)s_col * hq + h;
+  }
   // last key position + 1 this column may see (causal within the chunk, or
   // its own sequence's length), and with a window the first one (lo_col), and
   // the lowest first position of all columns of this pass (lo_seg): V rows
   // below it are zeroed in LDS
-  const int lim = kTok ? L - a.ntok + ti + 1 : kSeqs ? sc.lcol : L;
   constexpr int kNoLo = -(1 << 30);
-  const int lo_col = a.window > 0 ? lim - a.window : kNoLo;
+  int lim[CG], lo_col[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    lim[c] = kTok ? L - a.ntok + ti[c] + 1 : kSeqs ? sc.lcol : L;
+    lo_col[c] = a.window > 0 ? lim[c] - a.window : kNoLo;
+  }
   const int lo_seg = a.window > 0 ? (kTok ? L - a.ntok + tok0 + 1 : L) - a.window : kNoLo;
 
-  f32x4 acc[kNT];
+  f32x4 acc[CG][kNT];
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // queries of this group as the B operand of S = K q^T: lane (j, n) holds
   // q[h][32 kk + 8 j .. + 8] for each kk
@@ -400,9 +417,10 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // (taken from an in-bounds probe of the instruction), so B lane group j
   // holds q[16 j ..] and q[64 + 16 j ..]; past head_dim the values are 0.
   constexpr int kQV = kDirectK ? 4 : kNKK;
-  bf16x8 qop[kQV];
-  {
-    const uint16_t* qrow = a.q + (has_head ? out_row : (size_t)s * a.ntok * hq) * D;
+  bf16x8 qop[CG][kQV];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const uint16_t* qrow = a.q + (has_head[c] ? out_row[c] : (size_t)s * a.ntok * hq) * D;
 #pragma unroll
     for (int kk = 0; kk < kQV; ++kk) {
       int off = 32 * kk + 8 * j;
@@ -410,7 +428,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       if constexpr (KV == KV_FP4) off = kk < 2 ? 16 * j + 8 * kk : 64 + 16 * j + 8 * (kk - 2);
       bf16x8 v = {};
       if (!kDirectK || off < D) v = *reinterpret_cast<const bf16x8*>(qrow + off);
-      qop[kk] = has_head ? v : bf16x8{};
+      qop[c][kk] = has_head[c] ? v : bf16x8{};
     }
   }
   // Direct K: the queries, scaled per head by 2^qe, split into two operands
@@ -421,40 +439,44 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // integer u = 128 hi + lo with hi = (u + 64) >> 7 and lo in [-64, 63], both
   // int8, 13 bits in all, and the two integer products are exact.  The logit
   // multiplies by 2^-qe.
-  i32x8 qhi8 = {}, qlo8 = {};
-  float qinv_d = 1.f;
-  int qsum_i = 0;   // per-row uint8: sum of this lane's integer queries u
+  i32x8 qhi8[CG] = {}, qlo8[CG] = {};
+  float qinv_d[CG];
+  int qsum_i[CG];   // per-row uint8: sum of this lane's integer queries u
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+  qinv_d[c] = 1.f;
+  qsum_i[c] = 0;
   if constexpr (kDirectK) {
     float mq = 0.f;
 #pragma unroll
     for (int kk = 0; kk < kQV; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(static_cast<float>(qop[kk][e])));
+      for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(static_cast<float>(qop[c][kk][e])));
     mq = rows_max(mq);
     constexpr int kTop = kIntK ? 13 : 8;
     const int qe = mq > 0.f ? kTop - __builtin_amdgcn_frexp_expf(mq) : 0;
-    qinv_d = __builtin_ldexpf(1.f, -qe);
+    qinv_d[c] = __builtin_ldexpf(1.f, -qe);
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * w + e;   // byte v of the operand
-        y[e] = __builtin_ldexpf(static_cast<float>(qop[v / 8][v % 8]), qe);
+        y[e] = __builtin_ldexpf(static_cast<float>(qop[c][v / 8][v % 8]), qe);
       }
       if constexpr (kIntK) {
         uint32_t hw = 0, lw = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int u = (int)rintf(y[e]);
-          qsum_i += u;
+          qsum_i[c] += u;
           const int hi = (u + 64) >> 7;
           const int lo = u - (hi << 7);
           hw |= (uint32_t)(uint8_t)(int8_t)hi << (8 * e);
           lw |= (uint32_t)(uint8_t)(int8_t)lo << (8 * e);
         }
-        qhi8[w] = (int)hw;
-        qlo8[w] = (int)lw;
+        qhi8[c][w] = (int)hw;
+        qlo8[c][w] = (int)lw;
       } else {
         s16x2 h = {0, 0};
         h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, y[0], y[1], 1.0f, false);
@@ -466,14 +488,15 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, y[0] - d01[0], y[1] - d01[1], 1.0f,
                                                       false);
         l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, y[2] - d23[0], y[3] - d23[1], 1.0f, true);
-        qhi8[w] = (int)hw;
-        qlo8[w] = __builtin_bit_cast(int, l);
+        qhi8[c][w] = (int)hw;
+        qlo8[c][w] = __builtin_bit_cast(int, l);
       }
     }
   }
   // per-row uint8: the integer queries' sum over the head (exact: at most
   // 128 * 2^13 in magnitude)
-  if constexpr (KV == KV_U8Z) qsum_i = (int)rows_sum((float)qsum_i);
+  if constexpr (KV == KV_U8Z) qsum_i[c] = (int)rows_sum((float)qsum_i[c]);
+  }
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = a.blk_stride;
@@ -501,8 +524,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
     }
   }
 
-  float m = kNoMax;   // running reference maximum (log2 units)
-  float lsum = 0.f;   // this lane's share of the softmax denominator
+  float m[CG], lsum[CG], psum[CG];   // running reference maximum (log2 units); this
+                                     // lane's share of the softmax denominator
   // INT8: V codes enter P V as fp16 1024 + u too, and P, which carries the
   // block's V scale, as fp16.  To keep P finite it carries the V scale times
   // vfac = 2^-E, chosen per 64-block chunk so that the chunk's largest V scale
@@ -511,8 +534,14 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   // divided by vfac at the end.
   constexpr bool kV16 = KV == KV_I8;
   float vfac = 0.f;
-  float psum = 0.f;   // INT8: this lane's share of sum(P), rescaled like the accumulator;
-                      // asymmetric rows: of sum_t P_t zero_t, likewise
+  // psum: INT8: this lane's share of sum(P), rescaled like the accumulator;
+  // asymmetric rows: of sum_t P_t zero_t, likewise
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    m[c] = kNoMax;
+    lsum[c] = 0.f;
+    psum[c] = 0.f;
+  }
 
   // The range is walked in chunks of up to 64 blocks.  Per chunk, lane i
   // loads block-table entry i (and, for 8-bit KV, that block's two scales);
@@ -540,8 +569,11 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         if (vfac > 0.f) {
           const float r = f / vfac;
 #pragma unroll
-          for (int t = 0; t < kNT; ++t) acc[t] *= r;
-          psum *= r;
+          for (int c = 0; c < CG; ++c) {
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) acc[c][t] *= r;
+            psum[c] *= r;
+          }
         }
         vfac = f;
       }
@@ -729,15 +761,19 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       load_tile(kr, vr, pr, ph, b + NST);
 
       // ---- S = K q^T: lane (j, n) gets S[token 4j + i][head n]
+      f32x4 svc[CG];
+      int skc[CG][4];   // integer products (INT8, uint8)
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
       f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-      int sk[4] = {0, 0, 0, 0};   // integer products (INT8, uint8)
+      int sk[4] = {0, 0, 0, 0};
       if constexpr (kIntK) {
         typedef int i32x4 __attribute__((ext_vector_type(4)));
         const i32x4 a0 = {ka[0], ka[1], ka[2], ka[3]}, a1 = {ka[4], ka[5], ka[6], ka[7]};
-        const i32x4 h0 = {qhi8[0], qhi8[1], qhi8[2], qhi8[3]};
-        const i32x4 h1 = {qhi8[4], qhi8[5], qhi8[6], qhi8[7]};
-        const i32x4 l0 = {qlo8[0], qlo8[1], qlo8[2], qlo8[3]};
-        const i32x4 l1 = {qlo8[4], qlo8[5], qlo8[6], qlo8[7]};
+        const i32x4 h0 = {qhi8[c][0], qhi8[c][1], qhi8[c][2], qhi8[c][3]};
+        const i32x4 h1 = {qhi8[c][4], qhi8[c][5], qhi8[c][6], qhi8[c][7]};
+        const i32x4 l0 = {qlo8[c][0], qlo8[c][1], qlo8[c][2], qlo8[c][3]};
+        const i32x4 l1 = {qlo8[c][4], qlo8[c][5], qlo8[c][6], qlo8[c][7]};
         i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
         ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, h0, ah, 0, 0, 0);
         ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, h1, ah, 0, 0, 0);
@@ -751,15 +787,19 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         }
       } else if constexpr (kDirectK) {
         constexpr int kFmtA = KV == KV_FP8 ? 0 : 4;   // A operand: E4M3 or E2M1 codes
-        sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi8, sv, kFmtA, 0, 0, 127, 0,
-                                                              127);
-        sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo8, sv, kFmtA, 0, 0, 127, 0,
-                                                              127);
+        sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi8[c], sv, kFmtA, 0, 0, 127,
+                                                              0, 127);
+        sv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo8[c], sv, kFmtA, 0, 0, 127,
+                                                              0, 127);
       }
 #pragma unroll
       for (int kk = 0; kk < (kDirectK ? 0 : kNKK); ++kk) {
         const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D, KV>(n, 4 * kk + j));
-        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sv, 0, 0, 0);
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c][kk], sv, 0, 0, 0);
+      }
+      svc[c] = sv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) skc[c][i] = sk[i];
       }
 
       // ---- V^T operands of O^T += V^T P, read now so that their LDS latency
@@ -782,12 +822,16 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         }
       }
 
-      // ---- online softmax (base 2)
-      const float cb = a.scale_log2 * kscale * qinv_d;
+      // ---- online softmax (base 2), then PV, per column group
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+      const f32x4 sv = svc[c];
+      const int* sk = skc[c];
+      const float cb = a.scale_log2 * kscale * qinv_d[c];
       float x[4];
       float mx = -INFINITY;
-      const int vcol = MQ ? (cur_ok ? min(kBlock, lim - b * kBlock) : 0) : valid;
-      const int vmin = lo_col - b * kBlock;   // this column's first row in its window
+      const int vcol = MQ ? (cur_ok ? min(kBlock, lim[c] - b * kBlock) : 0) : valid;
+      const int vmin = lo_col[c] - b * kBlock;   // this column's first row in its window
       // one query token per sequence: every row of a block is in range for
       // every column unless the block is the last (or, with a window, the
       // first) of the sequence, so the per-row selects are skipped; a shared
@@ -798,7 +842,7 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       for (int i = 0; i < 4; ++i) {
         if constexpr (KV == KV_U8Z)
           // sum u (c - z) = sum u (c - 128) + (128 - z) sum u, all in int32
-          x[i] = (float)(sk[i] + (128 - (int)((kzw >> (8 * i)) & 0xFFu)) * qsum_i) *
+          x[i] = (float)(sk[i] + (128 - (int)((kzw >> (8 * i)) & 0xFFu)) * qsum_i[c]) *
                  (cb * ks4[i]);
         else
           x[i] = sv[i] * cb;
@@ -811,21 +855,21 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
       mx = rows_max(mx);
-      const bool bump = mx > m + kRescaleSlack;
+      const bool bump = mx > m[c] + kRescaleSlack;
       if (__any(bump)) {
-        const float mnew = bump ? mx : m;
-        const float alpha = exp2_weight(m - mnew);
-        lsum *= alpha;
-        if constexpr (KV == KV_I8 || KV == KV_U8Z) psum *= alpha;
+        const float mnew = bump ? mx : m[c];
+        const float alpha = exp2_weight(m[c] - mnew);
+        lsum[c] *= alpha;
+        if constexpr (KV == KV_I8 || KV == KV_U8Z) psum[c] *= alpha;
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) acc[t] *= alpha;
-        m = mnew;
+        for (int t = 0; t < kNT; ++t) acc[c][t] *= alpha;
+        m[c] = mnew;
       }
       f32x4 pw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pe = exp2_weight(x[i] - m);
-        lsum += pe;
+        const float pe = exp2_weight(x[i] - m[c]);
+        lsum[c] += pe;
         if constexpr (KV == KV_U8Z)   // rows past the end have p = 0 but may hold any scale
           pw[i] = full || (4 * j + i < vcol && 4 * j + i >= vmin) ? pe * vs4[i] : 0.f;
         else
@@ -838,24 +882,25 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
             f16x4, __builtin_shufflevector(__builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]),
                                            __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]), 0, 1, 2, 3));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) psum += static_cast<float>(poh[i]);
+        for (int i = 0; i < 4; ++i) psum[c] += static_cast<float>(poh[i]);
         // ---- O^T += V^T P
 #pragma unroll
         for (int t = 0; t < kNT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt[t]), poh,
-                                                        acc[t], 0, 0, 0);
+          acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt[t]), poh,
+                                                           acc[c][t], 0, 0, 0);
       } else {
         const bf16x4 pop = __builtin_convertvector(pw, bf16x4);   // two paired conversions
         if constexpr (KV == KV_U8Z) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            psum += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
+            psum[c] += static_cast<float>(pop[i]) * (float)((vzw >> (8 * i)) & 0xFFu);
         }
         // ---- O^T += V^T P
 #pragma unroll
         for (int t = 0; t < kNT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vt[t]),
-                                                            pop, acc[t], 0, 0, 0);
+          acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(bf16x4, vt[t]), pop, acc[c][t], 0, 0, 0);
+      }
       }
     };
 
@@ -875,32 +920,35 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
   }
 
   // ---- epilogue: lane (j, n) holds O^T[16 t + 4 j + i][n]
-  const float lt = rows_sum(lsum);
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+  const float lt = rows_sum(lsum[c]);
   if constexpr (KV == KV_I8 || KV == KV_U8Z) {
     // INT8 V codes entered as fp16 1024 + (c + 128): take 1152 * sum(P) off
     // every output row; asymmetric rows: take sum_t P_t zero_t off
-    const float pt = rows_sum(psum);
+    const float pt = rows_sum(psum[c]);
     const float voff = KV == KV_I8 ? 1152.f * pt : pt;
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) acc[t] -= voff;
+    for (int t = 0; t < kNT; ++t) acc[c][t] -= voff;
   }
   // a column that saw no key (a query token before the start, or a piece
   // past its causal limit) has lt == 0: zero output, zero weight
   const float inv = lt > 0.f ? (kV16 ? 1.0f / (lt * vfac) : 1.0f / lt) : 0.f;
-  if (!has_head) return;
+  if (!has_head[c]) continue;
   if (whole) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
-      store_out4<D, OUT>(a.out, out_row * D + 16 * t + 4 * j, acc[t] * inv);
+      store_out4<D, OUT>(a.out, out_row[c] * D + 16 * t + 4 * j, acc[c][t] * inv);
   } else {
-    const size_t row = out_row * a.kstride + slot;
+    const size_t row = out_row[c] * a.kstride + slot;
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
-      *reinterpret_cast<f32x4*>(a.ws_o + row * D + 16 * t + 4 * j) = acc[t] * inv;
+      *reinterpret_cast<f32x4*>(a.ws_o + row * D + 16 * t + 4 * j) = acc[c][t] * inv;
     if (j == 0) {
-      a.ws_m[row] = m;
+      a.ws_m[row] = m[c];
       a.ws_l[row] = lt;
     }
+  }
   }
 }
 
@@ -949,12 +997,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 // its fp16 P V it needs 170 registers and would otherwise drop to two
 // (measured on the shared-prefix INT8 workload: 91.8 us at two, 87.4 us at
 // three, where two registers are spilled: one 8-byte scratch store and
-// reload per two blocks).
+// reload per two blocks).  Two column groups per wavefront (kMqPair) need
+// about 350 registers and run one wavefront per SIMD.
 constexpr int kBalStages = 2;
 constexpr int kBalWaves = 2;
 template <int D, int KV, int OUT, int MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
-    KV == KV_I8 && !MQ ? 3 : kBalWaves))) void
+    MQ == kMqPair ? 1 : KV == KV_I8 && !MQ ? 3 : kBalWaves))) void
 decode_mfma_balanced_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * D * 2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[kBlock * D * 2];
@@ -964,13 +1013,14 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   // the range.  The passes of one (range, KV head) are launched side by side
   // and land on the same XCD, so a later pass finds the tiles the first one
   // fetched in that XCD's L2.
-  const int passes = (a.ntok + a.tok_per_pass - 1) / a.tok_per_pass;
+  const int tok_wave = MQ == kMqPair ? 2 * a.tok_per_pass : a.tok_per_pass;
+  const int passes = (a.ntok + tok_wave - 1) / tok_wave;
   const int g = blockIdx.x % a.hkv;
   const int pass = (blockIdx.x / a.hkv) % passes;
   const int v = blockIdx.x / (a.hkv * passes);
   const int V = gridDim.x / (a.hkv * passes);
   const int B = a.num_seqs;
-  const int tok0 = pass * a.tok_per_pass;
+  const int tok0 = pass * tok_wave;
 
   // The lengths of the first kLenChunks * 64 sequences are loaded once, all
   // at the same time, and kept in registers for both passes and the walk.
@@ -1012,6 +1062,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
         const int e = __ffsll((unsigned long long)empty) - 1;
         empty &= empty - 1;
         zero_rows<D, OUT>(a, base + e, g, tok0);
+        if (MQ == kMqPair) zero_rows<D, OUT>(a, base + e, g, tok0 + a.tok_per_pass);
       }
     }
   }
@@ -1623,15 +1674,32 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
       dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts), (unsigned)pl.passes);
       return launch(fixed_kernel, grid, block, st, m, pl.n_parts);
     };
-    // multi-pass launches of the balanced split get the cached-load kernel;
-    // the fixed split launches its passes as separate grid rows, which do not
-    // run side by side, so it keeps the streaming one
-    const int mq = a.ntok <= 1 ? kMqOne : (pl.balanced && pl.passes > 1 ? kMqPasses : kMqPass);
+    // two passes' worth of columns (k * G <= 32) go to one wavefront in the
+    // balanced split; more passes get the cached-load kernel, whose passes
+    // run side by side; the fixed split launches its passes as separate grid
+    // rows, which do not run side by side, so it keeps the streaming one
+    const int mq = a.ntok <= 1                       ? kMqOne
+                   : pl.balanced && pl.passes == 2 ? kMqPair
+                   : pl.balanced && pl.passes > 1  ? kMqPasses
+                                                   : kMqPass;
     auto by_kv = [&](auto kv) {
       constexpr int KV = decltype(kv)::value;
       if (a.prefix_blocks >= 0) {
         // shared-prefix split: one generation of wavefronts, as the balanced split
         auto kernel = decode_mfma_prefix_kernel<D, KV, OUT>;
+        const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(kernel));
+        if (per_cu <= 0) return (int)PKV_ERR_HIP;
+        const int64_t waves = (int64_t)pl.cus * per_cu;
+        ranges = (waves + hkv - 1) / hkv;
+        return launch(kernel, dim3((unsigned)(ranges * hkv)), block, st, m);
+      }
+      if (mq == kMqPair) {
+        // two column groups per wavefront: one wavefront per SIMD for D = 128
+        // (352 registers for bf16, accumulators in AGPRs), one generation.
+        // 8B shape, 8 query tokens: 145.7 us in two passes, 129.1 us; 70B
+        // shape, 4 tokens: 468.7 -> 433.4 us.  Half a generation: 141.9 and
+        // 482.9 us; three blocks in flight: 131.6 and 439.9 us.
+        auto kernel = decode_mfma_balanced_kernel<D, KV, OUT, kMqPair>;
         const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(kernel));
         if (per_cu <= 0) return (int)PKV_ERR_HIP;
         const int64_t waves = (int64_t)pl.cus * per_cu;

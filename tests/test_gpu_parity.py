@@ -815,9 +815,12 @@ MQ_CASES = [
     (5, dict(B=8, prefix=128, suffix_hi=200), 4, -1, "blocks", "u8z"),
     (5, dict(B=8, prefix=128, suffix_hi=200), 1, 0, "split", "u8z"),
     (5, dict(B=8, prefix=128, suffix_hi=200), 4, -1, "blocks", "fp4"),
-    # balanced split with several passes (their wavefronts run side by side
-    # and load the tiles without the non-temporal hint)
-    (3, dict(B=12, median=200, lo=1, hi=700), 4, -1, "blocks", None),  # G = 8, 2 passes
+    # balanced split past 16 columns: up to 32 in one wavefront (two column
+    # groups sharing the tiles), more as passes whose wavefronts run side by
+    # side and load the tiles without the non-temporal hint
+    (3, dict(B=12, median=200, lo=1, hi=700), 4, -1, "blocks", None),  # G = 8, 32 columns
+    (2, dict(B=6, lens=[0, 1, 3, 16, 17, 300], hi=300, pool=100), 8, -1, "blocks", None),
+    (2, dict(B=4, lo=1, hi=400, pool=200, D=64), 8, -1, "split", None),           # D = 64
     (2, dict(B=4, lo=1, hi=300, pool=200, Hq=8, Hkv=8), 40, -1, "split", None),   # 3 passes
     (5, dict(B=8, prefix=128, suffix_hi=200), 6, -1, "blocks", "i8"),
     (5, dict(B=8, prefix=128, suffix_hi=200), 5, -1, "split", "fp8"),
@@ -1090,6 +1093,8 @@ WINDOW_CASES = [
     (2, dict(B=7, lens=[1, 16, 17, 33, 0, 600, 255], hi=600, pool=300), 1, 100, 64, "split", None),
     (2, dict(B=9, lo=1, hi=700, pool=600), 1, 256, -1, "blocks", None),
     (2, dict(B=9, lo=1, hi=700, pool=600), 4, 33, -1, "blocks", None),
+    (2, dict(B=9, lo=1, hi=700, pool=600), 8, 100, -1, "blocks", None),     # 32 columns
+    (3, dict(B=24, median=300, lo=1, hi=1000), 4, 50, -1, "split", None),   # G = 8, 32 columns
     (2, dict(B=9, lo=1, hi=700, pool=600), 7, 130, 128, "split", None),
     (3, dict(B=24, median=300, lo=1, hi=1000), 1, 200, -1, "blocks", None),    # G = 8
     (3, dict(B=24, median=300, lo=1, hi=1000), 3, 64, 0, "split", None),
