@@ -566,7 +566,7 @@ def main():
         "bytes_per_step": ab["step"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic, "traffic_key": key,
                      "kernel": "the step's kernels (decode attention, then the combine)",
                      "bytes_per_launch": ab["step"]},
     }
