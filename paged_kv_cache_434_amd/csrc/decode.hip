@@ -79,6 +79,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));   // the packed conversion's type
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 // native clang vector (HIP's u32x4 is a wrapper struct that can keep arrays of
 // it out of registers)
@@ -745,7 +746,8 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
         for (int e = 0; e < 4; ++e) ka[e] = (int)kr[0][e];
       } else if constexpr (KV == KV_FP8 || kIntK) {
         constexpr int kC = D / 16;
-        if (2 * j < kC) {
+        // (always true for D = 128, where the four lane groups cover the row)
+        if (kC == 8 || 2 * j < kC) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const u32x4 c = *reinterpret_cast<const u32x4*>(
@@ -877,12 +879,14 @@ __device__ __forceinline__ void mfma_segment(const MfmaArgs& a, int s, int g, in
       }
       if constexpr (kV16) {
         // two paired conversions (toward zero: under 2^-10 relative, finer
-        // than bf16 to nearest); sum(P) is taken over the converted values
-        const f16x4 poh = __builtin_bit_cast(
-            f16x4, __builtin_shufflevector(__builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]),
-                                           __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]), 0, 1, 2, 3));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) psum[c] += static_cast<float>(poh[i]);
+        // than bf16 to nearest); sum(P) is taken over the converted values,
+        // two at a time by dot products with (1, 1)
+        const h16x2 p01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
+        const h16x2 p23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
+        const f16x4 poh = __builtin_bit_cast(f16x4, __builtin_shufflevector(p01, p23, 0, 1, 2, 3));
+        const h16x2 kOnes = {(__fp16)1.0f, (__fp16)1.0f};
+        psum[c] = __builtin_amdgcn_fdot2(p01, kOnes, psum[c], false);
+        psum[c] = __builtin_amdgcn_fdot2(p23, kOnes, psum[c], false);
         // ---- O^T += V^T P
 #pragma unroll
         for (int t = 0; t < kNT; ++t)
