@@ -340,10 +340,13 @@ int pkv_decode_step_noalloc(const pkv_cache_t* cache, const void* q, int32_t q_d
  *   workspace: at least pkv_decode_workspace_bytes(num_seqs * tokens_per_seq,
  *     num_q_heads, head_dim, max_blocks_per_seq, partition_tokens) bytes when
  *     that is nonzero.
- * A wavefront covers 16 / G query tokens of one KV head's group at a time
- * (the K/V of a block is read once per such pass); other arguments, splits
- * and dtypes as for pkv_attention_decode, except that fp32 pools are
- * PKV_ERR_UNSUPPORTED here. */
+ * A wavefront takes the query heads of one KV head for 16 / G query tokens
+ * (16 columns of the matrix cores), or with the balanced split up to 32 / G
+ * tokens in two column groups over one staging of each block; more tokens run
+ * in passes of 16 / G whose wavefronts read each block at the same time, so
+ * its K/V comes from HBM once.  Other arguments, splits and dtypes as for
+ * pkv_attention_decode, except that fp32 pools are PKV_ERR_UNSUPPORTED
+ * here. */
 int pkv_attention_multi(const pkv_cache_t* cache, const void* q, int32_t q_dtype,
                         int32_t tokens_per_seq, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,

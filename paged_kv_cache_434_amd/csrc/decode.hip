@@ -163,23 +163,21 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * (D * 2) + ((c ^ (row & (kChunks - 1))) << 4);
 }
 
-// 16 8-bit codes -> 16 bf16 values (two 16-byte chunks), exact.
+// 16 8-bit V codes -> 16 bf16 values (two 16-byte chunks), exact.
 // E4M3: the gfx950 conversion instruction, two codes at a time.
-// INT8: the sign bit is flipped, so code c becomes u = c + 128 in [1, 255];
-// an unsigned byte converts to binary32 in one instruction and u < 256 has at
-// most 8 significant bits, so its binary32 upper half is u in bf16 exactly.
-// The kernel subtracts the offset afterwards: 128 * sum(p) from each output
-// column.  Asymmetric uint8 codes are widened the same way without the flip.
-// (This widening serves the V codes of E4M3 and uint8 pools; INT8 V codes take
-// the cheaper fp16 route of widen16_k16, and K codes are not widened.)
+// Asymmetric uint8: an unsigned byte converts to binary32 in one instruction,
+// and u < 256 has at most 8 significant bits, so its binary32 upper half is u
+// in bf16 exactly.  (INT8 V codes take the cheaper fp16 route of widen16_k16;
+// K codes are not widened.)
 template <int KV>
 __device__ __forceinline__ void widen16(u32x4 c, u32x4& lo, u32x4& hi) {
+  static_assert(KV == KV_FP8 || KV == KV_U8Z, "E4M3 or uint8 codes");
   const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (KV == KV_I8 || KV == KV_U8Z) {
-      const uint32_t u = KV == KV_I8 ? w[i] ^ 0x80808080u : w[i];
+    if constexpr (KV == KV_U8Z) {
+      const uint32_t u = w[i];
       const float f0 = (float)(u & 0xFFu);
       const float f1 = (float)((u >> 8) & 0xFFu);
       const float f2 = (float)((u >> 16) & 0xFFu);
