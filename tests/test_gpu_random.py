@@ -144,3 +144,100 @@ def test_random_config(i):
     assert np.all(np.isfinite(got)), "non-finite output"
     err = np.abs(got - ref).max() if got.size else 0.0
     assert err <= TOL[fmt], f"max err {err:.3e} > {TOL[fmt]:g}"
+
+
+N_BYTE_CASES = 60
+
+
+@pytest.mark.parametrize("i", range(N_BYTE_CASES))
+def test_random_bytes(i):
+    """Byte-exact operations on one random pool, in sequence: quantize a
+    random subset of blocks, then all of them; copy-on-write block copies;
+    an append of one row into each of several distinct blocks (quantized for
+    8- and 4-bit pools, bitwise for bf16); gather in logical order; slot
+    mapping.  The oracle applies the same operations to its own copy, and
+    every byte (codes, scales, zero points, gathered rows, slots) must match."""
+    rng = np.random.default_rng(11000 + i)
+    fmt = ("bf16", "i8", "fp8", "fp4", "u8z")[i % 5]
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 13))
+    layout = str(rng.choice(["split", "blocks"]))
+    lens = [int(rng.choice([0, 1, 15, 16, 17, 33])) if rng.random() < 0.3 else
+            int(rng.integers(0, 500)) for _ in range(B)]
+    print(f"random bytes case {i}: fmt={fmt} Hkv={Hkv} D={D} B={B} layout={layout} lens={lens}",
+          flush=True)
+    wl = W.make(2, seed=500 + i, B=B, lens=lens, hi=max(lens + [1]), pool=None, Hq=Hkv,
+                Hkv=Hkv, D=D)
+    NB = wl.num_blocks
+    d = W.to_device(wl, layout=layout)
+    src = pkv.PagedCache(d["k_pool"], d["v_pool"], "bf16")
+    ks = vs = kz = vz = None
+    if fmt == "bf16":
+        cache = src
+        kc, vc = wl.k_pool.copy(), wl.v_pool.copy()
+    else:
+        cache = _qcache(fmt, NB, Hkv, D, layout == "blocks")
+        # a random subset first: those blocks' codes and parameters match
+        ids = np.sort(rng.choice(NB, size=int(rng.integers(1, NB + 1)), replace=False)).astype(
+            np.int32)
+        pkv.quantize(src, cache, torch.from_numpy(ids).cuda())
+        torch.cuda.synchronize()
+        if fmt == "u8z":
+            sc, ss, sz = oracle.quantize_asym(wl.k_pool, "bf16", block_ids=ids)
+            assert np.array_equal(W.from_device(cache.k_zero)[ids], sz[ids])
+        else:
+            sc, ss = oracle.quantize(wl.k_pool, "bf16", fmt, block_ids=ids)
+        assert np.array_equal(W.from_device(cache.k_cache)[ids], sc[ids])
+        assert np.array_equal(cache.k_scale.cpu().numpy()[ids].view(np.uint32),
+                              ss[ids].view(np.uint32))
+        # then every block
+        pkv.quantize(src, cache)
+        kc, vc, ks, vs, kz, vz = _oracle_pool(wl, fmt)
+    # copy-on-write: distinct destinations, none of them a source
+    n_pairs = int(rng.integers(0, min(8, NB // 2) + 1))
+    perm = rng.permutation(NB)
+    pairs = np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], axis=1).astype(np.int32)
+    if n_pairs:
+        pkv.copy_blocks(cache, torch.from_numpy(pairs).cuda())
+        oracle.copy_blocks(kc, vc, fmt, pairs, k_scale=ks, v_scale=vs, k_zero=kz, v_zero=vz)
+    # one new row into each of several distinct blocks (some slots skipped)
+    n_rows = int(rng.integers(1, min(12, NB) + 1))
+    blocks = rng.choice(NB, size=n_rows, replace=False)
+    slots = (blocks * 16 + rng.integers(0, 16, size=n_rows)).astype(np.int32)
+    slots[rng.random(n_rows) < 0.2] = -1
+    kn = W.to_bf16_bits((rng.standard_normal((n_rows, Hkv, D)) *
+                         rng.choice([0.5, 1.0, 4.0], size=(n_rows, 1, 1))).astype(np.float32))
+    vn = W.to_bf16_bits(rng.standard_normal((n_rows, Hkv, D)).astype(np.float32))
+    kn_d, vn_d = _dev_bf16(kn), _dev_bf16(vn)
+    slots_d = torch.from_numpy(slots).cuda()
+    if fmt == "bf16":
+        pkv.cache_write(cache, kn_d, vn_d, slots_d)
+        oracle.cache_write(kc, vc, "bf16", kn, vn, slots)
+    else:
+        pkv.cache_write_quant(cache, kn_d, vn_d, slots_d)
+        if fmt == "u8z":
+            oracle.cache_write_quant(kc, vc, ks, vs, kz, vz, kn, vn, "bf16", slots)
+        else:
+            oracle.cache_write_sym(kc, vc, ks, vs, fmt, kn, vn, "bf16", slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.from_device(cache.k_cache), kc)
+    assert np.array_equal(W.from_device(cache.v_cache), vc)
+    if ks is not None:
+        assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(cache.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    if kz is not None:
+        assert np.array_equal(W.from_device(cache.k_zero), kz)
+        assert np.array_equal(W.from_device(cache.v_zero), vz)
+    # gather in logical order
+    ko_ref, vo_ref, cu = oracle.gather(kc, vc, fmt, wl.tables, wl.lens)
+    if cu[-1] > 0:
+        ko, vo = pkv.gather(cache, d["tables"], d["lens"], torch.from_numpy(cu).cuda(),
+                            int(cu[-1]))
+        torch.cuda.synchronize()
+        assert np.array_equal(W.from_device(ko), ko_ref)
+        assert np.array_equal(W.from_device(vo), vo_ref)
+    # slot mapping of each sequence's newest position
+    got = pkv.slot_mapping(d["tables"], d["lens"])
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.slot_mapping(wl.tables, wl.lens))
