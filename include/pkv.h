@@ -107,7 +107,9 @@ enum {
  *   k_zero, v_zero: [num_blocks][num_kv_heads][block_size] uint8 zero points,
  *     required for PKV_U8_ZP and ignored otherwise.  Scales and zero points are
  *     dense arrays whatever block_stride is.
- * block_size must be 16 ([KVC] "PagedAttention"); head_dim must be 64 or 128. */
+ * block_size must be 16 ([KVC] "PagedAttention"); head_dim must be 64 or 128;
+ * num_blocks at most INT32_MAX / 16, since slots (block * 16 + row) are
+ * int32 (PKV_ERR_SHAPE otherwise). */
 typedef struct pkv_cache_t {
   int32_t num_blocks;
   int32_t num_kv_heads;

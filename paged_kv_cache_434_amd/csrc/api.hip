@@ -50,8 +50,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_cache(const pkv_cache_t* c) {
   if (!c) return PKV_ERR_NULL;
   if (elem_bits(c->kv_dtype) == 0) return PKV_ERR_DTYPE;
-  if (c->block_size != PKV_BLOCK_SIZE || c->num_blocks < 0 || c->num_kv_heads <= 0 ||
-      c->head_dim <= 0)
+  // slots (block * 16 + row) are 32-bit, so a pool holds at most INT_MAX / 16 blocks
+  if (c->block_size != PKV_BLOCK_SIZE || c->num_blocks < 0 ||
+      c->num_blocks > INT_MAX / PKV_BLOCK_SIZE || c->num_kv_heads <= 0 || c->head_dim <= 0)
     return PKV_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!c->k_cache || !c->v_cache) return PKV_ERR_NULL;

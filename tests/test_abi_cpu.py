@@ -89,6 +89,7 @@ def _decode(cache, q=FAKE, q_dtype=1, tables=FAKE, maxb=4, lens=FAKE, B=2, Hq=4,
     (dict(k_cache=None), 1),
     (dict(kv_dtype=2), 1),               # int8 pool without scales
     (dict(k_cache=FAKE + 8), 6),         # misaligned pool
+    (dict(num_blocks=(2**31 - 1) // 16 + 1), 2),   # slots would not fit 32 bits
 ])
 def test_decode_rejects_bad_cache(kw, status):
     assert _decode(_cache(**kw)) == status
