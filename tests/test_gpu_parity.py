@@ -1292,27 +1292,48 @@ def test_fp4_gather_bit_exact():
     assert np.array_equal(vo.cpu().numpy(), vo_ref)
 
 
-@pytest.mark.parametrize("part", [0, 64, -1])
-def test_decode_step_u8z_equals_append_then_attention(part):
-    """The append fused into the attention launch stores the same bytes as
-    pkv_cache_write_quant and gives the same output as attention after it."""
-    wl = W.make(2, B=9, lens=[1, 15, 16, 17, 32, 33, 300, 0, 511], hi=600, pool=300)
+@pytest.mark.parametrize("quant", ["u8z", "i8", "fp8", "fp4"])
+@pytest.mark.parametrize("part,D", [(0, 128), (64, 128), (-1, 128), (-1, 64), (32, 64)])
+def test_decode_step_quant_equals_append_then_attention(quant, part, D):
+    """pkv_decode_step over a quantized pool stores the same bytes as
+    pkv_cache_write_quant and gives the same output, bit for bit, as
+    attention after it, whichever kernel appends.  Rows at offsets 0, 14, 15
+    and 0 of a new block, an empty sequence and long ones; a second step
+    appends the next position with K rows x3 and V rows x4, so the per-tile
+    scales grow and earlier rows are re-encoded."""
+    wl = W.make(2, B=9, lens=[1, 15, 16, 17, 32, 33, 300, 0, 511], hi=600, pool=300, D=D)
+    _say(f"fused append {quant}: part={part} D={D}")
     d = W.to_device(wl, layout="blocks")
-    qa = _qcache("u8z", wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
-    qb = _qcache("u8z", wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
+    qa = _qcache(quant, wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
+    qb = _qcache(quant, wl.num_blocks, wl.Hkv, 16, wl.D, blocks=True)
     pkv.quantize(_dev_cache(d, wl), qa)
     pkv.quantize(_dev_cache(d, wl), qb)
-    fused = pkv.decode_step(qa, d["q"], d["k_new"], d["v_new"], d["tables"], d["lens"],
-                            float(wl.scale), partition_tokens=part, out_dtype=torch.float32)
-    slots = pkv.slot_mapping(d["tables"], d["lens"])
-    pkv.cache_write_quant(qb, d["k_new"], d["v_new"], slots)
-    sep = pkv.attention_decode(qb, d["q"], d["tables"], d["lens"], float(wl.scale),
-                               partition_tokens=part, out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    for x, y in ((qa.k_cache, qb.k_cache), (qa.v_cache, qb.v_cache), (qa.k_scale, qb.k_scale),
-                 (qa.v_scale, qb.v_scale), (qa.k_zero, qb.k_zero), (qa.v_zero, qb.v_zero)):
-        assert torch.equal(x, y)
-    assert torch.equal(fused, sep)
+    lens = wl.lens.copy()
+    rng = np.random.default_rng(11)
+    for step in range(2):
+        if step:
+            lens = lens + (lens % 16 != 0)   # the next position inside the last block
+            kn = _dev_src(W.to_bf16_bits((rng.standard_normal(wl.k_new.shape) * 3)
+                                         .astype(np.float32)), "bf16")
+            vn = _dev_src(W.to_bf16_bits((rng.standard_normal(wl.v_new.shape) * 4)
+                                         .astype(np.float32)), "bf16")
+        else:
+            kn, vn = d["k_new"], d["v_new"]
+        ld = torch.from_numpy(lens).cuda()
+        fused = pkv.decode_step(qa, d["q"], kn, vn, d["tables"], ld, float(wl.scale),
+                                partition_tokens=part, out_dtype=torch.float32)
+        slots = pkv.slot_mapping(d["tables"], ld)
+        pkv.cache_write_quant(qb, kn, vn, slots)
+        sep = pkv.attention_decode(qb, d["q"], d["tables"], ld, float(wl.scale),
+                                   partition_tokens=part, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        pairs = [(qa.k_cache, qb.k_cache), (qa.v_cache, qb.v_cache), (qa.k_scale, qb.k_scale),
+                 (qa.v_scale, qb.v_scale)]
+        if quant == "u8z":
+            pairs += [(qa.k_zero, qb.k_zero), (qa.v_zero, qb.v_zero)]
+        for x, y in pairs:
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"step {step}"
+        assert torch.equal(fused, sep), f"step {step}"
 
 
 # ------------------------------------------------------------- shared prefix
