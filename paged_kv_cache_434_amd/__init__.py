@@ -265,6 +265,7 @@ def cache_write(cache: PagedCache, k, v, slot_mapping, stream=None):
     n = slot_mapping.shape[0]
     if tuple(k.shape) != (n, cache.num_kv_heads, cache.head_dim) or k.shape != v.shape:
         raise ValueError("k/v must be [n][num_kv_heads][head_dim]")
+    _same_device(k, (("v", v), ("slot_mapping", slot_mapping)) + _cache_tensors(cache))
     _check("pkv_cache_write",
            _load().pkv_cache_write(ctypes.byref(cache.desc), _ptr(k), _ptr(v),
                                    _ptr(slot_mapping), n, _stream(stream)))
@@ -287,6 +288,7 @@ def cache_write_quant(cache: PagedCache, k, v, slot_mapping, stream=None):
     n = slot_mapping.shape[0]
     if tuple(k.shape) != (n, cache.num_kv_heads, cache.head_dim) or k.shape != v.shape:
         raise ValueError("k/v must be [n][num_kv_heads][head_dim]")
+    _same_device(k, (("v", v), ("slot_mapping", slot_mapping)) + _cache_tensors(cache))
     _check("pkv_cache_write_quant",
            _load().pkv_cache_write_quant(ctypes.byref(cache.desc), _ptr(k), _ptr(v),
                                          DTYPE_CODES[sd], _ptr(slot_mapping), n,
@@ -329,9 +331,20 @@ def _check_query_out(cache, q, out, tensors, lead):
         raise ValueError(f"q's leading dims {tuple(q.shape[:-2])} differ from {tuple(lead)}")
     if out is not None and tuple(out.shape) != tuple(q.shape):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q.shape)}")
-    for name, t in tensors:
+    for name, t in tuple(tensors) + _cache_tensors(cache):
         if t is not None and t.device != q.device:
             raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+
+
+def _cache_tensors(cache):
+    names = ("k_cache", "v_cache", "k_scale", "v_scale", "k_zero", "v_zero")
+    return tuple((n, getattr(cache, n, None)) for n in names)
+
+
+def _same_device(ref, tensors):
+    for name, t in tensors:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
 
 
 def _decode_call(cache: PagedCache, q, block_tables, context_lens, scale: float,
@@ -401,7 +414,9 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_tables, context_lens, 
                 partition_tokens: int = 0, workspace=None, out=None, out_dtype=None,
                 stream=None):
     """Append each sequence's new token at position context_lens - 1, then
-    attention over the whole context (one attention launch)."""
+    attention over the whole context.  For bf16 pools the append is part of
+    the attention launch; quantized pools append in a launch of their own
+    first (k_new / v_new then come in q's dtype)."""
     name, fn, args, out, _ = _decode_call(cache, q, block_tables, context_lens, scale,
                                           partition_tokens, workspace, out, out_dtype, stream,
                                           (k_new, v_new))
@@ -554,6 +569,8 @@ def quantize(src: PagedCache, dst: PagedCache, block_ids=None, stream=None):
     if block_ids is not None:
         _need(block_ids, "block_ids", torch.int32, 1)
         n = block_ids.shape[0]
+    _same_device(src.k_cache, _cache_tensors(src) + _cache_tensors(dst) +
+                 (("block_ids", block_ids),))
     _check("pkv_quantize",
            _load().pkv_quantize(ctypes.byref(src.desc), ctypes.byref(dst.desc), _ptr(block_ids),
                                 n, _stream(stream)))
@@ -565,6 +582,7 @@ def copy_blocks(cache: PagedCache, pairs, stream=None):
     _need(pairs, "pairs", torch.int32, 2)
     if pairs.shape[1] != 2:
         raise ValueError("pairs must be [n][2]")
+    _same_device(cache.k_cache, _cache_tensors(cache) + (("pairs", pairs),))
     _check("pkv_copy_blocks",
            _load().pkv_copy_blocks(ctypes.byref(cache.desc), _ptr(pairs), pairs.shape[0],
                                    _stream(stream)))
@@ -572,11 +590,20 @@ def copy_blocks(cache: PagedCache, pairs, stream=None):
 
 def gather(cache: PagedCache, block_tables, context_lens, cu_seqlens, total_tokens: int,
            stream=None):
+    """Each sequence's K and V in logical order into contiguous rows (codes
+    for quantized pools): returns (k_out, v_out) of total_tokens rows, where
+    total_tokens must be cu_seqlens[num_seqs], the prefix sum of the lengths
+    (the kernel writes row cu_seqlens[s] + t)."""
     torch = _torch()
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     B = context_lens.shape[0]
+    if block_tables.shape[0] != B or cu_seqlens.shape[0] != B + 1:
+        raise ValueError("block_tables must have num_seqs rows and cu_seqlens num_seqs + 1 entries")
+    _same_device(cache.k_cache, _cache_tensors(cache) + (
+        ("block_tables", block_tables), ("context_lens", context_lens),
+        ("cu_seqlens", cu_seqlens)))
     shape = (total_tokens, cache.num_kv_heads, cache.k_cache.shape[3])
     ko = torch.empty(shape, dtype=cache.k_cache.dtype, device=cache.k_cache.device)
     vo = torch.empty(shape, dtype=cache.k_cache.dtype, device=cache.k_cache.device)

@@ -294,6 +294,13 @@ def test_binding_rejects_mismatched_query_and_output_shapes():
         pkv.attention_decode(cache, q, meta, lens, 0.1)
     with pytest.raises(ValueError):
         pkv.attention_multi(cache, q4, tables, lens.to("meta"), 0.1)
+    # a pool on another device than q
+    elsewhere = types.SimpleNamespace(head_dim=128, num_kv_heads=8, kv_dtype="bf16",
+                                      k_cache=torch.empty((1, 8, 16, 128), device="meta"))
+    with pytest.raises(ValueError):
+        pkv.attention_decode(elsewhere, q, tables, lens, 0.1)
+    with pytest.raises(ValueError):
+        pkv.decode_step(elsewhere, q, q[:, :8], q[:, :8], tables, lens, 0.1)
 
 
 def test_decode_step_noalloc_rejects_bad_arguments():
