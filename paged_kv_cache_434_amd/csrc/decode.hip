@@ -5,12 +5,18 @@
 // 解析", section "PagedAttention：vLLM 的显存碎片治理") and the G = Hq/Hkv query
 // heads of a group sharing KV head h / G (same page, section "MQA 与 GQA").
 //
-// Work split.  One wavefront per (sequence, KV head, partition of the context).
-// All G query heads of the group are handled by that wavefront, so every KV
-// byte is read from HBM once.  The launch index is decoded KV-head-fastest:
-// consecutive workgroups go to consecutive XCDs, so with 8 KV heads every
-// wavefront of one KV head runs on the same XCD and blocks shared between
-// sequences (a common prefix) are served by that XCD's L2.
+// Work split.  A wavefront takes one KV head and all G query heads of its
+// group, so every KV byte is read from HBM once.  Fixed split: one wavefront
+// per (sequence, KV head, partition of partition_tokens).  Balanced split
+// (the default): a persistent grid of as many wavefronts as the GPU holds at
+// once cuts each KV head's blocks, all sequences laid end to end, into equal
+// ranges (decode_mfma_balanced_kernel).  Shared prefix: the common blocks run
+// once for the queries of 16 / G sequences (decode_mfma_prefix_kernel).
+// Several query tokens per sequence take the columns of one or two 16-column
+// groups per wavefront, or passes.  The launch index is decoded
+// KV-head-fastest: consecutive workgroups go to consecutive XCDs, so with 8
+// KV heads every wavefront of one KV head runs on the same XCD and blocks
+// shared between sequences (a common prefix) are served by that XCD's L2.
 //
 // Per 16-token block (bf16 / 8-bit KV, MFMA kernel):
 //   1. the K and V tiles ([16][D], contiguous per (block, head)) are read with
@@ -58,10 +64,10 @@
 // range, so they are never read, and rows outside a column's window are
 // masked like rows past the end.
 //
-// Split context: with partition_tokens > 0 each wavefront writes its
-// partition's (max, sum, normalised output) to the workspace and a second
-// kernel combines them with the log-sum-exp rule; a sequence that fits in one
-// partition is written directly.
+// Split context: each piece of a sequence (a fixed partition, or the part of
+// a sequence one balanced range covers) writes its (max, sum, normalised
+// output) to the workspace and a second kernel (reduce_kernel) combines them
+// with the log-sum-exp rule; a sequence in one piece is written directly.
 #include <atomic>
 #include <type_traits>
 #include <mutex>
