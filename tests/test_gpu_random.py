@@ -1,8 +1,9 @@
 """Randomized GPU parity: seeded small configurations drawn across every
 attention entry point (decode attention, decode step with its append, several
 query tokens, sliding window, shared prefix), every pool format, head
-grouping G = 1 .. 16, head_dim 64 and 128, the splits and both pool layouts,
-with lengths that include 0, 1 and block edges.  Each case is compared with
+grouping G = 1 .. 16 (powers of two and 3, and a second family with 5 .. 15
+and batches of 200-320 sequences), head_dim 64 and 128, the splits and both
+pool layouts, with lengths that include 0, 1 and block edges.  Each case is compared with
 the oracle at the stated tolerances (pool bytes bit-exact where a call writes
 them).  The case is printed before it runs, so a failure names it."""
 import numpy as np
@@ -75,9 +76,49 @@ def _oracle_pool(wl, fmt):
     return kc, vc, ks, vs, None, None
 
 
+def _case_wide(i):
+    """Groupings outside powers of two (G = 5 .. 15) and batches past 256
+    sequences (the balanced split keeps the lengths of the first 256 in
+    registers and loads the rest per chunk), one query token for the large
+    batches so the oracle stays quick."""
+    rng = np.random.default_rng(20000 + i)
+    entry = ENTRIES[i % len(ENTRIES)]
+    fmt = ("bf16", "i8", "fp8", "fp4", "u8z")[rng.integers(5)]
+    G = int(rng.choice([5, 6, 7, 9, 10, 12, 13, 15]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    big = entry in ("decode", "step", "prefix") and rng.random() < 0.5
+    B = int(rng.integers(200, 321)) if big else int(rng.integers(1, 13))
+    lo = 1 if entry == "step" else 0
+    hi = 300 if big else 700
+    edge = [0, 1, 15, 16, 17, 31, 33]
+    lens = [max(lo, int(rng.choice(edge)) if rng.random() < 0.3 else int(rng.integers(lo, hi)))
+            for _ in range(B)]
+    split = int(rng.choice([0, -1, -1, 64, 256]))
+    layout = str(rng.choice(["split", "blocks"]))
+    ntok = int(rng.integers(1, 11)) if entry in ("multi", "window") else 1
+    window = int(rng.integers(1, 400)) if entry == "window" else 0
+    prefix_blocks = int(rng.integers(1, 5)) if entry == "prefix" else 0
+    return dict(i=20000 + i, entry=entry, fmt=fmt, G=G, Hkv=Hkv, D=D, B=B, lens=lens,
+                split=split, layout=layout, ntok=ntok, window=window,
+                prefix_blocks=prefix_blocks)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_config(i):
-    c = _case(i)
+    _run_case(_case(i))
+
+
+N_WIDE_CASES = 60
+
+
+@pytest.mark.parametrize("i", range(N_WIDE_CASES))
+def test_random_config_wide(i):
+    _run_case(_case_wide(i))
+
+
+def _run_case(c):
+    i = c["i"]
     print(f"random case {c}", flush=True)
     Hq = c["G"] * c["Hkv"]
     if c["entry"] == "prefix":
