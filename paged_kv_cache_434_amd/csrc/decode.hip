@@ -1023,9 +1023,30 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   // fetched in that XCD's L2.
   const int tok_wave = MQ == kMqPair ? 2 * a.tok_per_pass : a.tok_per_pass;
   const int passes = (a.ntok + tok_wave - 1) / tok_wave;
-  const int g = blockIdx.x % a.hkv;
-  const int pass = (blockIdx.x / a.hkv) % passes;
-  const int v = blockIdx.x / (a.hkv * passes);
+  // bf16 pools (bound by HBM), full generation: consecutive launch indices
+  // alternate between even and odd XCDs, and the wavefronts on odd XCDs run
+  // 8-11 % slower for the same bytes (on every box and workload measured).
+  // So range v takes the parity of its launch index, and even ranges take
+  // per + per / 16 blocks, odd ones per - per / 16 (V even; the host rounds
+  // it).  Measured on one box against equal ranges, kernel time: 8B step
+  // 110.8 -> 109.1 us, 70B 406.4 -> 397.0, long context 174.6 -> 171.0,
+  // 8 tokens 129.4 -> 126.3, 70B with 4 tokens 432.0 -> 422.9; with 4 tokens
+  // on the 8B shape, a quarter generation, 108.9 -> 111.8, so those keep
+  // equal ranges.  Quantized kernels keep equal ranges and one KV head per
+  // XCD: over a shared prefix served by the caches, the skew and the split
+  // of a head over two XCDs cost 12 % (INT8 81 -> 91 us).
+  constexpr bool kSkew = KV == KV_BF16 && (MQ == kMqOne || MQ == kMqPair);
+  int g, pass, v;
+  if constexpr (kSkew) {
+    const unsigned lin = blockIdx.x >> 1;
+    g = lin % a.hkv;
+    pass = (lin / a.hkv) % passes;
+    v = 2 * (int)(lin / (a.hkv * passes)) + (int)(blockIdx.x & 1);
+  } else {
+    g = blockIdx.x % a.hkv;
+    pass = (blockIdx.x / a.hkv) % passes;
+    v = blockIdx.x / (a.hkv * passes);
+  }
   const int V = gridDim.x / (a.hkv * passes);
   const int B = a.num_seqs;
   const int tok0 = pass * tok_wave;
@@ -1079,9 +1100,25 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   // registers instead of being treated as per-lane values
   total = __builtin_amdgcn_readfirstlane(total);
   const int per = max((total + V - 1) / V, a.min_blocks);
-  const int x0 = v * per;
-  if (x0 >= total) return;
-  const int x1 = min(x0 + per, total);
+  // skewed pairs of ranges: [2 w per, 2 w per + pe) and [.. + pe, 2 (w + 1) per)
+  int x0, x1, pe = per;
+  if constexpr (kSkew) {
+    const int dsh = per - per / 16 >= a.min_blocks ? per / 16 : 0;
+    pe = per + dsh;
+    x0 = (v >> 1) * 2 * per + (v & 1) * pe;
+    if (x0 >= total) return;
+    x1 = min(x0 + ((v & 1) ? per - dsh : pe), total);
+  } else {
+    x0 = v * per;
+    if (x0 >= total) return;
+    x1 = min(x0 + per, total);
+  }
+  auto range_of = [&](int x) {   // the range holding flat position x
+    if constexpr (kSkew)
+      return 2 * (x / (2 * per)) + ((x % (2 * per)) >= pe ? 1 : 0);
+    else
+      return x / per;
+  };
 
   // pass 2: the sequence holding flat position x0; the lanes keep the lengths
   // and inclusive prefix of a 64-sequence chunk for the walk below
@@ -1107,8 +1144,8 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int fb = first_block(L, a.ntok, a.window);
     const int R1 = R0 + seq_blocks(L, a.ntok, a.window);
     const int e = min(x1, R1);
-    const int vf = R0 / per;
-    const int K = (R1 - 1) / per - vf + 1;
+    const int vf = range_of(R0);
+    const int K = range_of(R1 - 1) - vf + 1;
     const int slot = v - vf;
     if (g == 0 && pass == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
     mfma_segment<D, KV, OUT, kBalStages, MQ>(a, s, g, L, fb + x - R0, fb + e - R0, slot, K == 1,
@@ -1661,6 +1698,11 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
     m.vn = q8 ? nullptr : (const uint8_t*)a.v_new;
     m.kc_w = (uint8_t*)c.k_cache;
     m.vc_w = (uint8_t*)c.v_cache;
+    // the balanced bf16 kernels of one full generation (one query token, or
+    // two column groups) pair their ranges (even, odd): an even count
+    auto skew_ranges = [&](int64_t r) {
+      return c.kv_dtype == PKV_BF16 ? std::max<int64_t>(2, r & ~(int64_t)1) : r;
+    };
     auto go = [&](auto fixed_kernel, auto balanced_kernel) {
       if (pl.balanced) {
         // one generation: as many wavefronts as the GPU holds at once
@@ -1676,7 +1718,8 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         const int64_t div = a.ntok > 1 && c.kv_dtype == PKV_BF16 ? 4 : 1;
         const int64_t waves = (int64_t)pl.cus * per_cu / div;
         ranges = (waves + hkv - 1) / hkv;
-        dim3 grid((unsigned)(((waves + hkv - 1) / hkv) * hkv * pl.passes));
+        if (a.ntok <= 1) ranges = skew_ranges(ranges);   // the kMqOne kernel
+        dim3 grid((unsigned)(ranges * hkv * pl.passes));
         return launch(balanced_kernel, grid, block, st, m);
       }
       dim3 grid((unsigned)((int64_t)a.num_seqs * hkv * pl.n_parts), (unsigned)pl.passes);
@@ -1711,7 +1754,7 @@ int run_d_out(const DecodeArgs& a, const Plan& pl, hipStream_t st) {
         const int per_cu = resident_waves_per_cu(reinterpret_cast<const void*>(kernel));
         if (per_cu <= 0) return (int)PKV_ERR_HIP;
         const int64_t waves = (int64_t)pl.cus * per_cu;
-        ranges = (waves + hkv - 1) / hkv;
+        ranges = skew_ranges((waves + hkv - 1) / hkv);
         return launch(kernel, dim3((unsigned)(ranges * hkv)), block, st, m);
       }
       if (mq == kMqOne)
