@@ -988,16 +988,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 
 // Balanced split: a persistent grid of V wavefronts per KV head, one
 // generation on the GPU.  For KV head g, the blocks of all sequences are laid
-// end to end (sequence 0's blocks, then sequence 1's, ...; T in all) and
-// wavefront v takes the range [v P, v P + P) with P = max(ceil(T / V),
-// min_blocks), so every wavefront moves the same number of bytes and all of
-// them finish together.  A range that covers a sequence's blocks only in part
-// yields a partial in slot v - floor(R0 / P) of that sequence (R0: the
-// sequence's first position in the flat order); the sequence has
-// floor((R1 - 1) / P) - floor(R0 / P) + 1 pieces, which the wavefront holding
-// its first block records for the combine kernel.  The eight wavefronts of one
-// v are consecutive launch indices, so they run side by side on different XCDs
-// and read the eight heads of the same blocks at the same time.
+// end to end (sequence 0's blocks, then sequence 1's, ...; T in all, each
+// sequence preceded by kSeqStartCost blocks that stand for the cost of
+// entering it and are never read) and wavefront v takes the range
+// [v P, v P + P) with P = max(ceil(T / V), min_blocks) (bf16: pairs of ranges
+// skewed toward the even XCDs, below), so the wavefronts' work is even and
+// they finish together.  A range that covers a sequence's blocks only in part
+// yields a partial in slot v - range(R0) of that sequence (R0: the flat
+// position of its first real block, range(x) = floor(x / P) for equal
+// ranges); the sequence has range(R1 - 1) - range(R0) + 1 pieces, which the
+// wavefront holding its first block records for the combine kernel.  The
+// wavefronts of one v are consecutive launch indices, so they run side by
+// side and read the heads of the same blocks at the same time.
 //
 // Two blocks in flight per wavefront and two wavefronts per SIMD for every
 // format (three or four blocks in flight, and other occupancies, measured
@@ -1009,6 +1011,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 // about 350 registers and run one wavefront per SIMD.
 constexpr int kBalStages = 2;
 constexpr int kBalWaves = 2;
+constexpr int kSeqStartCost = 4;   // blocks charged per sequence start (see the kernel)
 template <int D, int KV, int OUT, int MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     MQ == kMqPair ? 1 : KV == KV_I8 && !MQ ? 3 : kBalWaves))) void
@@ -1074,15 +1077,27 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     return r;
   };
 
-  // pass 1: total blocks per KV head, from the inclusive prefix of each
+  // pass 1: total (virtual) blocks per KV head, from the inclusive prefix of each
   // 64-sequence chunk (the first chunk's is kept for pass 2, which then needs
   // no second scan when there are at most 64 sequences); zero rows of empty
   // sequences
+  //
+  // Each sequence counts kSeqStartCost blocks more than it has, placed before
+  // its first one and never read: a wavefront that enters a sequence starts
+  // its pipeline again (the table entries, then the first tiles, with nothing
+  // in flight), which costs it about that much streaming time, so ranges that
+  // hold sequence starts take fewer real blocks.  A piece and its slot are
+  // counted from the sequence's first real block.  Measured on one box
+  // against no start cost (kernel time): 8B 109.0 -> 107.2 us, INT8 8B step
+  // 74.8 -> 72.4, E4M3 73.1 -> 71.0, E2M1 49.7 -> 46.5, per-row uint8 78.8 ->
+  // 77.5, 1024-token window 54.9 -> 53.0, E4M3 over the shared prefix 77.0 ->
+  // 75.3; 2, 3 and 6 blocks gave less overall.
+  auto vblocks = [&](int nb) { return nb > 0 ? nb + kSeqStartCost : 0; };
   int total = 0, incl0 = 0;
   for (int base = 0; base < B; base += kWave) {
     const int si = base + lane;
     const int Ll = len_chunk(base);
-    const int inc = wave_incl_scan(seq_blocks(Ll, a.ntok, a.window));
+    const int inc = wave_incl_scan(vblocks(seq_blocks(Ll, a.ntok, a.window)));
     if (base == 0) incl0 = inc;
     total += readlane_i(inc, kWave - 1);
     if (v == 0) {
@@ -1125,7 +1140,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   int base = 0, carry = 0, s = -1, R0 = 0, Lreg = 0, incl = 0;
   for (; base < B; base += kWave) {
     Lreg = len_chunk(base);
-    const int nb = seq_blocks(Lreg, a.ntok, a.window);
+    const int nb = vblocks(seq_blocks(Lreg, a.ntok, a.window));
     incl = (base == 0 ? incl0 : wave_incl_scan(nb)) + carry;
     const uint64_t hit = __ballot(nb > 0 && incl - nb <= x0 && x0 < incl);
     if (hit) {
@@ -1142,14 +1157,18 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   while (true) {
     const int L = readlane_i(Lreg, s - base);
     const int fb = first_block(L, a.ntok, a.window);
-    const int R1 = R0 + seq_blocks(L, a.ntok, a.window);
+    const int R1 = R0 + vblocks(seq_blocks(L, a.ntok, a.window));
+    const int Rr = R0 + kSeqStartCost;   // the sequence's first real block
     const int e = min(x1, R1);
-    const int vf = range_of(R0);
-    const int K = range_of(R1 - 1) - vf + 1;
-    const int slot = v - vf;
-    if (g == 0 && pass == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
-    mfma_segment<D, KV, OUT, kBalStages, MQ>(a, s, g, L, fb + x - R0, fb + e - R0, slot, K == 1,
-                                          tok0, lds_k, lds_v, lds_p);
+    const int xs = max(x, Rr);
+    if (xs < e) {
+      const int vf = range_of(Rr);
+      const int K = range_of(R1 - 1) - vf + 1;
+      const int slot = v - vf;
+      if (g == 0 && pass == 0 && slot == 0 && lane == 0) a.ws_count[s] = K;
+      mfma_segment<D, KV, OUT, kBalStages, MQ>(a, s, g, L, fb + xs - Rr, fb + e - Rr, slot,
+                                            K == 1, tok0, lds_k, lds_v, lds_p);
+    }
     if (e >= x1) break;
     x = e;
     R0 = R1;
@@ -1161,7 +1180,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
         carry = readlane_i(incl, kWave - 1);
         base += kWave;
         Lreg = len_chunk(base);
-        incl = wave_incl_scan(seq_blocks(Lreg, a.ntok, a.window)) + carry;
+        incl = wave_incl_scan(vblocks(seq_blocks(Lreg, a.ntok, a.window))) + carry;
       }
       Lnext = readlane_i(Lreg, s - base);
     }
