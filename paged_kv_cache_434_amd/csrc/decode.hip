@@ -990,7 +990,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(MfmaArgs a, int n_parts
 // generation on the GPU.  For KV head g, the blocks of all sequences are laid
 // end to end (sequence 0's blocks, then sequence 1's, ...; T in all, each
 // sequence preceded by kSeqStartCost blocks that stand for the cost of
-// entering it and are never read) and wavefront v takes the range
+// entering it and are never read, when the ranges stay above min_blocks)
+// and wavefront v takes the range
 // [v P, v P + P) with P = max(ceil(T / V), min_blocks) (bf16: pairs of ranges
 // skewed toward the even XCDs, below), so the wavefronts' work is even and
 // they finish together.  A range that covers a sequence's blocks only in part
@@ -1092,14 +1093,19 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   // 74.8 -> 72.4, E4M3 73.1 -> 71.0, E2M1 49.7 -> 46.5, per-row uint8 78.8 ->
   // 77.5, 1024-token window 54.9 -> 53.0, E4M3 over the shared prefix 77.0 ->
   // 75.3; 2, 3 and 6 blocks gave less overall.
-  auto vblocks = [&](int nb) { return nb > 0 ? nb + kSeqStartCost : 0; };
-  int total = 0, incl0 = 0;
+  int total = 0, nseq = 0, incl0 = 0, cnt0 = 0;
   for (int base = 0; base < B; base += kWave) {
     const int si = base + lane;
     const int Ll = len_chunk(base);
-    const int inc = wave_incl_scan(vblocks(seq_blocks(Ll, a.ntok, a.window)));
-    if (base == 0) incl0 = inc;
+    const int nb = seq_blocks(Ll, a.ntok, a.window);
+    const int inc = wave_incl_scan(nb);
+    const int cnt = wave_incl_scan(nb > 0 ? 1 : 0);
+    if (base == 0) {
+      incl0 = inc;
+      cnt0 = cnt;
+    }
     total += readlane_i(inc, kWave - 1);
+    nseq += readlane_i(cnt, kWave - 1);
     if (v == 0) {
       uint64_t empty = __ballot(si < B && Ll == 0);
       while (empty) {
@@ -1114,6 +1120,15 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
   // from them (ranges, block indices, buffer descriptors) stays in scalar
   // registers instead of being treated as per-lane values
   total = __builtin_amdgcn_readfirstlane(total);
+  nseq = __builtin_amdgcn_readfirstlane(nseq);
+  // The start cost only where ranges stay above the floor of min_blocks: at
+  // the floor the ranges are not balanced in time anyway, and the extra
+  // blocks only move range edges off sequence edges (long context with a
+  // 4096-token window, 8 sequences: 31.9 -> 34.7 us with the cost).
+  const int c = (total + nseq * kSeqStartCost + V - 1) / V > a.min_blocks ? kSeqStartCost : 0;
+  auto vblocks = [&](int nb) { return nb > 0 ? nb + c : 0; };
+  total += nseq * c;
+  incl0 += cnt0 * c;
   const int per = max((total + V - 1) / V, a.min_blocks);
   // skewed pairs of ranges: [2 w per, 2 w per + pe) and [.. + pe, 2 (w + 1) per)
   int x0, x1, pe = per;
@@ -1158,7 +1173,7 @@ decode_mfma_balanced_kernel(MfmaArgs a) {
     const int L = readlane_i(Lreg, s - base);
     const int fb = first_block(L, a.ntok, a.window);
     const int R1 = R0 + vblocks(seq_blocks(L, a.ntok, a.window));
-    const int Rr = R0 + kSeqStartCost;   // the sequence's first real block
+    const int Rr = R0 + c;   // the sequence's first real block
     const int e = min(x1, R1);
     const int xs = max(x, Rr);
     if (xs < e) {
