@@ -9,8 +9,8 @@
 // group, so every KV byte is read from HBM once.  Fixed split: one wavefront
 // per (sequence, KV head, partition of partition_tokens).  Balanced split
 // (the default): a persistent grid of as many wavefronts as the GPU holds at
-// once cuts each KV head's blocks, all sequences laid end to end, into equal
-// ranges (decode_mfma_balanced_kernel).  Shared prefix: the common blocks run
+// once cuts each KV head's blocks, all sequences laid end to end, into ranges
+// of even work (decode_mfma_balanced_kernel).  Shared prefix: the common blocks run
 // once for the queries of 16 / G sequences (decode_mfma_prefix_kernel).
 // Several query tokens per sequence take the columns of one or two 16-column
 // groups per wavefront, or passes.  The launch index is decoded
