@@ -224,7 +224,7 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_blocks_per_seq, int32_t partition_tokens);
 
 /* The split this library recommends for the given geometry: always
- * PKV_SPLIT_BALANCED (one generation of wavefronts with equal shares of the
+ * PKV_SPLIT_BALANCED (one generation of wavefronts with even shares of the
  * blocks), or 0 for invalid sizes. */
 int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
                                      int32_t max_blocks_per_seq);
@@ -244,10 +244,11 @@ int32_t pkv_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
  *       output) and a second kernel combines them with the log-sum-exp rule.
  *     PKV_SPLIT_BALANCED: for each KV head the blocks of all sequences, laid
  *       end to end, are cut into equal ranges, one per wavefront of a grid
- *       that fills the GPU once (at least 16 blocks per range; for bf16
- *       pools, pairs of ranges one sixteenth larger and smaller, the larger
- *       on the even XCDs, which run faster); pieces of a sequence are
- *       combined as above.  With the fixed split, results are
+ *       that fills the GPU once (at least 16 blocks per range; each
+ *       sequence start counts as 4 more blocks when ranges stay above 16;
+ *       for bf16 pools, pairs of ranges one sixteenth larger and smaller,
+ *       the larger on the even XCDs, which run faster); pieces of a sequence
+ *       are combined as above.  With the fixed split, results are
  *       reproducible for given inputs; with the balanced split they are
  *       reproducible for given inputs and GPU model (the ranges depend on the
  *       compute-unit count).
